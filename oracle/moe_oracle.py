@@ -1,0 +1,291 @@
+"""fp64 CPU oracle of the ZONOS2 / ZONOS3-Mini mixture-of-experts layer.
+
+TEST INFRASTRUCTURE. Only the tests, the package's smoke check and the benchmark's CPU-baseline
+leg may import this module. The library never calls it, and it shares no code, constant or helper
+with the HIP implementation: it is plain numpy written from the definitions below.
+
+What the layer computes (one token t, E experts, k of them selected):
+  1. router logits   L[t,e] = sum_i x[t,i] * Wr[e,i] + b_r[e]      (b_r optional)
+  2. rank scores     s[t,e] = L[t,e] + sel_bias[e]  (SelectedSoftmax), else s = L
+  3. selection       the k experts with the largest s, ties to the lowest expert index,
+                     slot 0 holding the best
+  4. weights         SOFTMAX (ZONOS2): softmax over all E logits, each selected expert weighted
+                     by its full probability, no renormalisation (zonos2.cpp INTERNALS,
+                     "Model architecture" table, Router row: prob-weighted no-renorm top-k).
+                     SELECTED_SOFTMAX (ZONOS3-Mini): rank by raw logit plus selection bias, then
+                     softmax over the selected experts' logits only; the bias does not enter the
+                     weights (audio.cpp PR #1271, "Framework change", MoeScoring::SelectedSoftmax).
+  5. dispatch        counts, exclusive-scan offsets, assignment rows r = t*k + j grouped by
+                     expert in ascending r, and the inverse position of every row
+  6. expert FFN      SwiGLU: o = Wd[e] (silu(Wg[e] x) * (Wu[e] x)), silu(z) = z / (1 + e^-z)
+                     (audio.cpp PR #1271, "Summary": SwiGLU FFN; zonos2.cpp INTERNALS,
+                     "Recommended: F16 spine + K-quant experts": gate/up/down expert stacks)
+  7. combine         y[t] = sum_j w[t,j] * o[t,j], fp32 output stream in the library
+                     (zonos2.cpp INTERNALS, "Notes": activation/residual streams are F32).
+
+Everything floating is fp64 with no intermediate rounding, except the one place where the library
+contract fixes fp32: ranking on given fp32 logits, where ``L + sel_bias`` is one fp32
+round-to-nearest-even add (numpy float32 addition is exactly that).
+
+Pins (checked by the CPU tests against values the mathematics fixes, not against this code):
+brute-force selection, closed-form softmax weights, exact fp32 rounding cases, dispatch
+invariants, the E=1 layer equal to a dense SwiGLU FFN computed with torch's silu, and the full
+layer equal to a dense run-every-expert brute force.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+f64 = np.float64
+
+SOFTMAX = "softmax"
+SELECTED_SOFTMAX = "selected_softmax"
+
+
+# ----------------------------------------------------------------------------- routing (steps 1-4)
+
+def router_logits_ref(x, w_router, router_bias=None):
+    """Step 1 in fp64: L = x @ Wr^T (+ b_r)."""
+    L = np.asarray(x, dtype=f64) @ np.asarray(w_router, dtype=f64).T
+    if router_bias is not None:
+        L = L + np.asarray(router_bias, dtype=f64)[None, :]
+    return L
+
+
+def rank_scores_fp32(logits32, sel_bias=None):
+    """Step 2 on fp32 logits: s = fl32(L + sel_bias), a single IEEE RNE fp32 add."""
+    L = np.asarray(logits32, dtype=np.float32)
+    if sel_bias is None:
+        return L.copy()
+    return (L + np.asarray(sel_bias, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+def select_topk_ref(scores, k):
+    """Step 3: per token, order experts by (score descending, index ascending) and keep k.
+    -0.0 and +0.0 compare equal, so their order falls to the index."""
+    s = np.asarray(scores)
+    T, E = s.shape
+    ids = np.empty((T, k), dtype=np.int64)
+    idx = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((idx, -s[t].astype(f64)))
+        ids[t] = order[:k]
+    return ids
+
+
+def routing_weights_ref(logits, ids, scoring):
+    """Step 4 in fp64 from the (unbiased) logits."""
+    L = np.asarray(logits, dtype=f64)
+    ids = np.asarray(ids)
+    with np.errstate(invalid="ignore", over="ignore"):
+        if scoring == SOFTMAX:
+            m = L.max(axis=1, keepdims=True)
+            p = np.exp(L - m)
+            p = p / p.sum(axis=1, keepdims=True)
+            return np.take_along_axis(p, ids, axis=1)
+        if scoring == SELECTED_SOFTMAX:
+            sel = np.take_along_axis(L, ids, axis=1)
+            m = sel.max(axis=1, keepdims=True)
+            q = np.exp(sel - m)
+            return q / q.sum(axis=1, keepdims=True)
+    raise ValueError(f"unknown scoring {scoring}")
+
+
+def expert_counts_ref(ids, E):
+    counts = np.zeros(E, dtype=np.int64)
+    for e in np.asarray(ids).ravel():
+        counts[e] += 1
+    return counts
+
+
+def route_ref(logits32, sel_bias, k, scoring):
+    """The routing call on given fp32 logits: ids [T,k], fp64 weights [T,k], counts [E]."""
+    if scoring == SOFTMAX and sel_bias is not None:
+        raise ValueError("a selection bias is only defined for SelectedSoftmax")
+    s = rank_scores_fp32(logits32, sel_bias)
+    ids = select_topk_ref(s, k)
+    w = routing_weights_ref(np.asarray(logits32, dtype=np.float32), ids, scoring)
+    return ids, w, expert_counts_ref(ids, np.asarray(logits32).shape[1])
+
+
+# ------------------------------------------------------------------------------ dispatch (step 5)
+
+def permute_ref(ids, E):
+    """Step 5 with plain loops: offsets [E+1], sorted_rows [T*k], row_pos [T*k]."""
+    flat = [int(v) for v in np.asarray(ids).ravel()]
+    counts = [0] * E
+    for e in flat:
+        counts[e] += 1
+    offsets = [0] * (E + 1)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:E]
+    fill = list(fill)
+    sorted_rows = [0] * len(flat)
+    row_pos = [0] * len(flat)
+    for r, e in enumerate(flat):
+        sorted_rows[fill[e]] = r
+        row_pos[r] = fill[e]
+        fill[e] += 1
+    return (np.array(offsets, dtype=np.int64), np.array(sorted_rows, dtype=np.int64),
+            np.array(row_pos, dtype=np.int64))
+
+
+# ------------------------------------------------------------------------- experts (steps 6-7)
+
+def silu_ref(z):
+    z = np.asarray(z, dtype=f64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn_ref(xrows, wg, wu, wd):
+    """One expert on a block of token rows: Wd (silu(Wg x) * (Wu x)), fp64."""
+    X = np.asarray(xrows, dtype=f64)
+    g = X @ np.asarray(wg, dtype=f64).T
+    u = X @ np.asarray(wu, dtype=f64).T
+    h = silu_ref(g) * u
+    return h @ np.asarray(wd, dtype=f64).T
+
+
+def expert_ffn_ref(x, w_gate, w_up, w_down, offsets, sorted_rows, k):
+    """Step 6 over every expert group: expert_out [T*k, d] in grouped (sorted) order."""
+    x = np.asarray(x)
+    E = np.asarray(w_gate).shape[0]
+    d = x.shape[1]
+    out = np.zeros((len(sorted_rows), d), dtype=f64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        toks = np.asarray(sorted_rows[a:b]) // k
+        out[a:b] = swiglu_ffn_ref(x[toks], w_gate[e], w_up[e], w_down[e])
+    return out
+
+
+def combine_ref(expert_out, row_pos, w, k):
+    """Step 7: y[t] = sum over slots j (in slot order) of w[t,j] * expert_out[row_pos[t*k+j]]."""
+    w = np.asarray(w, dtype=f64)
+    T = w.shape[0]
+    eo = np.asarray(expert_out, dtype=f64)
+    y = np.zeros((T, eo.shape[1]), dtype=f64)
+    for t in range(T):
+        for j in range(k):
+            y[t] += w[t, j] * eo[int(row_pos[t * k + j])]
+    return y
+
+
+# ----------------------------------------------------------------------------- the whole layer
+
+def layer_ref(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None, sel_bias=None,
+              selection=None):
+    """Steps 1-7 in fp64. ``selection`` ([T,k] expert ids) replaces step 3 when given: it is how a
+    near-tied token is re-evaluated at the choice another implementation made."""
+    if scoring == SOFTMAX and sel_bias is not None:
+        raise ValueError("a selection bias is only defined for SelectedSoftmax")
+    E = np.asarray(w_router).shape[0]
+    L = router_logits_ref(x, w_router, router_bias)
+    s = L if sel_bias is None else L + np.asarray(sel_bias, dtype=f64)[None, :]
+    ids = select_topk_ref(s, k) if selection is None else np.asarray(selection, dtype=np.int64)
+    w = routing_weights_ref(L, ids, scoring)
+    counts = expert_counts_ref(ids, E)
+    offsets, sorted_rows, row_pos = permute_ref(ids, E)
+    eo = expert_ffn_ref(x, w_gate, w_up, w_down, offsets, sorted_rows, k)
+    y = combine_ref(eo, row_pos, w, k)
+    return dict(logits=L, scores=s, ids=ids, w=w, counts=counts, offsets=offsets,
+                sorted_rows=sorted_rows, row_pos=row_pos, expert_out=eo, y=y)
+
+
+def layer_tokens_ref(x, w_router, w_gate, w_up, w_down, k, scoring, tokens, router_bias=None,
+                     sel_bias=None, selection=None):
+    """The layer output for a subset of tokens, each computed on its own (every step is per
+    token except the dispatch bookkeeping, which does not change y)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    sel = None if selection is None else np.asarray(selection)[tokens]
+    return layer_ref(np.asarray(x)[tokens], w_router, w_gate, w_up, w_down, k, scoring,
+                     router_bias=router_bias, sel_bias=sel_bias, selection=sel)
+
+
+def dense_bruteforce_ref(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
+                         sel_bias=None):
+    """Run every expert on every token, then mask and weight. Selection by a full Python sort,
+    weights from the definitions, one token at a time. Small inputs only."""
+    x = np.asarray(x, dtype=f64)
+    T, d = x.shape
+    E = np.asarray(w_router).shape[0]
+    y = np.zeros((T, d), dtype=f64)
+    for t in range(T):
+        L = [float(np.dot(x[t], np.asarray(w_router[e], dtype=f64))) for e in range(E)]
+        if router_bias is not None:
+            L = [L[e] + float(router_bias[e]) for e in range(E)]
+        s = L if sel_bias is None else [L[e] + float(sel_bias[e]) for e in range(E)]
+        chosen = sorted(range(E), key=lambda e: (-s[e], e))[:k]
+        if scoring == SOFTMAX:
+            m = max(L)
+            z = sum(math.exp(v - m) for v in L)
+            wt = {e: math.exp(L[e] - m) / z for e in chosen}
+        else:
+            m = max(L[e] for e in chosen)
+            z = sum(math.exp(L[e] - m) for e in chosen)
+            wt = {e: math.exp(L[e] - m) / z for e in chosen}
+        for e in range(E):
+            mask = 1.0 if e in wt else 0.0
+            o = swiglu_ffn_ref(x[t:t + 1], w_gate[e], w_up[e], w_down[e])[0]
+            y[t] += mask * wt.get(e, 0.0) * o
+    return y
+
+
+# ------------------------------------------------------------------- near ties in the full layer
+
+def logit_error_bound(x, w_router, router_bias=None, sel_bias=None):
+    """Per-token bound B_t on |fp32 rank score - exact rank score| for ANY summation order of the
+    fp32 dot product (Higham, Accuracy and Stability of Numerical Algorithms, Thm 3.1:
+    |fl(x.w) - x.w| <= gamma_n sum |x_i w_i|, gamma_n = n u / (1 - n u), u = 2^-24), with one
+    extra gamma term for the product rounding of fp32 operands and one fp32 rounding for each
+    bias add."""
+    x = np.asarray(x, dtype=f64)
+    W = np.asarray(w_router, dtype=f64)
+    d = x.shape[1]
+    u = 2.0 ** -24
+    n = d + 3
+    gamma = n * u / (1.0 - n * u)
+    absdot = np.abs(x) @ np.abs(W).T
+    mag = absdot.copy()
+    if router_bias is not None:
+        mag = mag + np.abs(np.asarray(router_bias, dtype=f64))[None, :]
+    if sel_bias is not None:
+        mag = mag + np.abs(np.asarray(sel_bias, dtype=f64))[None, :]
+    return gamma * mag.max(axis=1) + 4.0 * u * mag.max(axis=1)
+
+
+def decided_tokens(scores64, k, bound):
+    """True where the gap between the k-th and (k+1)-th best fp64 score exceeds 2*bound, i.e.
+    every fp32 evaluation within the bound must pick the same k experts."""
+    s = np.asarray(scores64, dtype=f64)
+    T, E = s.shape
+    if k >= E:
+        return np.ones(T, dtype=bool)
+    srt = -np.sort(-s, axis=1)
+    gap = srt[:, k - 1] - srt[:, k]
+    return gap > 2.0 * np.asarray(bound)
+
+
+def selection_admissible(scores64, k, bound, ids):
+    """For an undecided token, a selection is admissible when its k experts are distinct and each
+    scores within 2*bound of the k-th best fp64 score."""
+    s = np.asarray(scores64, dtype=f64)
+    srt = -np.sort(-s, axis=1)
+    kth = srt[:, k - 1]
+    ok = np.ones(s.shape[0], dtype=bool)
+    for t in range(s.shape[0]):
+        sel = [int(v) for v in ids[t]]
+        if len(set(sel)) != k:
+            ok[t] = False
+            continue
+        for e in sel:
+            if s[t, e] < kth[t] - 2.0 * bound[t]:
+                ok[t] = False
+    return ok

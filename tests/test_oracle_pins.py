@@ -1,0 +1,383 @@
+"""Pins of the fp64 oracle against what the definitions and the mathematics fix (CPU only).
+
+Every check below uses something other than the oracle's own code: hand-derived closed forms
+(tests/golden/hand_cases.json), Python's own sort as a brute-force selector, IEEE-754 rounding
+cases worked by hand, torch's silu as an independent library routine, and a dense
+run-every-expert brute force. The mutation tests at the end plant plausible mistakes in the
+oracle and check that at least one pin catches each of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as orc
+from expert_routing_grouped_moe_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def _ev(s):
+    return float(eval(s, {"__builtins__": {}}, {"log": math.log}))
+
+
+def _arr(v):
+    if isinstance(v, list):
+        return np.array([_arr(a) for a in v], dtype=np.float64)
+    return _ev(v)
+
+
+@pytest.fixture(scope="module")
+def hand():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------------------- hand-derived
+
+def test_hand_softmax_no_renorm(hand):
+    c = hand["softmax_topk_no_renorm"]
+    L = _arr(c["logits"])[None, :].astype(np.float32)
+    for case in c["cases"]:
+        ids, w, counts = orc.route_ref(L, None, case["k"], orc.SOFTMAX)
+        assert ids[0].tolist() == case["ids"]
+        np.testing.assert_allclose(w[0], [_ev(v) for v in case["w"]], rtol=0, atol=1e-7)
+        assert counts.sum() == case["k"]
+
+
+def test_hand_selected_softmax(hand):
+    c = hand["selected_softmax"]
+    L = _arr(c["logits"])[None, :].astype(np.float32)
+    b = _arr(c["sel_bias"]).astype(np.float32)
+    for case in c["cases"]:
+        ids, w, _ = orc.route_ref(L, b, case["k"], orc.SELECTED_SOFTMAX)
+        assert ids[0].tolist() == case["ids"]
+        np.testing.assert_allclose(w[0], [_ev(v) for v in case["w"]], rtol=0, atol=1e-7)
+
+
+def test_hand_fp32_rank_add(hand):
+    c = hand["fp32_rank_add"]
+    L32 = _arr(c["logits"])[None, :].astype(np.float32)
+    b32 = _arr(c["sel_bias"]).astype(np.float32)
+    assert float(L32[0, 0]) == 1 + 2 ** -23 and float(b32[1]) == 2 ** -23 + 2 ** -25
+    ids, _, _ = orc.route_ref(L32, b32, c["k"], orc.SELECTED_SOFTMAX)
+    assert ids[0].tolist() == c["ids_fp32"]
+    s64 = L32.astype(np.float64) + b32.astype(np.float64)[None, :]
+    assert orc.select_topk_ref(s64, c["k"])[0].tolist() == c["ids_exact"]
+
+
+@pytest.mark.parametrize("name", ["swiglu_one_expert", "swiglu_two_experts_top1"])
+def test_hand_swiglu_layer(hand, name):
+    c = hand[name]
+    out = orc.layer_ref(_arr(c["x"]), _arr(c["w_router"]), _arr(c["w_gate"]), _arr(c["w_up"]),
+                        _arr(c["w_down"]), c["k"], c["scoring"])
+    np.testing.assert_allclose(out["y"], _arr(c["y"]), rtol=0, atol=1e-14)
+
+
+# -------------------------------------------------------------------------- selection pins
+
+def _python_topk(row, k):
+    return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:k]
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "equal", "signed_zero", "neg_inf"])
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 1), (8, 8), (16, 1), (16, 2), (64, 2), (64, 8),
+                                 (256, 8), (5, 3)])
+def test_select_matches_python_sort(kind, E, k):
+    L = gen.make_logits(48, E, seed=E * 31 + k, kind=kind)
+    ids = orc.select_topk_ref(L, k)
+    for t in range(L.shape[0]):
+        assert ids[t].tolist() == _python_topk(L[t], k)
+        # dominance: every chosen expert beats every unchosen one under (score desc, idx asc)
+        chosen = set(ids[t].tolist())
+        for e in chosen:
+            for f in range(E):
+                if f in chosen:
+                    continue
+                assert L[t, e] > L[t, f] or (L[t, e] == L[t, f] and e < f)
+
+
+def test_select_equal_rows_closed_form():
+    for E, k in [(8, 1), (16, 2), (64, 8)]:
+        L = np.full((4, E), 0.37, dtype=np.float32)
+        assert (orc.select_topk_ref(L, k) == np.arange(k)[None, :]).all()
+
+
+def test_signed_zero_equal():
+    L = np.array([[-0.0, 0.0, -0.0]], dtype=np.float32)
+    assert orc.select_topk_ref(L, 3)[0].tolist() == [0, 1, 2]
+    L = np.array([[0.0, -0.0]], dtype=np.float32)
+    assert orc.select_topk_ref(L, 1)[0].tolist() == [0]
+
+
+def test_fp32_add_is_rne():
+    # binary32 ties go to the even significand; above half rounds up
+    one = np.float32(1.0)
+    assert float(orc.rank_scores_fp32([[one]], [np.float32(2 ** -24)])[0, 0]) == 1.0
+    a = np.float32(1 + 2 ** -23)
+    assert float(orc.rank_scores_fp32([[a]], [np.float32(2 ** -24)])[0, 0]) == 1 + 2 ** -22
+    assert float(orc.rank_scores_fp32([[one]], [np.float32(1.5 * 2 ** -24)])[0, 0]) == 1 + 2 ** -23
+
+
+# ----------------------------------------------------------------------------- weight pins
+
+def test_softmax_weight_invariants():
+    rng = np.random.default_rng(7)
+    for E in (1, 2, 8, 16, 64):
+        L = rng.standard_normal((32, E)).astype(np.float32) * 3
+        ids, w, _ = orc.route_ref(L, None, E, orc.SOFTMAX)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        ids1, w1, _ = orc.route_ref(L, None, 1, orc.SOFTMAX)
+        assert (w1[:, 0] >= 1.0 / E - 1e-15).all()
+        assert (w1[:, 0] <= 1.0).all()
+        if E == 1:
+            assert (w1 == 1.0).all()
+        # closed form of the top-1 probability
+        Ld = L.astype(np.float64)
+        pmax = 1.0 / np.exp(Ld - Ld.max(axis=1, keepdims=True)).sum(axis=1)
+        np.testing.assert_allclose(w1[:, 0], pmax, rtol=1e-14)
+        if E >= 2:
+            _, w2, _ = orc.route_ref(L, None, 2, orc.SOFTMAX)
+            assert (w2.sum(axis=1) <= 1.0 + 1e-15).all()
+            assert (w2[:, 0] >= w2[:, 1]).all()
+
+
+def test_selected_softmax_weight_invariants():
+    rng = np.random.default_rng(8)
+    for E in (2, 8, 64):
+        L = rng.standard_normal((32, E)).astype(np.float32) * 2
+        b = rng.standard_normal(E).astype(np.float32)
+        for k in range(1, min(E, 8) + 1):
+            ids, w, _ = orc.route_ref(L, b, k, orc.SELECTED_SOFTMAX)
+            np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+            if k == 1:
+                assert (w == 1.0).all()
+            if k == 2:
+                l0 = np.take_along_axis(L, ids[:, :1], 1)[:, 0].astype(np.float64)
+                l1 = np.take_along_axis(L, ids[:, 1:2], 1)[:, 0].astype(np.float64)
+                np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+        # the bias changes the ranking only: for a fixed selection the weights ignore it
+        ids, w, _ = orc.route_ref(L, b, 2, orc.SELECTED_SOFTMAX)
+        w_nobias = orc.routing_weights_ref(L, ids, orc.SELECTED_SOFTMAX)
+        np.testing.assert_array_equal(w, w_nobias)
+
+
+def test_mode_equivalence_k_equals_E():
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((16, 8)).astype(np.float32)
+    i1, w1, _ = orc.route_ref(L, None, 8, orc.SOFTMAX)
+    i2, w2, _ = orc.route_ref(L, np.zeros(8, np.float32), 8, orc.SELECTED_SOFTMAX)
+    assert (i1 == i2).all()
+    np.testing.assert_allclose(w1, w2, rtol=1e-14)
+
+
+def test_neg_inf_logit_gets_zero_weight():
+    L = np.array([[0.0, -np.inf, 1.0, -np.inf]], dtype=np.float32)
+    ids, w, _ = orc.route_ref(L, None, 3, orc.SOFTMAX)
+    assert ids[0].tolist() == [2, 0, 1]
+    assert w[0, 2] == 0.0
+    np.testing.assert_allclose(w[0, :2], [math.e / (1 + math.e), 1 / (1 + math.e)], rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------- dispatch pins
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (64, 8, 1), (64, 64, 2), (300, 16, 1), (257, 64, 8),
+                                   (5, 256, 3)])
+def test_permute_invariants(T, E, k):
+    L = gen.make_logits(T, E, seed=T + E + k, kind="normal")
+    ids, _, counts = orc.route_ref(L, None, k, orc.SOFTMAX)
+    offsets, sorted_rows, row_pos = orc.permute_ref(ids, E)
+    assert counts.sum() == T * k
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(ids.ravel(), minlength=E))]))
+    assert sorted(sorted_rows.tolist()) == list(range(T * k))
+    np.testing.assert_array_equal(sorted_rows[row_pos], np.arange(T * k))
+    # a stable sort of the flat expert ids is the same permutation
+    np.testing.assert_array_equal(sorted_rows, np.argsort(ids.ravel(), kind="stable"))
+    for e in range(E):
+        grp = sorted_rows[offsets[e]:offsets[e + 1]]
+        assert (ids.ravel()[grp] == e).all()
+        assert (np.diff(grp) > 0).all()
+
+
+# ----------------------------------------------------------------------------- FFN / layer pins
+
+def _case(T, d, E, k, H, scoring, seed, with_rb=False, with_sb=False):
+    rb = None
+    if with_rb:
+        rb = np.random.default_rng(seed + 100).standard_normal(E).astype(np.float32)
+    inp = gen.make_inputs_custom(T, d, E, k, H, scoring, "f32", seed,
+                                 sel_bias_var=0.5 if with_sb else None, router_bias=rb)
+    return inp
+
+
+def _layer(inp, **kw):
+    return orc.layer_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k, inp.scoring,
+                         router_bias=inp.router_bias, sel_bias=inp.sel_bias, **kw)
+
+
+def test_single_expert_is_dense_swiglu_torch():
+    torch = pytest.importorskip("torch")
+    inp = _case(T=40, d=64, E=1, k=1, H=96, scoring=orc.SOFTMAX, seed=11)
+    y = _layer(inp)["y"]
+    X = torch.from_numpy(inp.x.astype(np.float64))
+    g = X @ torch.from_numpy(inp.w_gate[0].astype(np.float64)).T
+    u = X @ torch.from_numpy(inp.w_up[0].astype(np.float64)).T
+    ref = (torch.nn.functional.silu(g) * u) @ torch.from_numpy(inp.w_down[0].astype(np.float64)).T
+    np.testing.assert_allclose(y, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_zero_up_gives_zero_and_linear_in_down():
+    inp = _case(T=16, d=32, E=4, k=2, H=48, scoring=orc.SELECTED_SOFTMAX, seed=12, with_sb=True)
+    base = _layer(inp)["y"]
+    z = orc.layer_ref(inp.x, inp.w_router, inp.w_gate, np.zeros_like(inp.w_up), inp.w_down, inp.k,
+                      inp.scoring, sel_bias=inp.sel_bias)["y"]
+    assert np.abs(z).max() == 0.0
+    wd2 = np.random.default_rng(3).standard_normal(inp.w_down.shape)
+    y2 = orc.layer_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, wd2, inp.k, inp.scoring,
+                       sel_bias=inp.sel_bias)["y"]
+    ysum = orc.layer_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down + wd2, inp.k,
+                         inp.scoring, sel_bias=inp.sel_bias)["y"]
+    np.testing.assert_allclose(ysum, base + y2, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("scoring,k,rb,sb", [(orc.SOFTMAX, 1, False, False), (orc.SOFTMAX, 2, True, False),
+                                             (orc.SELECTED_SOFTMAX, 2, False, True),
+                                             (orc.SELECTED_SOFTMAX, 3, True, True),
+                                             (orc.SOFTMAX, 8, False, False)])
+def test_layer_equals_dense_bruteforce(scoring, k, rb, sb):
+    inp = _case(T=24, d=32, E=8, k=k, H=40, scoring=scoring, seed=20 + k, with_rb=rb, with_sb=sb)
+    y = _layer(inp)["y"]
+    yb = orc.dense_bruteforce_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, k,
+                                  scoring, router_bias=inp.router_bias, sel_bias=inp.sel_bias)
+    np.testing.assert_allclose(y, yb, rtol=0, atol=1e-12)
+
+
+def test_token_permutation_equivariance():
+    inp = _case(T=32, d=32, E=8, k=2, H=40, scoring=orc.SELECTED_SOFTMAX, seed=31, with_sb=True)
+    y = _layer(inp)["y"]
+    perm = np.random.default_rng(1).permutation(inp.T)
+    yp = orc.layer_ref(inp.x[perm], inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k,
+                       inp.scoring, sel_bias=inp.sel_bias)["y"]
+    np.testing.assert_allclose(yp, y[perm], rtol=0, atol=1e-13)
+
+
+def test_expert_relabel_invariance():
+    inp = _case(T=32, d=32, E=8, k=2, H=40, scoring=orc.SOFTMAX, seed=32, with_rb=True)
+    y = _layer(inp)["y"]
+    pi = np.random.default_rng(2).permutation(inp.E)
+    yp = orc.layer_ref(inp.x, inp.w_router[pi], inp.w_gate[pi], inp.w_up[pi], inp.w_down[pi],
+                       inp.k, inp.scoring, router_bias=inp.router_bias[pi])["y"]
+    np.testing.assert_allclose(yp, y, rtol=0, atol=1e-13)
+
+
+def test_tokens_subset_matches_full():
+    inp = _case(T=40, d=32, E=8, k=2, H=40, scoring=orc.SELECTED_SOFTMAX, seed=33, with_sb=True)
+    full = _layer(inp)["y"]
+    toks = np.array([0, 7, 39, 12])
+    sub = orc.layer_tokens_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k,
+                               inp.scoring, toks, sel_bias=inp.sel_bias)["y"]
+    np.testing.assert_allclose(sub, full[toks], rtol=0, atol=1e-13)
+
+
+def test_combine_and_ffn_steps_compose():
+    inp = _case(T=20, d=16, E=4, k=2, H=24, scoring=orc.SOFTMAX, seed=34)
+    out = _layer(inp)
+    # expert_out in grouped order: each row is the SwiGLU of its token through its expert
+    for pos, r in enumerate(out["sorted_rows"]):
+        t, j = divmod(int(r), inp.k)
+        e = int(out["ids"][t, j])
+        ref = orc.swiglu_ffn_ref(inp.x[t:t + 1], inp.w_gate[e], inp.w_up[e], inp.w_down[e])[0]
+        np.testing.assert_allclose(out["expert_out"][pos], ref, rtol=0, atol=1e-14)
+
+
+# -------------------------------------------------------------------------- near-tie bound pin
+
+def test_logit_error_bound_holds_for_several_fp32_orders():
+    inp = gen.make_inputs_custom(64, 256, 16, 1, 64, orc.SOFTMAX, "bf16", seed=5)
+    rb = np.linspace(-1, 1, 16).astype(np.float32)
+    B = orc.logit_error_bound(inp.x, inp.w_router, rb)
+    exact = orc.router_logits_ref(inp.x, inp.w_router, rb)
+    x32, w32 = inp.x.astype(np.float32), inp.w_router.astype(np.float32)
+    seq = np.zeros((64, 16), np.float32)
+    for i in range(256):
+        seq = (seq + x32[:, i:i + 1] * w32[None, :, i]).astype(np.float32)
+    rev = np.zeros((64, 16), np.float32)
+    for i in reversed(range(256)):
+        rev = (rev + x32[:, i:i + 1] * w32[None, :, i]).astype(np.float32)
+    for L32 in ((x32 @ w32.T).astype(np.float32), seq, rev):
+        L32 = (L32 + rb[None, :]).astype(np.float32)
+        assert (np.abs(L32.astype(np.float64) - exact) <= B[:, None]).all()
+
+
+def test_decided_tokens_agree_between_fp32_and_fp64():
+    inp = gen.make_inputs("zonos3mini-decode-cfg")
+    L64 = orc.router_logits_ref(inp.x, inp.w_router)
+    s64 = L64 + inp.sel_bias.astype(np.float64)[None, :]
+    B = orc.logit_error_bound(inp.x, inp.w_router, None, inp.sel_bias)
+    dec = orc.decided_tokens(s64, inp.k, B)
+    L32 = (inp.x.astype(np.float32) @ inp.w_router.astype(np.float32).T).astype(np.float32)
+    ids32, _, _ = orc.route_ref(L32, inp.sel_bias, inp.k, orc.SELECTED_SOFTMAX)
+    ids64 = orc.select_topk_ref(s64, inp.k)
+    assert dec.sum() >= 60
+    assert (ids32[dec] == ids64[dec]).all()
+    assert orc.selection_admissible(s64, inp.k, B, ids32).all()
+
+
+# ---------------------------------------------------------------------- planted mistakes (CPU)
+
+def _pins_pass():
+    """A compact run of the pins above; returns False at the first failure."""
+    try:
+        with open(GOLDEN) as f:
+            hand = json.load(f)
+        test_hand_softmax_no_renorm(hand)
+        test_hand_selected_softmax(hand)
+        test_hand_fp32_rank_add(hand)
+        test_hand_swiglu_layer(hand, "swiglu_one_expert")
+        test_hand_swiglu_layer(hand, "swiglu_two_experts_top1")
+        test_select_matches_python_sort("ties", 16, 2)
+        test_softmax_weight_invariants()
+        test_selected_softmax_weight_invariants()
+        test_permute_invariants(64, 64, 2)
+        test_layer_equals_dense_bruteforce(orc.SELECTED_SOFTMAX, 2, False, True)
+        test_single_expert_is_dense_swiglu_torch()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_pins_pass_unmodified():
+    assert _pins_pass()
+
+
+MUTATIONS = {
+    # silu with a sign slip: z / (1 + e^z)
+    "silu_sign": ("silu_ref", lambda orig: (lambda z: np.asarray(z, np.float64) /
+                                            (1.0 + np.exp(np.asarray(z, np.float64))))),
+    # ties to the highest index
+    "tie_high": ("select_topk_ref", lambda orig: (lambda s, k: (
+        np.asarray(s).shape[1] - 1 - orig(np.asarray(s)[:, ::-1], k)))),
+    # renormalise the SOFTMAX weights over the selected experts
+    "renorm": ("routing_weights_ref", lambda orig: (lambda L, ids, scoring: (
+        (lambda w: w / w.sum(axis=1, keepdims=True))(orig(L, ids, scoring))))),
+    # SelectedSoftmax weights taken over all experts instead of the selected ones
+    "sel_over_all": ("routing_weights_ref", lambda orig: (lambda L, ids, scoring: orig(L, ids, orc.SOFTMAX))),
+    # gate and up swapped inside the expert
+    "gate_up_swap": ("swiglu_ffn_ref", lambda orig: (lambda X, wg, wu, wd: orig(X, wu, wg, wd))),
+    # combine reads the wrong row of the grouped output
+    "combine_sorted": ("combine_ref", lambda orig: (lambda eo, row_pos, w, k: orig(
+        eo, np.arange(len(row_pos)), w, k))),
+    # rank on the fp64 sum instead of the binary32 add
+    "rank_fp64": ("rank_scores_fp32", lambda orig: (lambda L, b=None: np.asarray(L, np.float64) + (
+        0 if b is None else np.asarray(b, np.float64)[None, :]))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = MUTATIONS[name]
+    orig = getattr(orc, attr)
+    monkeypatch.setattr(orc, attr, make(orig))
+    assert not _pins_pass(), f"mutation {name} slipped through every pin"
