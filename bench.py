@@ -1,0 +1,295 @@
+"""Benchmark of the fused MoE layer (moe_layer_forward) on one MI355X.
+
+A step is one moe_layer_forward over one batch: router logits, top-k + weights, dispatch,
+gate/up + SwiGLU, down projection and combine. Inputs are seeded synthetic tensors resident in
+HBM before timing. The default workload is the ZONOS2-shaped decode step (T=64 tokens, d=2048,
+16 experts, top-1, expert hidden 2816, bf16 weights, fp32 accumulation).
+
+Cold weights: the layer's expert weights are kept in several identical copies and consecutive
+steps rotate through them, so that no step finds its weights in the 256 MB Infinity Cache left
+over from the step before (the copies together exceed 1.5 GB). The steps are replayed from a HIP
+graph (the decode loop of the pages replays a captured graph) holding one step per copy, with
+a HIP event at every stage boundary; the per-stage durations come from those events, recorded
+on the stream the kernels run on, over the same timed region.
+
+Prints one JSON line (see the `result` dict at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
+STAGES = ("route", "dispatch", "gate_up", "down_combine")
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s vs MI355X peak"
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def algorithmic(inp, counts):
+    """Bytes and FLOPs the step must move/do (touched experts only; intermediates excluded)."""
+    T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
+    wb = 2 if inp.dtype == "bf16" else 4
+    touched = int((counts > 0).sum())
+    rows = T * k
+    step_bytes = touched * 3 * d * H * wb + T * d * wb + E * d * wb + T * d * 4 + rows * 8
+    step_flops = 6 * d * H * rows + 2 * T * d * E
+    # the gate/up kernel alone: its weights, the gathered x rows, the bf16 h it writes
+    gu_bytes = touched * 2 * d * H * wb + rows * d * wb + rows * H * wb
+    gu_flops = 4 * d * H * rows
+    return dict(touched=touched, step_bytes=step_bytes, step_flops=step_flops, gu_bytes=gu_bytes,
+                gu_flops=gu_flops)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle as it stands, timed on this host on the same workload."""
+    import numpy as np
+    import oracle.moe_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    tokens = inp.T
+    sample = f"full step ({inp.T} tokens)"
+    x = inp.x
+    if inp.T > 1024:
+        tokens = 512
+        x = inp.x[:tokens]
+        sample = f"first {tokens} of {inp.T} tokens"
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.layer_ref(x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k, inp.scoring,
+                      router_bias=inp.router_bias, sel_bias=inp.sel_bias)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    return {"value": tokens * reps / el, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{sample} x {reps} runs, {el:.1f} s, numpy fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="zonos2-decode")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from expert_routing_grouped_moe_amd import inputs as gen
+    from expert_routing_grouped_moe_amd import moe
+
+    dev = "cuda:0"
+    inp = gen.make_inputs(args.workload)
+    T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
+    dt_code = moe.MOE_BF16 if inp.dtype == "bf16" else moe.MOE_F32
+    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+
+    def up(key):
+        if inp.dtype == "bf16":
+            return torch.from_numpy(inp.bits[key].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(getattr(inp, key)).to(dev)
+
+    x = up("x")
+    wr = up("w_router")
+    base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
+    wbytes = sum(t.numel() * t.element_size() for t in base.values())
+    ncopies = 1 if args.warm else max(2, min(16, math.ceil(1.6e9 / wbytes)))
+    copies = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(ncopies - 1)]
+    rb = None if inp.router_bias is None else torch.from_numpy(inp.router_bias).to(dev)
+    sb = None if inp.sel_bias is None else torch.from_numpy(inp.sel_bias).to(dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    counts = torch.zeros((E,), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, moe.moe_workspace_size(T, d, E, H, k, dt_code)), dtype=torch.uint8,
+                     device=dev)
+
+    hip = _hip()
+    nev = moe.MOE_PROF_EVENTS
+    events = []
+    ev_arrays = []
+    arg_list = []
+    for c in range(ncopies):
+        evs = []
+        for _ in range(nev):
+            h = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            evs.append(h)
+        arr = (ctypes.c_void_p * nev)(*[e.value for e in evs])
+        events.append(evs)
+        ev_arrays.append(arr)
+        a = moe.make_layer_args(x, wr, copies[c]["w_gate"], copies[c]["w_up"],
+                                copies[c]["w_down"], k, inp.scoring, y, rb, sb,
+                                expert_counts=counts)
+        arg_list.append(a)
+
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def one_step(c, with_events):
+        a = arg_list[c]
+        a.prof_events = ctypes.cast(ev_arrays[c], ctypes.c_void_p).value if with_events else None
+        st = moe.LIB.moe_layer_forward(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                       ws.numel(), sptr)
+        if st != 0:
+            raise moe.MoeError(st, "moe_layer_forward")
+
+    def capture(with_events):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(ncopies):
+                one_step(c, with_events)
+        return g
+
+    # eager warm-up (also validates the call), then one graph holding one step per weight copy
+    with torch.cuda.stream(stream):
+        for i in range(max(ncopies, 3)):
+            one_step(i % ncopies, False)
+    torch.cuda.synchronize()
+    graph = capture(False)
+    y.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item(), "graph replay did not run the layer"
+    replays_w = max(1, math.ceil(args.warmup / ncopies))
+    replays = max(1, math.ceil(args.steps / ncopies))
+    steps = replays * ncopies
+    for _ in range(replays_w):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: `steps` layer steps replayed back to back
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / steps * 1e3
+
+    # stage timing: the same steps with a HIP event at every stage boundary, on the kernels'
+    # stream; replayed from a graph with event nodes when the runtime times those, else eager
+    def read_events():
+        out = []
+        for c in range(ncopies):
+            ms = []
+            for i in range(nev - 1):
+                f = ctypes.c_float()
+                if hip.hipEventElapsedTime(ctypes.byref(f), events[c][i], events[c][i + 1]) != 0:
+                    return None
+                ms.append(f.value)
+            out.append(ms)
+        return out
+
+    stage_ms = {s: [] for s in STAGES}
+    ev_mode = "graph"
+    try:
+        graph_ev = capture(True)
+        graph_ev.replay()
+        torch.cuda.synchronize()
+        if read_events() is None:
+            raise RuntimeError("event nodes carry no timestamps")
+    except Exception:
+        ev_mode = "eager"
+        graph_ev = None
+    ev_replays = max(1, min(replays, math.ceil(400 / ncopies)))
+    t_ev = time.perf_counter()
+    for _ in range(ev_replays):
+        if graph_ev is not None:
+            graph_ev.replay()
+        else:
+            with torch.cuda.stream(stream):
+                for c in range(ncopies):
+                    one_step(c, True)
+        torch.cuda.synchronize()
+        got = read_events()
+        assert got is not None, "stage events unreadable"
+        for ms in got:
+            for s_, v in zip(STAGES, ms):
+                stage_ms[s_].append(v)
+    ev_wall = time.perf_counter() - t_ev
+    step_ms_ev = [sum(stage_ms[s_][i] for s_ in STAGES) for i in range(len(stage_ms["route"]))]
+
+    cnt = counts.cpu().numpy()
+    alg = algorithmic(inp, cnt)
+    med = {s: statistics.median(v) for s, v in stage_ms.items()}
+    gu_ms = statistics.mean(stage_ms["gate_up"])
+    prefill = gen.WORKLOADS[args.workload].shape == "prefill"
+    if prefill:
+        ach = alg["gu_flops"] / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        ach = alg["gu_bytes"] / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    roof["kernel"] = "gemm_decode_kernel<gate/up>" if not prefill and (T * k / E) <= 32 else \
+        "gemm_prefill_kernel<gate/up>"
+    roof["avg_launch_us"] = gu_ms * 1e3
+    roof["algorithmic_bytes_per_launch"] = alg["gu_bytes"]
+    roof["algorithmic_flops_per_launch"] = alg["gu_flops"]
+
+    step_s = ms_per_step * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": T / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": replays_w * ncopies,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "H": H,
+                   "scoring": inp.scoring, "seed": gen.WORKLOADS[args.workload].seed,
+                   "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
+                   "timing": "HIP graph replay, one step per weight copy",
+                   "stage_events": ev_mode, "stage_event_steps": len(step_ms_ev)},
+        "step_hbm_gbps": alg["step_bytes"] / step_s / 1e9,
+        "step_hbm_frac": alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
+        "step_tflops": alg["step_flops"] / step_s / 1e12,
+        "step_mfma_frac": alg["step_flops"] / step_s / 1e12 / BF16_PEAK_TFLOPS,
+        "touched_experts": alg["touched"],
+        "stage_median_us": {s: v * 1e3 for s, v in med.items()},
+        "event_step_median_us": statistics.median(step_ms_ev) * 1e3,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 bit handling, 16-byte vector types,
+// the CDNA4 bf16 MFMA wrapper and wave64 utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// D = A(16x32) * B(32x16) + C on the CDNA4 matrix cores, fp32 accumulate.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, eight consecutive k each
+// (k = 8 * (l / 16) + 0..7); it receives C rows 4 * (l / 16) + 0..3 of column (l % 16).
+// Any fixed lane->k assignment used identically for A and B gives the same sum over k.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_precise(float z) { return z / (1.0f + expf(-z)); }
+
+// Upper bound on the number of row tiles of height bm over E expert groups holding `rows` rows
+// in total: sum_e ceil(c_e / bm) <= (rows + E (bm - 1)) / bm, and never more than rows.
+__host__ __device__ inline int max_tiles(int rows, int E, int bm) {
+  if (rows <= 0) return 0;
+  const long long bound = (static_cast<long long>(rows) + static_cast<long long>(E) * (bm - 1)) / bm;
+  return static_cast<int>(bound < rows ? bound : rows);
+}
+
+// Expert tile lookup shared by the grouped FFN kernels. Expert e owns ceil(count_e / bm) row
+// tiles; tiles are numbered expert by expert. Every thread of the block gets the same answer.
+// Needs 2 * (E + 1) ints of LDS in `sh`; every thread of the block must call it.
+struct TileInfo {
+  int e;      // expert, or -1 when the tile index is past the last tile
+  int row0;   // first position in the grouped row order covered by the tile
+  int rows;   // rows of the tile that belong to expert e (1..bm)
+};
+
+__device__ inline TileInfo find_tile(const int32_t* __restrict__ offsets, int E, int bm, int tile,
+                                     int* sh) {
+  // sh[0..E]: offsets; sh[E+1 .. 2E+1]: inclusive tile scan
+  int* soff = sh;
+  int* scum = sh + E + 1;
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) soff[i] = offsets[i];
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    // one wave scans E <= 256 tile counts, four per lane
+    const int lane = threadIdx.x;
+    int c[4];
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      int n = 0;
+      if (e < E) {
+        const int cnt = soff[e + 1] - soff[e];
+        n = (cnt + bm - 1) / bm;
+      }
+      run += n;
+      c[q] = run;
+    }
+    // inclusive scan of the per-lane totals across the wave
+    int tot = run;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(tot, o);
+      if (lane >= o) tot += v;
+    }
+    const int excl = tot - run;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      if (e < E) scum[e] = excl + c[q];
+    }
+  }
+  __syncthreads();
+  TileInfo ti;
+  ti.e = -1;
+  ti.row0 = 0;
+  ti.rows = 0;
+  if (tile >= scum[E - 1]) return ti;
+  // first expert whose inclusive tile count exceeds `tile`
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (scum[mid] > tile) hi = mid; else lo = mid + 1;
+  }
+  const int before = lo > 0 ? scum[lo - 1] : 0;
+  const int m0 = (tile - before) * bm;
+  const int cnt = soff[lo + 1] - soff[lo];
+  ti.e = lo;
+  ti.row0 = soff[lo] + m0;
+  ti.rows = min(bm, cnt - m0);
+  return ti;
+}
+
+}  // namespace moe

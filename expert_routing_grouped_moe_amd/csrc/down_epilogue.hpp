@@ -1,0 +1,45 @@
+// Delivery of one down-projection output element (step 6 -> step 7).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// o = expert output at grouped position p, column n (of d). Combine rule (zonos2.cpp INTERNALS,
+// "Model architecture" table, Router row: the chosen experts' outputs are summed with their
+// routing weights; "Notes": the residual stream is F32):
+//   kDownExpertOut  expert_out[p, n] = o
+//   kDownStoreY     y[t, n] = w[t, j] * o           (k == 1)
+//   kDownAtomicY    y[t, n] += w[t, j] * o          (k == 2, y cleared beforehand; two addends
+//                   onto 0 give fl(a + b) in either order, so the result is deterministic)
+struct DownRow {
+  float* dst;   // row pointer in expert_out or y
+  float scale;  // routing weight (1 for expert_out)
+};
+
+__device__ __forceinline__ DownRow down_row(const DownArgs& a, int p, int d) {
+  DownRow r;
+  if (a.mode == kDownExpertOut) {
+    r.dst = a.out + static_cast<long long>(p) * d;
+    r.scale = 1.0f;
+  } else {
+    const int row = a.sorted_rows[p];
+    const int t = row / a.k;
+    r.dst = a.out + static_cast<long long>(t) * d;
+    r.scale = a.topk_w[row];
+  }
+  return r;
+}
+
+__device__ __forceinline__ void down_put(const DownArgs& a, const DownRow& r, int n, float o) {
+  if (a.mode == kDownAtomicY) {
+    unsafeAtomicAdd(r.dst + n, r.scale * o);
+  } else if (a.mode == kDownStoreY) {
+    r.dst[n] = r.scale * o;
+  } else {
+    r.dst[n] = o;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,289 @@
+// C ABI of libmoe.so: argument validation, workspace layout and the launch sequences.
+// Validation never touches the GPU, so a machine without one can exercise every error path.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using moe::DownArgs;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_dims(int T, int d, int E, int H, int k, int dtype) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || E < 1 || E > moe::kMaxE || k < 1 || k > moe::kMaxK || k > E) return MOE_ERR_SHAPE;
+  if (d <= 0 || H <= 0) return MOE_ERR_SHAPE;
+  const int mult = dtype == MOE_BF16 ? 64 : 4;
+  if (d % mult != 0 || H % mult != 0) return MOE_ERR_SHAPE;
+  if (static_cast<long long>(T) * k >= (1ll << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_route_dims(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > moe::kMaxE || k < 1 || k > moe::kMaxK || k > E) return MOE_ERR_SHAPE;
+  if (static_cast<long long>(T) * k >= (1ll << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_scoring(int scoring, const float* sel_bias) {
+  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SELECTED_SOFTMAX) return MOE_ERR_UNSUPPORTED;
+  if (scoring == MOE_SCORING_SOFTMAX && sel_bias != nullptr) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Device workspace regions of the fused layer (the step calls use a subset).
+struct Layout {
+  size_t logits, ids, w, counts, offsets, sorted_rows, row_pos, h, eo, total;
+  Layout(int T, int d, int E, int H, int k, int dtype) {
+    const size_t rows = static_cast<size_t>(T) * k;
+    size_t o = 0;
+    h = o;           o += up(rows * H * (dtype == MOE_BF16 ? 2 : 4));
+    logits = o;      o += up(static_cast<size_t>(T) * E * 4);
+    ids = o;         o += up(rows * 4);
+    w = o;           o += up(rows * 4);
+    counts = o;      o += up(static_cast<size_t>(E) * 4);
+    offsets = o;     o += up(static_cast<size_t>(E + 1) * 4);
+    sorted_rows = o; o += up(rows * 4);
+    row_pos = o;     o += up(rows * 4);
+    eo = o;          o += k > 2 ? up(rows * d * 4) : 0;
+    total = o;
+  }
+};
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Launch errors are read back with hipGetLastError(); an error left by an earlier, unrelated
+// HIP call would otherwise be reported against this call's first launch.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+// Stage marker: an external event node while the stream is being captured, a plain record
+// otherwise.
+hipError_t record_event(void* ev, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return e;
+  if (cs == hipStreamCaptureStatusActive)
+    return hipEventRecordWithFlags(static_cast<hipEvent_t>(ev), s, hipEventRecordExternal);
+  return hipEventRecord(static_cast<hipEvent_t>(ev), s);
+}
+
+#define MOE_TRY(expr)                      \
+  do {                                     \
+    const hipError_t _e = (expr);          \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+namespace moe {
+hipError_t record_stage_event(void* ev, hipStream_t s) { return record_event(ev, s); }
+}  // namespace moe
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "size out of range or pointer not 16-byte aligned";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, scoring mode or argument combination";
+    case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_size()";
+    case MOE_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_size(int T, int d, int E, int H, int k, int dtype) {
+  if (check_dims(T, d, E, H, k, dtype) != MOE_OK || T == 0) return 0;
+  return Layout(T, d, E, H, k, dtype).total;
+}
+
+int moe_router_logits(const void* x, const void* w_router, const float* router_bias, int T, int d,
+                      int E, int dtype, float* logits, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || E < 1 || E > moe::kMaxE || d <= 0) return MOE_ERR_SHAPE;
+  if (d % (dtype == MOE_BF16 ? 64 : 4) != 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits) ||
+      (router_bias && !aligned16(router_bias)))
+    return MOE_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  if (dtype == MOE_F32)
+    return hip_status(moe::launch_logits_f32(static_cast<const float*>(x),
+                                             static_cast<const float*>(w_router), router_bias, T,
+                                             d, E, logits, s));
+  return hip_status(moe::launch_logits_bf16(static_cast<const uint16_t*>(x),
+                                            static_cast<const uint16_t*>(w_router), router_bias,
+                                            T, d, E, logits, s));
+}
+
+int moe_route(const float* logits, const float* sel_bias, int T, int E, int k, int scoring,
+              int32_t* topk_ids, float* topk_w, int32_t* expert_counts, void* stream) {
+  int st = check_route_dims(T, E, k);
+  if (st != MOE_OK) return st;
+  st = check_scoring(scoring, sel_bias);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_NULL;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+      !aligned16(expert_counts) || (sel_bias && !aligned16(sel_bias)))
+    return MOE_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(moe::launch_route_from_logits(logits, sel_bias, T, E, k, scoring, topk_ids,
+                                                  topk_w, expert_counts, nullptr, 0,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, int E, int k,
+                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* stream) {
+  const int st = check_route_dims(T, E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !expert_counts || !expert_offsets || !sorted_rows || !row_pos) return MOE_ERR_NULL;
+  if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
+      !aligned16(sorted_rows) || !aligned16(row_pos))
+    return MOE_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(moe::launch_permute(topk_ids, expert_counts, T * k, E, expert_offsets,
+                                        sorted_rows, row_pos, nullptr,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* w_up,
+                   const void* w_down, int E, int H, int k, int dtype,
+                   const int32_t* expert_offsets, const int32_t* sorted_rows, float* expert_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_dims(T, d, E, H, k, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !sorted_rows || !expert_out)
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(expert_offsets) || !aligned16(sorted_rows) || !aligned16(expert_out))
+    return MOE_ERR_SHAPE;
+  const Layout lay(T, d, E, H, k, dtype);
+  if (!ws || ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_SHAPE;
+  DownArgs down{moe::kDownExpertOut, expert_out, sorted_rows, nullptr, k};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  if (dtype == MOE_BF16)
+    return hip_status(moe::launch_ffn_bf16(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
+        static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), T, d, E, H, k,
+        expert_offsets, sorted_rows, at<uint16_t>(ws, lay.h), down, s, nullptr));
+  return hip_status(moe::launch_ffn_f32(
+      static_cast<const float*>(x), static_cast<const float*>(w_gate),
+      static_cast<const float*>(w_up), static_cast<const float*>(w_down), T, d, E, H, k,
+      expert_offsets, sorted_rows, at<float>(ws, lay.h), down, s, nullptr));
+}
+
+int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
+                int d, int k, float* y, void* stream) {
+  if (T < 0 || d <= 0 || d % 4 != 0 || k < 1 || k > moe::kMaxK) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!expert_out || !row_pos || !topk_w || !y) return MOE_ERR_NULL;
+  if (!aligned16(expert_out) || !aligned16(row_pos) || !aligned16(topk_w) || !aligned16(y))
+    return MOE_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(moe::launch_combine(expert_out, row_pos, topk_w, T, d, k, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (!a) return MOE_ERR_NULL;
+  if (a->struct_size < sizeof(moe_layer_args)) return MOE_ERR_UNSUPPORTED;
+  const int T = a->T, d = a->d, E = a->E, H = a->H, k = a->k, dtype = a->dtype;
+  int st = check_dims(T, d, E, H, k, dtype);
+  if (st != MOE_OK) return st;
+  st = check_scoring(a->scoring, a->sel_bias);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!a->x || !a->w_router || !a->w_gate || !a->w_up || !a->w_down || !a->y) return MOE_ERR_NULL;
+  const void* ptrs[] = {a->x, a->w_router, a->router_bias, a->sel_bias, a->w_gate, a->w_up,
+                        a->w_down, a->y, a->logits, a->topk_ids, a->topk_w, a->expert_counts};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_SHAPE;
+  const Layout lay(T, d, E, H, k, dtype);
+  if (!ws || ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  void* const* ev = a->prof_events;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? record_event(ev[i], s) : hipSuccess;
+  };
+
+  int32_t* ids = a->topk_ids ? a->topk_ids : at<int32_t>(ws, lay.ids);
+  float* w = a->topk_w ? a->topk_w : at<float>(ws, lay.w);
+  int32_t* counts = a->expert_counts ? a->expert_counts : at<int32_t>(ws, lay.counts);
+  int32_t* offsets = at<int32_t>(ws, lay.offsets);
+  int32_t* sorted_rows = at<int32_t>(ws, lay.sorted_rows);
+  int32_t* row_pos = at<int32_t>(ws, lay.row_pos);
+  float* zero_y = k == 2 ? a->y : nullptr;
+
+  DownArgs down{};
+  down.sorted_rows = sorted_rows;
+  down.topk_w = w;
+  down.k = k;
+  if (k == 1) {
+    down.mode = moe::kDownStoreY;
+    down.out = a->y;
+  } else if (k == 2) {
+    down.mode = moe::kDownAtomicY;
+    down.out = a->y;
+  } else {
+    down.mode = moe::kDownExpertOut;
+    down.out = at<float>(ws, lay.eo);
+  }
+
+  MOE_TRY(mark(0));
+  if (dtype == MOE_BF16) {
+    MOE_TRY(moe::launch_route_fused_bf16(
+        static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_router),
+        a->router_bias, a->sel_bias, T, d, E, k, a->scoring, a->logits, ids, w, zero_y, s));
+  } else {
+    float* logits = a->logits ? a->logits : at<float>(ws, lay.logits);
+    MOE_TRY(moe::launch_logits_f32(static_cast<const float*>(a->x),
+                                   static_cast<const float*>(a->w_router), a->router_bias, T, d, E,
+                                   logits, s));
+    MOE_TRY(moe::launch_route_from_logits(logits, a->sel_bias, T, E, k, a->scoring, ids, w,
+                                          nullptr, zero_y, d, s));
+  }
+  MOE_TRY(mark(1));
+  MOE_TRY(moe::launch_permute(ids, nullptr, T * k, E, offsets, sorted_rows, row_pos, counts, s));
+  MOE_TRY(mark(2));
+  if (dtype == MOE_BF16) {
+    MOE_TRY(moe::launch_ffn_bf16(
+        static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_gate),
+        static_cast<const uint16_t*>(a->w_up), static_cast<const uint16_t*>(a->w_down), T, d, E,
+        H, k, offsets, sorted_rows, at<uint16_t>(ws, lay.h), down, s, ev ? ev[3] : nullptr));
+  } else {
+    MOE_TRY(moe::launch_ffn_f32(
+        static_cast<const float*>(a->x), static_cast<const float*>(a->w_gate),
+        static_cast<const float*>(a->w_up), static_cast<const float*>(a->w_down), T, d, E, H, k,
+        offsets, sorted_rows, at<float>(ws, lay.h), down, s, ev ? ev[3] : nullptr));
+  }
+  if (k > 2) MOE_TRY(moe::launch_combine(at<float>(ws, lay.eo), row_pos, w, T, d, k, a->y, s));
+  MOE_TRY(mark(4));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+"""Python binding of libmoe.so (include/moe.h): argument marshalling only.
+
+Each function takes torch tensors, checks device/dtype/shape/contiguity, allocates any output the
+caller did not pass (torch owns all device memory), and calls the C entry point of the same name
+on torch's current HIP stream. Every step of the computation runs in the library's HIP kernels;
+there is no other implementation behind these names. If the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_int, c_int32, c_size_t, c_uint32, c_void_p
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = -1
+MOE_ERR_SHAPE = -2
+MOE_ERR_UNSUPPORTED = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_HIP = -5
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+MOE_SCORING_SOFTMAX = 0
+MOE_SCORING_SELECTED_SOFTMAX = 1
+
+SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELECTED_SOFTMAX}
+
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
+           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)} (status {status})")
+
+
+class MoeLayerArgs(Structure):
+    _fields_ = [
+        ("struct_size", c_uint32),
+        ("T", c_int32), ("d", c_int32), ("E", c_int32), ("H", c_int32), ("k", c_int32),
+        ("dtype", c_int32), ("scoring", c_int32),
+        ("x", c_void_p), ("w_router", c_void_p), ("router_bias", c_void_p), ("sel_bias", c_void_p),
+        ("w_gate", c_void_p), ("w_up", c_void_p), ("w_down", c_void_p), ("y", c_void_p),
+        ("logits", c_void_p), ("topk_ids", c_void_p), ("topk_w", c_void_p),
+        ("expert_counts", c_void_p),
+        ("prof_events", c_void_p),   # void* const*: MOE_PROF_EVENTS hipEvent_t handles or NULL
+    ]
+
+
+MOE_PROF_EVENTS = 5
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run expert_routing_grouped_moe_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.moe_abi_version.restype = c_int
+    lib.moe_abi_version.argtypes = []
+    lib.moe_status_string.restype = c_char_p
+    lib.moe_status_string.argtypes = [c_int]
+    lib.moe_workspace_size.restype = c_size_t
+    lib.moe_workspace_size.argtypes = [c_int] * 6
+    lib.moe_router_logits.restype = c_int
+    lib.moe_router_logits.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                      c_void_p, c_void_p]
+    lib.moe_route.restype = c_int
+    lib.moe_route.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                              c_void_p, c_void_p]
+    lib.moe_permute.restype = c_int
+    lib.moe_permute.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                                c_void_p, c_void_p]
+    lib.moe_expert_ffn.restype = c_int
+    lib.moe_expert_ffn.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                   c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]
+    lib.moe_combine.restype = c_int
+    lib.moe_combine.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                                c_void_p]
+    lib.moe_layer_forward.restype = c_int
+    lib.moe_layer_forward.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_size_t, c_void_p]
+    return lib
+
+
+LIB = _load()
+LIB_PATH = _LIB_PATH
+
+
+# ------------------------------------------------------------------------------------ helpers
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        if torch.cuda.is_available():
+            return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: x and weights are float32 or bfloat16")
+
+
+def _need(t, name, shape, dtype=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _scoring_code(scoring) -> int:
+    if isinstance(scoring, str):
+        return SCORING[scoring]
+    return int(scoring)
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# --------------------------------------------------------------------------------- entry points
+
+def moe_abi_version() -> int:
+    return LIB.moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return LIB.moe_status_string(int(status)).decode()
+
+
+def moe_workspace_size(T, d, E, H, k, dtype) -> int:
+    return int(LIB.moe_workspace_size(T, d, E, H, k, dtype))
+
+
+def moe_router_logits(x, w_router, router_bias=None, logits=None, stream=None):
+    T, d = x.shape
+    E = w_router.shape[0]
+    dt = _dtype_code(x)
+    _need(x, "x", (T, d))
+    _need(w_router, "w_router", (E, d), x.dtype)
+    _need(router_bias, "router_bias", (E,), torch.float32)
+    if logits is None:
+        logits = _empty((T, E), torch.float32, x)
+    _need(logits, "logits", (T, E), torch.float32)
+    _check(LIB.moe_router_logits(_ptr(x), _ptr(w_router), _ptr(router_bias), T, d, E, dt,
+                                 _ptr(logits), _stream(stream)), "moe_router_logits")
+    return logits
+
+
+def moe_route(logits, k, scoring, sel_bias=None, topk_ids=None, topk_w=None, expert_counts=None,
+              stream=None):
+    T, E = logits.shape
+    _need(logits, "logits", (T, E), torch.float32)
+    _need(sel_bias, "sel_bias", (E,), torch.float32)
+    topk_ids = _empty((T, k), torch.int32, logits) if topk_ids is None else topk_ids
+    topk_w = _empty((T, k), torch.float32, logits) if topk_w is None else topk_w
+    expert_counts = _empty((E,), torch.int32, logits) if expert_counts is None else expert_counts
+    _need(topk_ids, "topk_ids", (T, k), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(expert_counts, "expert_counts", (E,), torch.int32)
+    _check(LIB.moe_route(_ptr(logits), _ptr(sel_bias), T, E, k, _scoring_code(scoring),
+                         _ptr(topk_ids), _ptr(topk_w), _ptr(expert_counts), _stream(stream)),
+           "moe_route")
+    return topk_ids, topk_w, expert_counts
+
+
+def moe_permute(topk_ids, expert_counts, E, expert_offsets=None, sorted_rows=None, row_pos=None,
+                stream=None):
+    T, k = topk_ids.shape
+    _need(topk_ids, "topk_ids", (T, k), torch.int32)
+    _need(expert_counts, "expert_counts", (E,), torch.int32)
+    expert_offsets = _empty((E + 1,), torch.int32, topk_ids) if expert_offsets is None else expert_offsets
+    sorted_rows = _empty((T * k,), torch.int32, topk_ids) if sorted_rows is None else sorted_rows
+    row_pos = _empty((T * k,), torch.int32, topk_ids) if row_pos is None else row_pos
+    _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
+    _need(sorted_rows, "sorted_rows", (T * k,), torch.int32)
+    _need(row_pos, "row_pos", (T * k,), torch.int32)
+    _check(LIB.moe_permute(_ptr(topk_ids), _ptr(expert_counts), T, E, k, _ptr(expert_offsets),
+                           _ptr(sorted_rows), _ptr(row_pos), _stream(stream)), "moe_permute")
+    return expert_offsets, sorted_rows, row_pos
+
+
+def moe_expert_ffn(x, w_gate, w_up, w_down, k, expert_offsets, sorted_rows, expert_out=None,
+                   workspace=None, stream=None):
+    T, d = x.shape
+    E, H, _ = w_gate.shape
+    dt = _dtype_code(x)
+    _need(x, "x", (T, d))
+    _need(w_gate, "w_gate", (E, H, d), x.dtype)
+    _need(w_up, "w_up", (E, H, d), x.dtype)
+    _need(w_down, "w_down", (E, d, H), x.dtype)
+    _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
+    _need(sorted_rows, "sorted_rows", (T * k,), torch.int32)
+    expert_out = _empty((T * k, d), torch.float32, x) if expert_out is None else expert_out
+    _need(expert_out, "expert_out", (T * k, d), torch.float32)
+    ws_bytes = moe_workspace_size(T, d, E, H, k, dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _check(LIB.moe_expert_ffn(_ptr(x), T, d, _ptr(w_gate), _ptr(w_up), _ptr(w_down), E, H, k, dt,
+                              _ptr(expert_offsets), _ptr(sorted_rows), _ptr(expert_out),
+                              _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_expert_ffn")
+    return expert_out
+
+
+def moe_combine(expert_out, row_pos, topk_w, y=None, stream=None):
+    T, k = topk_w.shape
+    d = expert_out.shape[1]
+    _need(expert_out, "expert_out", (T * k, d), torch.float32)
+    _need(row_pos, "row_pos", (T * k,), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    y = _empty((T, d), torch.float32, expert_out) if y is None else y
+    _need(y, "y", (T, d), torch.float32)
+    _check(LIB.moe_combine(_ptr(expert_out), _ptr(row_pos), _ptr(topk_w), T, d, k, _ptr(y),
+                           _stream(stream)), "moe_combine")
+    return y
+
+
+def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias=None,
+                    sel_bias=None, logits=None, topk_ids=None, topk_w=None, expert_counts=None):
+    T, d = x.shape
+    E, H, _ = w_gate.shape
+    _need(x, "x", (T, d))
+    _need(w_router, "w_router", (E, d), x.dtype)
+    _need(w_gate, "w_gate", (E, H, d), x.dtype)
+    _need(w_up, "w_up", (E, H, d), x.dtype)
+    _need(w_down, "w_down", (E, d, H), x.dtype)
+    _need(router_bias, "router_bias", (E,), torch.float32)
+    _need(sel_bias, "sel_bias", (E,), torch.float32)
+    _need(y, "y", (T, d), torch.float32)
+    _need(logits, "logits", (T, E), torch.float32)
+    _need(topk_ids, "topk_ids", (T, k), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(expert_counts, "expert_counts", (E,), torch.int32)
+    a = MoeLayerArgs()
+    a.struct_size = ctypes.sizeof(MoeLayerArgs)
+    a.T, a.d, a.E, a.H, a.k = T, d, E, H, k
+    a.dtype = _dtype_code(x)
+    a.scoring = _scoring_code(scoring)
+    for name, t in (("x", x), ("w_router", w_router), ("router_bias", router_bias),
+                    ("sel_bias", sel_bias), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down),
+                    ("y", y), ("logits", logits), ("topk_ids", topk_ids), ("topk_w", topk_w),
+                    ("expert_counts", expert_counts)):
+        setattr(a, name, None if t is None else t.data_ptr())
+    return a
+
+
+def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
+                      sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
+                      expert_counts=None, workspace=None, stream=None, args=None):
+    """The fused layer. Returns y [T, d] fp32. Optional outputs are written when passed."""
+    T, d = x.shape
+    E, H, _ = w_gate.shape
+    y = _empty((T, d), torch.float32, x) if y is None else y
+    if args is None:
+        args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias,
+                               sel_bias, logits, topk_ids, topk_w, expert_counts)
+    ws_bytes = moe_workspace_size(T, d, E, H, k, args.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _check(LIB.moe_layer_forward(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "moe_layer_forward")
+    return y

@@ -1,0 +1,210 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) mixture-of-experts layer library, libmoe.so.
+ *
+ * The layer is the MoE block of the ZONOS2 and ZONOS3-Mini TTS backbones:
+ *   router logits -> top-k expert selection + routing weights -> dispatch (grouping of the
+ *   token-to-expert assignments by expert) -> per-expert SwiGLU FFN -> weighted combine.
+ *
+ * Sources of the definitions (cited by page title and section):
+ *   - zonos2.cpp INTERNALS, "Model architecture" table, MoE row: 16 experts, top-1.
+ *   - zonos2.cpp INTERNALS, "Model architecture" table, Router row: prob-weighted, no-renorm
+ *     top-k (ZONOS2 scoring: softmax over all experts, each chosen expert weighted by its full
+ *     probability).
+ *   - audio.cpp PR #1271 "New Community Model: ZONOS3-Mini", "Framework change": SelectedSoftmax
+ *     scoring (rank experts by raw logit plus a per-expert selection bias, take the top k, then
+ *     weight them by the softmax of their raw logits over the selected set only).
+ *   - audio.cpp PR #1271, "Summary": top-2-of-64 MoE at width 1024; SwiGLU FFN.
+ *   - zonos2.cpp INTERNALS, "Recommended: F16 spine + K-quant experts": expert weights are
+ *     3-D gate/up/down stacks.
+ *   - zonos2.cpp INTERNALS, "Notes": activation and residual streams are F32; token-major
+ *     [T, C] activations (ggml's [C, T] in reversed order).
+ *   - zonos2.cpp INTERNALS, "Performance": the decode graph is replayed as a captured graph,
+ *     so every call here is capturable (no host synchronisation, no allocation).
+ *
+ * Conventions shared by every entry point
+ *   Pointers     Every tensor pointer is a DEVICE pointer, borrowed for the duration of the
+ *                stream work the call enqueues. The library allocates nothing and keeps no
+ *                state between calls; buffers must stay alive until the stream has passed the
+ *                call. Tensors are dense row-major (C order) with no padding.
+ *   Alignment    Every tensor pointer must be 16-byte aligned (MOE_ERR_SHAPE otherwise).
+ *   Stream       `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call is
+ *                asynchronous: it only enqueues kernels. No call reads device memory on the host,
+ *                synchronises, or allocates, so every call may be captured into a HIP graph.
+ *                Launch shapes depend only on the scalar arguments, never on routing results.
+ *   Dtypes       `dtype` (MOE_F32 or MOE_BF16) is the type of x and of every weight matrix.
+ *                Logits, biases, routing weights, expert outputs and y are always fp32.
+ *   Errors       A negative return means nothing was enqueued, except MOE_ERR_HIP, which reports
+ *                a failed launch (work enqueued before it by the same call may have run).
+ *                Device data is never validated: NaN logits or expert ids outside [0, E) are
+ *                outside the contract. No C++ exception crosses this interface.
+ *   Shapes       1 <= E <= 256, 1 <= k <= min(E, 8), T >= 0 (T == 0 enqueues nothing and
+ *                returns MOE_OK), T * k < 2^31, d and H multiples of 64 (bf16) or of 4 (fp32),
+ *                d, H >= 64 for bf16. Violations return MOE_ERR_SHAPE / MOE_ERR_UNSUPPORTED.
+ *   Reentrancy   Stateless and thread-safe; calls on different streams may run concurrently
+ *                when their buffers do not overlap.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL                                    */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range, or a pointer is not 16-byte aligned   */
+  MOE_ERR_UNSUPPORTED = -3, /* unknown dtype/scoring, or an argument combination not defined */
+  MOE_ERR_WORKSPACE = -4,   /* workspace pointer NULL or smaller than moe_workspace_size()   */
+  MOE_ERR_HIP = -5          /* a HIP launch failed                                           */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+enum moe_scoring {
+  /* ZONOS2 (zonos2.cpp INTERNALS, "Model architecture", Router row): rank experts by logit
+     (equivalently by softmax probability), weight each chosen expert by its softmax probability
+     over ALL E experts, no renormalisation. sel_bias must be NULL in this mode. */
+  MOE_SCORING_SOFTMAX = 0,
+  /* ZONOS3-Mini (audio.cpp PR #1271, "Framework change"): rank by fp32(logit + sel_bias[e])
+     (one round-to-nearest-even add), take the top k, weight them by the softmax of their raw
+     logits over the k selected experts only (weights sum to 1; k = 1 gives exactly 1). */
+  MOE_SCORING_SELECTED_SOFTMAX = 1
+};
+
+/* Returns MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/* Bytes of device workspace that moe_expert_ffn and moe_layer_forward need for these sizes
+   (0 when T == 0). The value depends only on the arguments. Returns 0 for invalid sizes. */
+size_t moe_workspace_size(int T, int d, int E, int H, int k, int dtype);
+
+/*
+ * Router logits, step 1 (zonos2.cpp INTERNALS, "Model architecture", Router row; the router here
+ * is a plain linear map, the pages do not define the EDA router's internals):
+ *   logits[t, e] = sum_i x[t, i] * w_router[e, i] + router_bias[e]
+ *   x         [T, d]  dtype      token activations
+ *   w_router  [E, d]  dtype      router weight
+ *   router_bias [E]   fp32/NULL  added to every token's logits (NULL = no bias)
+ *   logits    [T, E]  fp32       output; accumulated in fp32 (bf16 products are exact in fp32)
+ */
+int moe_router_logits(const void* x, const void* w_router, const float* router_bias,
+                      int T, int d, int E, int dtype, float* logits, void* stream);
+
+/*
+ * Routing, steps 2-3: top-k selection, routing weights and per-expert counts on GIVEN fp32 logits
+ * (audio.cpp PR #1271, "Framework change"; zonos2.cpp INTERNALS, "Model architecture", Router
+ * row). Selection orders experts by (score descending, expert index ascending), where
+ * score = logits (SOFTMAX) or fp32(logits + sel_bias) (SELECTED_SOFTMAX); -0.0 equals +0.0.
+ * Slot 0 holds the best expert. Indices and counts are exact integers: identical logits give
+ * identical results on every call.
+ *   logits        [T, E] fp32   input
+ *   sel_bias      [E]    fp32   SELECTED_SOFTMAX only (may be NULL = zero bias); must be NULL
+ *                               for SOFTMAX (MOE_ERR_UNSUPPORTED otherwise)
+ *   topk_ids      [T, k] int32  output, expert id per slot
+ *   topk_w        [T, k] fp32   output, routing weight per slot (fp32 exp; ~1e-7 relative)
+ *   expert_counts [E]    int32  output, number of (token, slot) assignments per expert
+ *                               (overwritten, not accumulated)
+ */
+int moe_route(const float* logits, const float* sel_bias, int T, int E, int k, int scoring,
+              int32_t* topk_ids, float* topk_w, int32_t* expert_counts, void* stream);
+
+/*
+ * Dispatch, step 4: groups the T*k assignment rows r = t*k + j by expert. The pages name the
+ * grouped expert matmul over the expert stacks (zonos2.cpp INTERNALS, "Performance": mul_mat_id
+ * over the expert stacks) but not its bookkeeping; this call fixes it:
+ *   expert_offsets[e] = sum_{e' < e} expert_counts[e'],  expert_offsets[E] = T*k
+ *   sorted_rows[expert_offsets[e] + i] = the i-th row r (ascending r) with topk_ids[r] == e
+ *   row_pos[r] = the position of row r in sorted_rows (the inverse permutation)
+ *   topk_ids      [T, k]  int32  input (values must be in [0, E))
+ *   expert_counts [E]     int32  input (must equal the histogram of topk_ids)
+ *   expert_offsets[E + 1] int32  output
+ *   sorted_rows   [T * k] int32  output
+ *   row_pos       [T * k] int32  output
+ * All results are exact integers, identical on every call.
+ */
+int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, int E, int k,
+                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* stream);
+
+/*
+ * Expert FFN, steps 5-6: for every expert e and every row at position p of its group
+ * (expert_offsets[e] <= p < expert_offsets[e+1]), with token t = sorted_rows[p] / k:
+ *   g = w_gate[e] x[t],  u = w_up[e] x[t],  h = silu(g) * u,  expert_out[p] = w_down[e] h
+ * with silu(z) = z / (1 + exp(-z)) (audio.cpp PR #1271, "Summary": SwiGLU FFN; zonos2.cpp
+ * INTERNALS, "Recommended: F16 spine + K-quant experts": ffn_{gate,up,down}_exps stacks).
+ *   x          [T, d]     dtype
+ *   w_gate     [E, H, d]  dtype
+ *   w_up       [E, H, d]  dtype
+ *   w_down     [E, d, H]  dtype
+ *   expert_offsets [E+1], sorted_rows [T*k]: as produced by moe_permute
+ *   expert_out [T*k, d]   fp32 output, in grouped (sorted) order
+ *   ws, ws_bytes          device workspace of at least moe_workspace_size(T, d, E, H, k, dtype)
+ * bf16: products on MFMA with fp32 accumulation; h is rounded to bf16 before the down matmul.
+ * fp32: fp32 FMA throughout.
+ */
+int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* w_up,
+                   const void* w_down, int E, int H, int k, int dtype,
+                   const int32_t* expert_offsets, const int32_t* sorted_rows, float* expert_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine, step 7: y[t] = sum_{j=0}^{k-1} topk_w[t, j] * expert_out[row_pos[t*k + j]], summed in
+ * slot order in fp32 (zonos2.cpp INTERNALS, "Model architecture", Router row: prob-weighted sum;
+ * "Notes": F32 residual stream).
+ *   expert_out [T*k, d] fp32, row_pos [T*k] int32, topk_w [T, k] fp32 -> y [T, d] fp32
+ */
+int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
+                int d, int k, float* y, void* stream);
+
+/* Arguments of the fused layer call. Set struct_size = sizeof(struct moe_layer_args). */
+typedef struct moe_layer_args {
+  uint32_t struct_size;
+  int32_t T, d, E, H, k;
+  int32_t dtype;             /* MOE_F32 or MOE_BF16: x and all weights                    */
+  int32_t scoring;           /* enum moe_scoring                                          */
+  const void* x;             /* [T, d]                                                    */
+  const void* w_router;      /* [E, d]                                                    */
+  const float* router_bias;  /* [E] or NULL; part of the logits (enters the weights)      */
+  const float* sel_bias;     /* [E] or NULL; SELECTED_SOFTMAX ranking only                */
+  const void* w_gate;        /* [E, H, d]                                                 */
+  const void* w_up;          /* [E, H, d]                                                 */
+  const void* w_down;        /* [E, d, H]                                                 */
+  float* y;                  /* [T, d] fp32 output                                        */
+  /* Optional outputs (NULL = not written). */
+  float* logits;             /* [T, E] fp32 router logits                                 */
+  int32_t* topk_ids;         /* [T, k]                                                    */
+  float* topk_w;             /* [T, k]                                                    */
+  int32_t* expert_counts;    /* [E]                                                       */
+  /* Optional stage timing (NULL = none): an array of MOE_PROF_EVENTS hipEvent_t handles passed
+     as void*. an event record of prof_events[i] is enqueued at each stage boundary
+     (an external event node, hipEventRecordExternal, while the stream is being captured):
+     [0] before routing, [1] after routing (logits, top-k, weights), [2] after dispatch,
+     [3] after gate/up + SwiGLU, [4] after down projection and combine. The events are owned by
+     the caller. */
+  void* const* prof_events;
+} moe_layer_args;
+
+#define MOE_PROF_EVENTS 5
+
+/*
+ * The whole layer, steps 1-7, as one capturable sequence of kernels on `stream`:
+ *   y = moe_combine(moe_expert_ffn(x, moe_permute(moe_route(moe_router_logits(x)))))
+ * Routing (ids, weights, counts) equals moe_route applied to the logits this call computes
+ * (write them out through `logits` to check). Internally the combine is fused into the down
+ * matmul where that stays deterministic (k <= 2). ws must hold moe_workspace_size(...) bytes.
+ */
+int moe_layer_forward(const moe_layer_args* args, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

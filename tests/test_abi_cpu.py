@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and rejects
+bad arguments before touching the device (CPU only; no call here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_routing_grouped_moe_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced by these calls
+MISALIGNED = ctypes.c_void_p(0x100004)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert declared_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert moe.moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert moe.moe_status_string(st) and moe.moe_status_string(st) != "unknown status"
+    assert moe.moe_status_string(7) == "unknown status"
+
+
+def test_workspace_size():
+    L = moe.LIB
+    assert L.moe_workspace_size(0, 128, 8, 256, 1, 0) == 0
+    assert L.moe_workspace_size(64, 100, 8, 256, 1, 1) == 0          # d % 64 for bf16
+    assert L.moe_workspace_size(64, 128, 8, 256, 9, 0) == 0          # k > 8
+    a = L.moe_workspace_size(64, 2048, 16, 2816, 1, 1)
+    b = L.moe_workspace_size(128, 2048, 16, 2816, 1, 1)
+    assert 0 < a < b
+    # h (bf16) alone is T*k*H*2 bytes
+    assert a >= 64 * 2816 * 2
+    # k > 2 adds the fp32 expert_out staging
+    assert L.moe_workspace_size(64, 128, 8, 256, 3, 0) > L.moe_workspace_size(64, 128, 8, 256, 2, 0) * 1.5
+
+
+def test_route_validation():
+    L = moe.LIB
+    call = lambda logits, sb, T, E, k, sc, ids=FAKE, w=FAKE, c=FAKE: L.moe_route(
+        logits, sb, T, E, k, sc, ids, w, c, None)
+    assert call(FAKE, None, 0, 8, 1, 0) == moe.MOE_OK                  # T == 0: nothing to do
+    assert call(FAKE, None, 4, 0, 1, 0) == moe.MOE_ERR_SHAPE
+    assert call(FAKE, None, 4, 257, 1, 0) == moe.MOE_ERR_SHAPE
+    assert call(FAKE, None, 4, 8, 0, 0) == moe.MOE_ERR_SHAPE
+    assert call(FAKE, None, 4, 4, 5, 0) == moe.MOE_ERR_SHAPE           # k > E
+    assert call(FAKE, None, 4, 64, 9, 0) == moe.MOE_ERR_SHAPE          # k > 8
+    assert call(FAKE, None, -1, 8, 1, 0) == moe.MOE_ERR_SHAPE
+    assert call(FAKE, None, 4, 8, 1, 7) == moe.MOE_ERR_UNSUPPORTED
+    assert call(FAKE, FAKE, 4, 8, 1, 0) == moe.MOE_ERR_UNSUPPORTED     # bias needs SelectedSoftmax
+    assert call(None, None, 4, 8, 1, 0) == moe.MOE_ERR_NULL
+    assert call(FAKE, None, 4, 8, 1, 1, ids=None) == moe.MOE_ERR_NULL
+    assert call(MISALIGNED, None, 4, 8, 1, 0) == moe.MOE_ERR_SHAPE
+    assert call(FAKE, MISALIGNED, 4, 8, 1, 1) == moe.MOE_ERR_SHAPE
+
+
+def test_permute_combine_logits_validation():
+    L = moe.LIB
+    assert L.moe_permute(FAKE, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, None) == moe.MOE_OK
+    assert L.moe_permute(FAKE, FAKE, 4, 8, 9, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_permute(FAKE, None, 4, 8, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_NULL
+    assert L.moe_permute(FAKE, FAKE, 4, 8, 1, FAKE, MISALIGNED, FAKE, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 6, 1, FAKE, None) == moe.MOE_ERR_SHAPE     # d % 4
+    assert L.moe_combine(FAKE, None, FAKE, 4, 8, 1, FAKE, None) == moe.MOE_ERR_NULL
+    assert L.moe_combine(FAKE, FAKE, FAKE, 0, 8, 1, FAKE, None) == moe.MOE_OK
+    assert L.moe_router_logits(FAKE, FAKE, None, 4, 128, 8, 2, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_router_logits(FAKE, FAKE, None, 4, 96, 8, 1, FAKE, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_router_logits(FAKE, None, None, 4, 128, 8, 1, FAKE, None) == moe.MOE_ERR_NULL
+
+
+def test_expert_ffn_validation():
+    L = moe.LIB
+    ws = L.moe_workspace_size(16, 128, 8, 256, 1, 1)
+    f = lambda T=16, d=128, E=8, H=256, k=1, dt=1, ws_ptr=FAKE, ws_bytes=ws, x=FAKE: L.moe_expert_ffn(
+        x, T, d, FAKE, FAKE, FAKE, E, H, k, dt, FAKE, FAKE, FAKE, ws_ptr, ws_bytes, None)
+    assert f(T=0) == moe.MOE_OK
+    assert f(d=96) == moe.MOE_ERR_SHAPE
+    assert f(H=100) == moe.MOE_ERR_SHAPE
+    assert f(dt=5) == moe.MOE_ERR_UNSUPPORTED
+    assert f(ws_ptr=None) == moe.MOE_ERR_WORKSPACE
+    assert f(ws_bytes=ws - 1) == moe.MOE_ERR_WORKSPACE
+    assert f(x=None) == moe.MOE_ERR_NULL
+    assert f(x=MISALIGNED) == moe.MOE_ERR_SHAPE
+
+
+def _args(**kw):
+    a = moe.MoeLayerArgs()
+    a.struct_size = ctypes.sizeof(moe.MoeLayerArgs)
+    a.T, a.d, a.E, a.H, a.k, a.dtype, a.scoring = 16, 128, 8, 256, 1, 1, 0
+    for name in ("x", "w_router", "w_gate", "w_up", "w_down", "y"):
+        setattr(a, name, FAKE.value)
+    for key, v in kw.items():
+        setattr(a, key, v)
+    return a
+
+
+def test_layer_forward_validation():
+    L = moe.LIB
+    ws = L.moe_workspace_size(16, 128, 8, 256, 1, 1)
+    run = lambda a, w=FAKE, n=ws: L.moe_layer_forward(ctypes.byref(a), w, n, None)
+    assert L.moe_layer_forward(None, FAKE, ws, None) == moe.MOE_ERR_NULL
+    assert run(_args(struct_size=8)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(T=0)) == moe.MOE_OK
+    assert run(_args(k=3, E=2)) == moe.MOE_ERR_SHAPE
+    assert run(_args(scoring=4)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(sel_bias=FAKE.value)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(x=None)) == moe.MOE_ERR_NULL
+    assert run(_args(y=MISALIGNED.value)) == moe.MOE_ERR_SHAPE
+    assert run(_args(logits=MISALIGNED.value)) == moe.MOE_ERR_SHAPE
+    assert run(_args(), n=ws - 256) == moe.MOE_ERR_WORKSPACE
+    assert run(_args(), w=None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_binding_checks_shapes_before_calling():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_router_logits(x, torch.zeros(8, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        moe.moe_router_logits(x.half(), torch.zeros(8, 128, dtype=torch.half))

@@ -1,0 +1,131 @@
+"""moe_layer_forward on the GPU against the fp64 oracle: the five workloads at full size (the
+largest compared on a token sample), edge cases, determinism and HIP-graph replay."""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as orc
+from expert_routing_grouped_moe_amd import inputs as gen
+
+from _parity import DEV, check_layer, run_layer, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(T, n, seed):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    s = rng.choice(T, size=n, replace=False)
+    return np.sort(np.concatenate([s, [0, T - 1]]))
+
+
+@pytest.mark.parametrize("name", gen.WORKLOAD_ORDER)
+def test_layer_workload(name):
+    inp = gen.make_inputs(name)
+    res = run_layer(inp)
+    tokens = _sample(inp.T, 1024 if inp.T > 4096 else inp.T, seed=7)
+    rep = check_layer(inp, res, tokens=tokens)
+    print(f"{name}: {rep}")
+    # the layer's ids equal moe_route on the logits the layer computed (same fp32 values)
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    ids, w, counts = moe.moe_route(torch.from_numpy(res["logits"]).to(DEV), inp.k, inp.scoring,
+                                   sel_bias=None if inp.sel_bias is None else
+                                   torch.from_numpy(inp.sel_bias).to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), res["topk_ids"])
+    np.testing.assert_array_equal(counts.cpu().numpy(), res["expert_counts"])
+    np.testing.assert_array_equal(w.cpu().numpy(), res["topk_w"])
+
+
+def test_skewed_workload_loads():
+    inp = gen.make_inputs("zonos2-skewed-prefill")
+    res = run_layer(inp, with_logits=False)
+    c = res["expert_counts"]
+    assert c[14] == 0 and c[15] == 0
+    assert abs(c[0] / inp.T - 0.40) < 0.03
+
+
+EDGE = [
+    # name, T, d, E, k, H, scoring, dtype, sel_bias_var, router_bias
+    ("T1-bf16", 1, 128, 16, 1, 128, orc.SOFTMAX, "bf16", None, None),
+    ("T1-f32", 1, 64, 8, 2, 64, orc.SELECTED_SOFTMAX, "f32", 0.5, None),
+    ("ragged-bf16", 37, 256, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("E1", 50, 128, 1, 1, 128, orc.SOFTMAX, "bf16", None, None),
+    ("kE-f32", 40, 64, 8, 8, 64, orc.SOFTMAX, "f32", None, None),
+    ("k3-bf16", 90, 128, 16, 3, 192, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("E256-k8", 64, 128, 256, 8, 64, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("all-one-expert", 500, 128, 16, 1, 256, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("prefill-ragged", 1111, 192, 8, 2, 320, orc.SOFTMAX, "bf16", None, None),
+    ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_layer_edge_cases(case):
+    name, T, d, E, k, H, scoring, dtype, sbv, rb = case
+    router_bias = None
+    if rb == "hot5":
+        router_bias = np.full(E, -30.0, np.float32)
+        router_bias[5] = 30.0
+    inp = gen.make_inputs_custom(T, d, E, k, H, scoring, dtype, seed=T + E + k,
+                                 sel_bias_var=sbv, router_bias=router_bias)
+    res = run_layer(inp)
+    rep = check_layer(inp, res)
+    print(f"{name}: {rep}")
+    if rb == "hot5":
+        assert res["expert_counts"][5] == T
+
+
+def test_layer_T0_is_noop():
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs_custom(4, 128, 8, 1, 128, orc.SOFTMAX, "bf16", seed=1)
+    dev = upload(inp)
+    y = torch.full((0, 128), 7.0, device=DEV)
+    moe.moe_layer_forward(dev["x"][:0], dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                          1, "softmax", y=y)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill"])
+def test_layer_deterministic(name):
+    inp = gen.make_inputs(name)
+    dev = upload(inp)
+    a = run_layer(inp, dev)
+    b = run_layer(inp, dev)
+    for key in ("y", "topk_ids", "topk_w", "expert_counts", "logits"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["zonos2-decode", "zonos3mini-decode-cfg", "tiny-fp32"])
+def test_layer_graph_replay(name):
+    """The fused call captured in a HIP graph and replayed; every replay equals the eager run."""
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs(name)
+    dev = upload(inp)
+    T, d, E, H, k = inp.T, inp.d, inp.E, inp.H, inp.k
+    y = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    ws = torch.empty(moe.moe_workspace_size(T, d, E, H, k, 1 if inp.dtype == "bf16" else 0),
+                     dtype=torch.uint8, device=DEV)
+    args = moe.make_layer_args(dev["x"], dev["w_router"], dev["w_gate"], dev["w_up"],
+                               dev["w_down"], k, inp.scoring, y, dev["router_bias"],
+                               dev["sel_bias"])
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        moe.moe_layer_forward(dev["x"], dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                              k, inp.scoring, y=y, workspace=ws, args=args)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        moe.moe_layer_forward(dev["x"], dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                              k, inp.scoring, y=y, workspace=ws, args=args)
+    for i in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {i} differs"

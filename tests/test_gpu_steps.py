@@ -1,0 +1,101 @@
+"""The step entry points on the GPU against the oracle: router logits (within the fp32 error
+bound), dispatch (bit-exact), expert FFN and combine (within the float tolerances)."""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as orc
+from expert_routing_grouped_moe_amd import inputs as gen
+
+from _parity import DEV, TOL, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+@pytest.mark.parametrize("name", gen.WORKLOAD_ORDER)
+def test_router_logits_within_bound(name):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs(name)
+    dev = upload(inp)
+    L = moe.moe_router_logits(dev["x"], dev["w_router"], dev["router_bias"])
+    torch.cuda.synchronize()
+    L = L.cpu().numpy().astype(np.float64)
+    ref = orc.router_logits_ref(inp.x, inp.w_router, inp.router_bias)
+    B = orc.logit_error_bound(inp.x, inp.w_router, inp.router_bias)
+    assert (np.abs(L - ref) <= B[:, None]).all()
+    # the rigorous bound is loose; the typical error is far below it
+    assert np.abs(L - ref).max() < 1e-3
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (64, 8, 1), (64, 64, 2), (1000, 16, 1), (8192, 16, 1),
+                                   (4096, 64, 2), (333, 256, 8), (3000, 5, 3)])
+def test_permute_bit_exact(T, E, k):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    L = gen.make_logits(T, E, seed=T * 7 + E, kind="ties")
+    ids, _, counts = orc.route_ref(L, None, k, orc.SOFTMAX)
+    off, rows, pos = moe.moe_permute(_t(ids.astype(np.int32)), _t(counts.astype(np.int32)), E)
+    torch.cuda.synchronize()
+    roff, rrows, rpos = orc.permute_ref(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), roff)
+    np.testing.assert_array_equal(rows.cpu().numpy(), rrows)
+    np.testing.assert_array_equal(pos.cpu().numpy(), rpos)
+
+
+def test_permute_all_to_one_expert_and_empty():
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    T, E, k = 5000, 64, 1
+    ids = np.full((T, k), 17, dtype=np.int64)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    off, rows, pos = moe.moe_permute(_t(ids.astype(np.int32)), _t(counts.astype(np.int32)), E)
+    torch.cuda.synchronize()
+    roff, rrows, rpos = orc.permute_ref(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), roff)
+    np.testing.assert_array_equal(rows.cpu().numpy(), rrows)
+    np.testing.assert_array_equal(pos.cpu().numpy(), rpos)
+
+
+FFN_CASES = [
+    # name, T, d, E, k, H, dtype   (avg rows per expert decides decode vs prefill kernels)
+    ("f32-tiny", 64, 128, 8, 1, 256, "f32"),
+    ("f32-ragged", 37, 64, 5, 3, 96, "f32"),
+    ("bf16-decode-k1", 64, 512, 16, 1, 384, "bf16"),
+    ("bf16-decode-k2", 64, 256, 64, 2, 256, "bf16"),
+    ("bf16-decode-mt2", 300, 256, 16, 1, 256, "bf16"),
+    ("bf16-prefill", 700, 256, 4, 2, 384, "bf16"),
+    ("bf16-prefill-odd", 517, 192, 3, 1, 320, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+def test_expert_ffn_and_combine(case):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    _, T, d, E, k, H, dtype = case
+    inp = gen.make_inputs_custom(T, d, E, k, H, orc.SOFTMAX, dtype, seed=T + d + E)
+    dev = upload(inp)
+    # routing from the oracle (fp64 logits), so the FFN sees exactly the oracle's grouping
+    L = orc.router_logits_ref(inp.x, inp.w_router)
+    ids = orc.select_topk_ref(L, k)
+    w = orc.routing_weights_ref(L, ids, orc.SOFTMAX)
+    off, rows, pos = orc.permute_ref(ids, E)
+    eo = moe.moe_expert_ffn(dev["x"], dev["w_gate"], dev["w_up"], dev["w_down"], k,
+                            _t(off.astype(np.int32)), _t(rows.astype(np.int32)))
+    y = moe.moe_combine(eo, _t(pos.astype(np.int32)), _t(w.astype(np.float32)))
+    torch.cuda.synchronize()
+    eo_ref = orc.expert_ffn_ref(inp.x, inp.w_gate, inp.w_up, inp.w_down, off, rows, k)
+    y_ref = orc.combine_ref(eo_ref, pos, w.astype(np.float32), k)
+    tol = TOL[dtype]
+    eo_err = np.abs(eo.cpu().numpy() - eo_ref).max()
+    assert eo_err <= tol * np.sqrt(np.mean(eo_ref ** 2)), eo_err
+    y_err = np.abs(y.cpu().numpy() - y_ref).max()
+    assert y_err <= tol * np.sqrt(np.mean(y_ref ** 2)), y_err
