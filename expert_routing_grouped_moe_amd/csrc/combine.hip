@@ -21,7 +21,8 @@ __global__ void combine_kernel(const float* __restrict__ eo, const int32_t* __re
   for (int j = 0; j < k; ++j) {
     const long long r = static_cast<long long>(t) * k + j;
     const float wt = w[r];
-    const float4 o = reinterpret_cast<const float4*>(eo + static_cast<long long>(row_pos[r]) * d)[c];
+    const long long src = row_pos ? row_pos[r] : r;
+    const float4 o = reinterpret_cast<const float4*>(eo + src * d)[c];
     acc.x = acc.x + wt * o.x;
     acc.y = acc.y + wt * o.y;
     acc.z = acc.z + wt * o.z;

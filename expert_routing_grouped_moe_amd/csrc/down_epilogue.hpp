@@ -6,9 +6,10 @@
 
 namespace moe {
 
-// o = expert output at grouped position p, column n (of d). Combine rule (zonos2.cpp INTERNALS,
-// "Model architecture" table, Router row: the chosen experts' outputs are summed with their
-// routing weights; "Notes": the residual stream is F32):
+// o = expert output of assignment row r (token t = r / k, slot j = r % k), stored at position p
+// of the expert-output array. Combine rule (zonos2.cpp INTERNALS, "Model architecture" table,
+// Router row: the chosen experts' outputs are summed with their routing weights; "Notes": the
+// residual stream is F32):
 //   kDownExpertOut  expert_out[p, n] = o
 //   kDownStoreY     y[t, n] = w[t, j] * o           (k == 1)
 //   kDownAtomicY    y[t, n] += w[t, j] * o          (k == 2, y cleared beforehand; two addends
@@ -18,18 +19,16 @@ struct DownRow {
   float scale;  // routing weight (1 for expert_out)
 };
 
-__device__ __forceinline__ DownRow down_row(const DownArgs& a, int p, int d) {
-  DownRow r;
+__device__ __forceinline__ DownRow down_row(const DownArgs& a, int r, int p, int d) {
+  DownRow out;
   if (a.mode == kDownExpertOut) {
-    r.dst = a.out + static_cast<long long>(p) * d;
-    r.scale = 1.0f;
+    out.dst = a.out + static_cast<long long>(p) * d;
+    out.scale = 1.0f;
   } else {
-    const int row = a.sorted_rows[p];
-    const int t = row / a.k;
-    r.dst = a.out + static_cast<long long>(t) * d;
-    r.scale = a.topk_w[row];
+    out.dst = a.out + static_cast<long long>(r / a.k) * d;
+    out.scale = a.topk_w[r];
   }
-  return r;
+  return out;
 }
 
 __device__ __forceinline__ void down_put(const DownArgs& a, const DownRow& r, int n, float o) {

@@ -7,10 +7,13 @@
 // K-quant experts") are stored.
 //
 // Two kernels, chosen on the host from the static shape (average rows per expert):
-//  * decode (few rows per expert): the layer is a read of the touched experts' weights (the
-//    single-stream regime of the ZONOS2-4bit MLX card, "Performance notes"). Weight rows stream
-//    from HBM straight into registers, 64 contiguous bytes per lane per 128-k block, double
-//    buffered; the 16 (or 32) gathered token rows sit in LDS and are reused by every wave.
+//  * streaming (few rows per expert, decode): the layer is a read of the touched experts'
+//    weights (the single-stream regime of the ZONOS2-4bit MLX card, "Performance notes"). One
+//    one-wave block per (16-feature slab, expert); weight rows stream from HBM straight into
+//    registers (each load instruction covers 64 contiguous bytes of 16 rows), two 128-k blocks in
+//    flight, with the expert's token rows read alongside from L2. The block finds its expert's
+//    rows itself (from the dispatch order, or by scanning the expert ids), so the decode layer
+//    needs no dispatch kernel.
 //  * prefill (many rows per expert): a grouped GEMM with 128 x 128 block tiles, A (gathered rows)
 //    and B (weights) staged through double-buffered LDS, 2 x 2 waves of 64 x 64 each.
 #include "common.hpp"
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
           }
         }
       } else {
-        const DownRow dr = down_row(down, p, N);
+        const DownRow dr = down_row(down, sorted_rows[p], p, N);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int f = n0 + wn * 64 + cb * 16 + l16;
@@ -158,171 +161,169 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
   }
 }
 
-// ------------------------------------------------------------------------------------- decode
+// ------------------------------------------------------------------------------ streaming
 
-constexpr int kDcFeat = 16;                 // output features per wave
-constexpr int kDcBlockFeat = 4 * kDcFeat;   // per block of 4 waves
+constexpr int kStFeat = 16;  // output features per block (one wave)
 
-template <bool GATEUP, int MT>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
-    const uint16_t* __restrict__ W1, int K, int N, int E, int k,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
-    uint16_t* __restrict__ h_out, DownArgs down) {
-  constexpr int BM = 16 * MT;
-  constexpr int KC = 1024 / MT;             // k staged in LDS per chunk
-  constexpr int LD = KC + 8;                // pitch in bf16; 16 rows land on distinct bank groups
-  __shared__ int sh_tiles[2 * (kMaxE + 1)];
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LD];
-
-  const TileInfo ti = find_tile(offsets, E, BM, blockIdx.y, sh_tiles);
-  if (ti.e < 0) return;
-  const int tid = threadIdx.x;
+// Rows r (ascending) of expert e, from the expert ids, by one wave: a ballot per 64 ids.
+__device__ int scan_rows(const int32_t* __restrict__ ids, int n, int e, int* lr) {
   const int lane = lane_id();
-  const int wave = tid / kWave;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int total = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int r = base + lane;
+    const bool m = r < n && ids[r] == e;
+    const unsigned long long mask = __ballot(m);
+    if (m) lr[total + __popcll(mask & lt)] = r;
+    total += __popcll(mask);
+  }
+  __syncthreads();
+  return total;
+}
+
+// One group of up to 16 rows (entries m0 .. of the expert's row list) against this wave's 16
+// features over the whole reduction length K, with no barrier and no LDS staging:
+//  * per 128-k block a lane loads four 16-byte pieces of its weight row (and of its up row for the
+//    gate/up product) at k = 32 c + 8 (lane / 16), the MFMA operand layout, so that each load
+//    instruction reads 64 contiguous bytes of each of 16 rows, and the same pieces of its A row
+//    (a token row of x or a row of h, both L2-resident);
+//  * two blocks are in flight ahead of use;
+//  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
+//    that concurrent waves spread over the HBM channels instead of reading the same offset of
+//    their rows. The sum order is fixed per wave, so results repeat exactly.
+template <bool GATEUP>
+__device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
+                                            const uint16_t* __restrict__ W0,
+                                            const uint16_t* __restrict__ W1, int K, int N, int k,
+                                            int e, const int* lr, int m0, int rows, int hbase,
+                                            uint16_t* __restrict__ h_out, const DownArgs& down) {
+  const int lane = lane_id();
   const int l16 = lane & 15;
-  const int kg = (lane >> 4) * 32;          // this lane's 32-wide k group inside a 128-k block
-  const int f = blockIdx.x * kDcBlockFeat + wave * kDcFeat + l16;   // weight row (feature)
-  const bool f_ok = f < N;
-  const long long wstride = static_cast<long long>(N) * K;
-  const uint16_t* pg = W0 + ti.e * wstride + static_cast<long long>(min(f, N - 1)) * K + kg;
-  const uint16_t* pu = GATEUP ? W1 + ti.e * wstride + static_cast<long long>(min(f, N - 1)) * K + kg : nullptr;
+  const int kq = (lane >> 4) * 8;
+  const int f = blockIdx.x * kStFeat + l16;  // weight row (N % 16 == 0)
+  const long long wofs = static_cast<long long>(e) * N * K + static_cast<long long>(f) * K + kq;
+  const uint16_t* pg = W0 + wofs;
+  const uint16_t* pu = GATEUP ? W1 + wofs : nullptr;
+  // lanes past the group's rows read row 0 of the group: their output rows are never stored
+  // (row i of the product depends only on A row i), and the duplicate reads coalesce
+  const int li_a = m0 + (l16 < rows ? l16 : 0);
+  const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
+  const uint16_t* pa = A + arow * K + kq;
+  const int nb = K / 128;                     // even: K % 256 == 0 on this path
+  const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
 
-  // gathered A row sources for the LDS staging loop
-  auto stage_a = [&](int k0) {
-    const int kc = min(KC, K - k0);
-    const int chunks = kc / 8;
-    __syncthreads();
-    for (int i = tid; i < BM * chunks; i += 256) {
-      const int r = i / chunks, c = i % chunks;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (r < ti.rows) {
-        const int p = ti.row0 + r;
-        const long long src = GATEUP ? static_cast<long long>(sorted_rows[p] / k) : p;
-        v = load16(A + src * K + k0 + c * 8);
-      }
-      store16(&As[r * LD + c * 8], v);
-    }
-    __syncthreads();
-  };
-
-  u32x4 bg0[4], bg1[4], bu0[4], bu1[4];
-  auto load_b = [&](u32x4* bg, u32x4* bu, int kb) {
+  u32x4 a0[4], bg0[4], bu0[4], a1[4], bg1[4], bu1[4];
+  auto load = [&](u32x4* a, u32x4* bg, u32x4* bu, int sq) {
+    const int kb = ((min(sq, nb - 1) + rot) % nb) * 128;  // past the end: re-read the last block
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      bg[c] = load16(pg + kb + c * 8);
-      if constexpr (GATEUP) bu[c] = load16(pu + kb + c * 8);
+      bg[c] = load16(pg + kb + c * 32);
+      if constexpr (GATEUP) bu[c] = load16(pu + kb + c * 32);
+      a[c] = load16(pa + kb + c * 32);
     }
   };
-
-  f32x4 accg[MT], accu[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    accg[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accu[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  auto compute = [&](const u32x4* bg, const u32x4* bu, int kloc) {
+  f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4* a, const u32x4* bg, const u32x4* bu) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const u32x4 a = load16(&As[(m * 16 + l16) * LD + kloc + kg + c * 8]);
-        accg[m] = mfma16x16x32(a, bg[c], accg[m]);
-        if constexpr (GATEUP) accu[m] = mfma16x16x32(a, bu[c], accu[m]);
-      }
+      accg = mfma16x16x32(a[c], bg[c], accg);
+      if constexpr (GATEUP) accu = mfma16x16x32(a[c], bu[c], accu);
     }
   };
-
-  const int nb = K / 128;                   // K % 128 == 0 on this path
-  constexpr int kBlocksPerChunk = KC / 128; // even, so odd blocks never start a chunk
-  load_b(bg0, bu0, 0);
-  int chunk0 = 0;
-  for (int b = 0; b < nb; b += 2) {
-    if (b % kBlocksPerChunk == 0) {
-      chunk0 = b * 128;
-      stage_a(chunk0);
-    }
-    if (b + 1 < nb) load_b(bg1, bu1, (b + 1) * 128);
-    compute(bg0, bu0, b * 128 - chunk0);
-    if (b + 1 < nb) {
-      if (b + 2 < nb) load_b(bg0, bu0, (b + 2) * 128);
-      compute(bg1, bu1, (b + 1) * 128 - chunk0);
-    }
+  load(a0, bg0, bu0, 0);
+  load(a1, bg1, bu1, 1);
+  for (int sq = 0; sq < nb; sq += 2) {
+    // sched_barrier keeps the scheduler from sinking the prefetches below the next compute
+    compute(a0, bg0, bu0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(a0, bg0, bu0, sq + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(a1, bg1, bu1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(a1, bg1, bu1, sq + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  if (!f_ok) return;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m * 16 + (lane >> 4) * 4 + r;
-      if (row >= ti.rows) continue;
-      const int p = ti.row0 + row;
-      if constexpr (GATEUP) {
-        const float hv = silu(accg[m][r]) * accu[m][r];
-        h_out[static_cast<long long>(p) * N + f] = f32_to_bf16_bits(hv);
-      } else {
-        const DownRow dr = down_row(down, p, N);
-        down_put(down, dr, f, accg[m][r]);
-      }
+  for (int r = 0; r < 4; ++r) {
+    const int i = (lane >> 4) * 4 + r;  // row of this group
+    if (i >= rows) continue;
+    const int li = m0 + i;              // entry of the expert's row list
+    const int hrow = hbase >= 0 ? hbase + li : lr[li];
+    if constexpr (GATEUP) {
+      const float hv = silu(accg[r]) * accu[r];
+      h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
+    } else {
+      const DownRow dr = down_row(down, lr[li], hrow, N);
+      down_put(down, dr, f, accg[r]);
     }
   }
 }
 
-template <int MT>
-hipError_t launch_decode(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
-                         const uint16_t* wd, int T, int d, int E, int H, int k,
-                         const int32_t* offsets, const int32_t* sorted_rows, uint16_t* h,
-                         const DownArgs& down, hipStream_t s, void* mid_event) {
-  const int tiles = max_tiles(T * k, E, 16 * MT);
-  DownArgs none{};
-  dim3 g1((H + kDcBlockFeat - 1) / kDcBlockFeat, tiles);
-  gemm_decode_kernel<true, MT><<<g1, 256, 0, s>>>(x, wg, wu, d, H, E, k, offsets, sorted_rows, h,
-                                                  none);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (mid_event) {
-    err = record_stage_event(mid_event, s);
-    if (err != hipSuccess) return err;
+// Grid (N / 16, E), one wave per block: block (x, e) computes features [16 x, 16 x + 16) of
+// expert e for all of the expert's rows, 16 rows per pass (a second pass over the same weights
+// mostly hits the caches).
+template <bool GATEUP>
+__global__ __launch_bounds__(kWave) void ffn_stream_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
+    const uint16_t* __restrict__ W1, int K, int N, int k, RowSource rs,
+    uint16_t* __restrict__ h_out, DownArgs down) {
+  __shared__ int lr[kMaxScanRows];
+  const int e = blockIdx.y;
+  int count, hbase;
+  if (rs.ids) {
+    count = scan_rows(rs.ids, rs.n_rows, e, lr);
+    hbase = -1;
+    if (rs.counts_out && blockIdx.x == 0 && threadIdx.x == 0) rs.counts_out[e] = count;
+  } else {
+    hbase = rs.offsets[e];
+    count = rs.offsets[e + 1] - hbase;
+    for (int i = threadIdx.x; i < count; i += blockDim.x) lr[i] = rs.sorted_rows[hbase + i];
+    __syncthreads();
   }
-  dim3 g2((d + kDcBlockFeat - 1) / kDcBlockFeat, tiles);
-  gemm_decode_kernel<false, MT><<<g2, 256, 0, s>>>(h, wd, nullptr, H, d, E, k, offsets,
-                                                   sorted_rows, nullptr, down);
-  return hipGetLastError();
+  for (int m0 = 0; m0 < count; m0 += 16)
+    stream_tile<GATEUP>(A, W0, W1, K, N, k, e, lr, m0, min(16, count - m0), hbase, h_out, down);
 }
 
 }  // namespace
 
+bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
+  const long long rows = static_cast<long long>(T) * k;
+  return rows <= kMaxScanRows && d % 256 == 0 && H % 256 == 0 && rows <= 32ll * E;
+}
+
 hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                            const uint16_t* wd, int T, int d, int E, int H, int k,
-                           const int32_t* offsets, const int32_t* sorted_rows, uint16_t* h,
-                           const DownArgs& down, hipStream_t s, void* mid_event) {
+                           const RowSource& rs, uint16_t* h, const DownArgs& down, hipStream_t s,
+                           void* mid_event) {
   const int rows = T * k;
   if (rows <= 0) return hipSuccess;
-  const bool k128 = (d % 128 == 0) && (H % 128 == 0);
-  const double avg = static_cast<double>(rows) / E;
-  if (k128 && avg <= 12.0) {
-    return launch_decode<1>(x, wg, wu, wd, T, d, E, H, k, offsets, sorted_rows, h, down, s,
-                            mid_event);
-  }
-  if (k128 && avg <= 32.0) {
-    return launch_decode<2>(x, wg, wu, wd, T, d, E, H, k, offsets, sorted_rows, h, down, s,
-                            mid_event);
-  }
-  const int tiles = max_tiles(rows, E, kPfBM);
   DownArgs none{};
-  dim3 g1((H + kPfBN / 2 - 1) / (kPfBN / 2), tiles);
-  gemm_prefill_kernel<true><<<g1, 256, 0, s>>>(x, wg, wu, d, H, E, k, offsets, sorted_rows, h,
-                                               none);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (mid_event) {
-    err = record_stage_event(mid_event, s);
+  hipError_t err;
+  if (ffn_bf16_streaming(T, d, E, H, k)) {
+    ffn_stream_kernel<true><<<dim3(H / kStFeat, E), kWave, 0, s>>>(x, wg, wu, d, H, k, rs, h,
+                                                                    none);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (mid_event && (err = record_stage_event(mid_event, s)) != hipSuccess) return err;
+    RowSource rs2 = rs;
+    rs2.counts_out = nullptr;
+    ffn_stream_kernel<false><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
+                                                                     rs2, nullptr, down);
+    return hipGetLastError();
   }
+  // grouped GEMM over the dispatch order (rs.offsets / rs.sorted_rows)
+  const int tiles = max_tiles(rows, E, kPfBM);
+  dim3 g1((H + kPfBN / 2 - 1) / (kPfBN / 2), tiles);
+  gemm_prefill_kernel<true><<<g1, 256, 0, s>>>(x, wg, wu, d, H, E, k, rs.offsets, rs.sorted_rows,
+                                               h, none);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (mid_event && (err = record_stage_event(mid_event, s)) != hipSuccess) return err;
   dim3 g2((d + kPfBN - 1) / kPfBN, tiles);
-  gemm_prefill_kernel<false><<<g2, 256, 0, s>>>(h, wd, nullptr, H, d, E, k, offsets, sorted_rows,
-                                                nullptr, down);
+  gemm_prefill_kernel<false><<<g2, 256, 0, s>>>(h, wd, nullptr, H, d, E, k, rs.offsets,
+                                                rs.sorted_rows, nullptr, down);
   return hipGetLastError();
 }
 

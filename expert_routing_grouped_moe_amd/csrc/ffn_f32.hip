@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
       if (n < N) h_out[static_cast<long long>(p) * N + n] = silu_precise(acc0[i]) * acc1[i];
     }
   } else {
-    const DownRow dr = down_row(down, p, N);
+    const DownRow dr = down_row(down, sorted_rows[p], p, N);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + c + 16 * i;

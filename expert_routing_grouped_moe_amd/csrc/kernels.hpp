@@ -9,9 +9,11 @@ namespace moe {
 
 enum Scoring { kSoftmax = 0, kSelectedSoftmax = 1 };
 
+constexpr int kTokTile = 16;  // tokens per routing block; also the dispatch block of rows
+
 // How the down-projection epilogue delivers its result.
 enum DownOut {
-  kDownExpertOut = 0,  // expert_out[p, :] = o                       (grouped order, fp32)
+  kDownExpertOut = 0,  // expert_out[p, :] = o                       (fp32)
   kDownStoreY = 1,     // y[t, :] = w * o            (k == 1: each token written once)
   kDownAtomicY = 2     // y[t, :] += w * o on a zeroed y (k == 2: two addends, order-free)
 };
@@ -19,10 +21,41 @@ enum DownOut {
 struct DownArgs {
   int mode;                 // DownOut
   float* out;               // expert_out or y
-  const int32_t* sorted_rows;
   const float* topk_w;      // [T, k]
   int k;
 };
+
+// Outputs of the routing tail (any may be NULL except ids and w).
+struct RouteOut {
+  int32_t* ids;         // [T, k]
+  float* w;             // [T, k]
+  int32_t* counts;      // [E], accumulated with integer atomics on a zeroed array
+  int32_t* block_hist;  // [ceil(T/16), E] expert histogram of each block's 16*k rows
+  int32_t* lrank;       // [T*k] rank of row r among its block's rows of the same expert
+  float* zero_y;        // [T, d] cleared (for the two-addend atomic combine)
+  int d;
+};
+
+// Stable per-block histogram and ranks of the `nrows` assignment rows whose experts sit in LDS
+// `sids` (row i of the block is assignment row row0 + i). Every thread of the block calls it.
+__device__ inline void block_hist_rank(const int* sids, int nrows, int E, int row0,
+                                       int32_t* block_hist, int32_t* lrank) {
+  if (lrank) {
+    for (int i = threadIdx.x; i < nrows; i += blockDim.x) {
+      const int e = sids[i];
+      int rank = 0;
+      for (int j = 0; j < i; ++j) rank += sids[j] == e;
+      lrank[row0 + i] = rank;
+    }
+  }
+  if (block_hist) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      int c = 0;
+      for (int j = 0; j < nrows; ++j) c += sids[j] == e;
+      block_hist[static_cast<long long>(blockIdx.x) * E + e] = c;
+    }
+  }
+}
 
 // Stage marker for the optional timing events: an external event node while `s` is being
 // captured into a graph, a plain event record otherwise (defined in moe_api.hip).
@@ -37,37 +70,58 @@ hipError_t launch_logits_f32(const float* x, const float* wr, const float* rb, i
 hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* wr, const float* rb, int T,
                               int d, int E, float* logits, hipStream_t s);
 
-// top-k + weights from fp32 logits in global memory. counts may be NULL; when not NULL they
-// are overwritten. zero_y (may be NULL) gets rows [T, d] cleared.
+// top-k + weights from fp32 logits in global memory.
 hipError_t launch_route_from_logits(const float* logits, const float* sel_bias, int T, int E,
-                                    int k, int scoring, int32_t* ids, float* w, int32_t* counts,
-                                    float* zero_y, int d, hipStream_t s);
+                                    int k, int scoring, const RouteOut& o, hipStream_t s);
 
-// logits on MFMA + top-k + weights in one kernel (bf16 x / router weight).
+// logits on MFMA + top-k + weights in one kernel (bf16 x / router weight); logits_out optional.
 hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const float* rb,
                                    const float* sel_bias, int T, int d, int E, int k, int scoring,
-                                   float* logits_out, int32_t* ids, float* w, float* zero_y,
-                                   hipStream_t s);
+                                   float* logits_out, const RouteOut& o, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch (permute.hip)
-// counts_in may be NULL (then computed); counts_out may be NULL.
-hipError_t launch_permute(const int32_t* ids, const int32_t* counts_in, int n_rows, int E,
-                          int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
-                          int32_t* counts_out, hipStream_t s);
+// Bytes of scratch the dispatch needs for T tokens (block histograms, ranks, block bases).
+size_t dispatch_scratch_bytes(int T, int E, int k);
+// From expert ids alone (moe_permute): block histograms + ranks, then the scan/scatter.
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
+                          void* scratch, hipStream_t s);
+// The scan/scatter alone, when the routing kernel already wrote block_hist and lrank.
+hipError_t launch_scan_scatter(const int32_t* ids, const int32_t* block_hist,
+                               const int32_t* lrank, int T, int E, int k, int32_t* offsets,
+                               int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
+                               int32_t* base_scratch, hipStream_t s);
 
 // ---------------------------------------------------------------- experts (ffn_*.hip)
-// h is the [T*k, H] intermediate in grouped order (bf16 bits or fp32). `mid_event` (a hipEvent_t
-// or NULL) is recorded on `s` between the gate/up and the down launches.
+// Where a grouped FFN finds the rows of expert e:
+//   grouped (ids == NULL): rows sorted_rows[offsets[e] + i]; h and expert_out at offsets[e] + i
+//   by ids  (ids != NULL): the rows r (ascending) with ids[r] == e; h and expert_out at row r
+struct RowSource {
+  const int32_t* ids;
+  int n_rows;               // T * k
+  const int32_t* offsets;   // [E + 1] (grouped)
+  const int32_t* sorted_rows;
+  int32_t* counts_out;      // by-ids mode may write expert counts here (or NULL)
+};
+
+// True when the weight-streaming kernels handle this shape (few rows per expert).
+bool ffn_bf16_streaming(int T, int d, int E, int H, int k);
+// Largest T*k the by-ids row scan supports.
+constexpr int kMaxScanRows = 2048;
+
+// h is the [T*k, H] intermediate (bf16 bits or fp32). `mid_event` (a hipEvent_t or NULL) is
+// recorded on `s` between the gate/up and the down launches.
 hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                            const uint16_t* wd, int T, int d, int E, int H, int k,
-                           const int32_t* offsets, const int32_t* sorted_rows, uint16_t* h,
-                           const DownArgs& down, hipStream_t s, void* mid_event);
+                           const RowSource& rs, uint16_t* h, const DownArgs& down, hipStream_t s,
+                           void* mid_event);
 hipError_t launch_ffn_f32(const float* x, const float* wg, const float* wu, const float* wd,
                           int T, int d, int E, int H, int k, const int32_t* offsets,
                           const int32_t* sorted_rows, float* h, const DownArgs& down,
                           hipStream_t s, void* mid_event);
 
 // ---------------------------------------------------------------- combine (combine.hip)
+// row_pos == NULL: expert_out is indexed by the assignment row itself.
 hipError_t launch_combine(const float* expert_out, const int32_t* row_pos, const float* w, int T,
                           int d, int k, float* y, hipStream_t s);
 

@@ -11,6 +11,8 @@
 namespace {
 
 using moe::DownArgs;
+using moe::RouteOut;
+using moe::RowSource;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -41,7 +43,7 @@ int check_scoring(int scoring, const float* sel_bias) {
 
 // Device workspace regions of the fused layer (the step calls use a subset).
 struct Layout {
-  size_t logits, ids, w, counts, offsets, sorted_rows, row_pos, h, eo, total;
+  size_t h, logits, ids, w, counts, offsets, sorted_rows, row_pos, dispatch, eo, total;
   Layout(int T, int d, int E, int H, int k, int dtype) {
     const size_t rows = static_cast<size_t>(T) * k;
     size_t o = 0;
@@ -53,8 +55,23 @@ struct Layout {
     offsets = o;     o += up(static_cast<size_t>(E + 1) * 4);
     sorted_rows = o; o += up(rows * 4);
     row_pos = o;     o += up(rows * 4);
+    dispatch = o;    o += up(moe::dispatch_scratch_bytes(T, E, k));
     eo = o;          o += k > 2 ? up(rows * d * 4) : 0;
     total = o;
+  }
+};
+
+// Sub-regions of the dispatch scratch: block histograms, block bases, ranks.
+struct DispatchScratch {
+  int32_t* hist;
+  int32_t* base;
+  int32_t* lrank;
+  DispatchScratch(void* p, int T, int E) {
+    const size_t nb = (static_cast<size_t>(T) + moe::kTokTile - 1) / moe::kTokTile;
+    char* c = static_cast<char*>(p);
+    hist = reinterpret_cast<int32_t*>(c);
+    base = reinterpret_cast<int32_t*>(c + up(nb * E * 4));
+    lrank = reinterpret_cast<int32_t*>(c + 2 * up(nb * E * 4));
   }
 };
 
@@ -80,10 +97,10 @@ hipError_t record_event(void* ev, hipStream_t s) {
   return hipEventRecord(static_cast<hipEvent_t>(ev), s);
 }
 
-#define MOE_TRY(expr)                      \
-  do {                                     \
-    const hipError_t _e = (expr);          \
-    if (_e != hipSuccess) return MOE_ERR_HIP; \
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    const hipError_t _e = (expr);              \
+    if (_e != hipSuccess) return MOE_ERR_HIP;  \
   } while (0)
 
 }  // namespace
@@ -102,7 +119,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "size out of range or pointer not 16-byte aligned";
     case MOE_ERR_UNSUPPORTED: return "unsupported dtype, scoring mode or argument combination";
-    case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_size()";
+    case MOE_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case MOE_ERR_HIP: return "a HIP kernel launch failed";
     default: return "unknown status";
   }
@@ -111,6 +128,11 @@ const char* moe_status_string(int status) {
 size_t moe_workspace_size(int T, int d, int E, int H, int k, int dtype) {
   if (check_dims(T, d, E, H, k, dtype) != MOE_OK || T == 0) return 0;
   return Layout(T, d, E, H, k, dtype).total;
+}
+
+size_t moe_permute_workspace_size(int T, int E, int k) {
+  if (check_route_dims(T, E, k) != MOE_OK || T == 0) return 0;
+  return moe::dispatch_scratch_bytes(T, E, k);
 }
 
 int moe_router_logits(const void* x, const void* w_router, const float* router_bias, int T, int d,
@@ -146,13 +168,14 @@ int moe_route(const float* logits, const float* sel_bias, int T, int E, int k, i
       !aligned16(expert_counts) || (sel_bias && !aligned16(sel_bias)))
     return MOE_ERR_SHAPE;
   clear_stale_error();
-  return hip_status(moe::launch_route_from_logits(logits, sel_bias, T, E, k, scoring, topk_ids,
-                                                  topk_w, expert_counts, nullptr, 0,
+  const RouteOut o{topk_ids, topk_w, expert_counts, nullptr, nullptr, nullptr, 0};
+  return hip_status(moe::launch_route_from_logits(logits, sel_bias, T, E, k, scoring, o,
                                                   static_cast<hipStream_t>(stream)));
 }
 
 int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, int E, int k,
-                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* stream) {
+                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* ws,
+                size_t ws_bytes, void* stream) {
   const int st = check_route_dims(T, E, k);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -160,10 +183,11 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, in
   if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
       !aligned16(sorted_rows) || !aligned16(row_pos))
     return MOE_ERR_SHAPE;
+  if (!ws || ws_bytes < moe::dispatch_scratch_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_SHAPE;
   clear_stale_error();
-  return hip_status(moe::launch_permute(topk_ids, expert_counts, T * k, E, expert_offsets,
-                                        sorted_rows, row_pos, nullptr,
-                                        static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_permute(topk_ids, T, E, k, expert_offsets, sorted_rows, row_pos,
+                                        nullptr, ws, static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* w_up,
@@ -181,14 +205,16 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
   const Layout lay(T, d, E, H, k, dtype);
   if (!ws || ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_SHAPE;
-  DownArgs down{moe::kDownExpertOut, expert_out, sorted_rows, nullptr, k};
+  const DownArgs down{moe::kDownExpertOut, expert_out, nullptr, k};
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  if (dtype == MOE_BF16)
+  if (dtype == MOE_BF16) {
+    const RowSource rs{nullptr, T * k, expert_offsets, sorted_rows, nullptr};
     return hip_status(moe::launch_ffn_bf16(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
         static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), T, d, E, H, k,
-        expert_offsets, sorted_rows, at<uint16_t>(ws, lay.h), down, s, nullptr));
+        rs, at<uint16_t>(ws, lay.h), down, s, nullptr));
+  }
   return hip_status(moe::launch_ffn_f32(
       static_cast<const float*>(x), static_cast<const float*>(w_gate),
       static_cast<const float*>(w_up), static_cast<const float*>(w_down), T, d, E, H, k,
@@ -227,9 +253,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
   void* const* ev = a->prof_events;
-  auto mark = [&](int i) -> hipError_t {
-    return ev ? record_event(ev[i], s) : hipSuccess;
-  };
+  auto mark = [&](int i) -> hipError_t { return ev ? record_event(ev[i], s) : hipSuccess; };
 
   int32_t* ids = a->topk_ids ? a->topk_ids : at<int32_t>(ws, lay.ids);
   float* w = a->topk_w ? a->topk_w : at<float>(ws, lay.w);
@@ -237,10 +261,13 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   int32_t* offsets = at<int32_t>(ws, lay.offsets);
   int32_t* sorted_rows = at<int32_t>(ws, lay.sorted_rows);
   int32_t* row_pos = at<int32_t>(ws, lay.row_pos);
+  const DispatchScratch ds(at<void>(ws, lay.dispatch), T, E);
+  float* eo = at<float>(ws, lay.eo);
   float* zero_y = k == 2 ? a->y : nullptr;
+  // few rows per expert (decode): the expert kernels find their rows from the ids themselves
+  const bool streaming = dtype == MOE_BF16 && moe::ffn_bf16_streaming(T, d, E, H, k);
 
   DownArgs down{};
-  down.sorted_rows = sorted_rows;
   down.topk_w = w;
   down.k = k;
   if (k == 1) {
@@ -251,37 +278,45 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
     down.out = a->y;
   } else {
     down.mode = moe::kDownExpertOut;
-    down.out = at<float>(ws, lay.eo);
+    down.out = eo;
   }
 
+  const RouteOut ro{ids, w, nullptr, streaming ? nullptr : ds.hist,
+                    streaming ? nullptr : ds.lrank, zero_y, d};
   MOE_TRY(mark(0));
   if (dtype == MOE_BF16) {
     MOE_TRY(moe::launch_route_fused_bf16(
         static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_router),
-        a->router_bias, a->sel_bias, T, d, E, k, a->scoring, a->logits, ids, w, zero_y, s));
+        a->router_bias, a->sel_bias, T, d, E, k, a->scoring, a->logits, ro, s));
   } else {
     float* logits = a->logits ? a->logits : at<float>(ws, lay.logits);
     MOE_TRY(moe::launch_logits_f32(static_cast<const float*>(a->x),
                                    static_cast<const float*>(a->w_router), a->router_bias, T, d, E,
                                    logits, s));
-    MOE_TRY(moe::launch_route_from_logits(logits, a->sel_bias, T, E, k, a->scoring, ids, w,
-                                          nullptr, zero_y, d, s));
+    MOE_TRY(moe::launch_route_from_logits(logits, a->sel_bias, T, E, k, a->scoring, ro, s));
   }
   MOE_TRY(mark(1));
-  MOE_TRY(moe::launch_permute(ids, nullptr, T * k, E, offsets, sorted_rows, row_pos, counts, s));
+  if (!streaming)
+    MOE_TRY(moe::launch_scan_scatter(ids, ds.hist, ds.lrank, T, E, k, offsets, sorted_rows,
+                                     row_pos, counts, ds.base, s));
   MOE_TRY(mark(2));
+  void* mid = ev ? ev[3] : nullptr;
   if (dtype == MOE_BF16) {
+    const RowSource rs = streaming ? RowSource{ids, T * k, nullptr, nullptr, counts}
+                                   : RowSource{nullptr, T * k, offsets, sorted_rows, nullptr};
     MOE_TRY(moe::launch_ffn_bf16(
         static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_gate),
         static_cast<const uint16_t*>(a->w_up), static_cast<const uint16_t*>(a->w_down), T, d, E,
-        H, k, offsets, sorted_rows, at<uint16_t>(ws, lay.h), down, s, ev ? ev[3] : nullptr));
+        H, k, rs, at<uint16_t>(ws, lay.h), down, s, mid));
   } else {
     MOE_TRY(moe::launch_ffn_f32(
         static_cast<const float*>(a->x), static_cast<const float*>(a->w_gate),
         static_cast<const float*>(a->w_up), static_cast<const float*>(a->w_down), T, d, E, H, k,
-        offsets, sorted_rows, at<float>(ws, lay.h), down, s, ev ? ev[3] : nullptr));
+        offsets, sorted_rows, at<float>(ws, lay.h), down, s, mid));
   }
-  if (k > 2) MOE_TRY(moe::launch_combine(at<float>(ws, lay.eo), row_pos, w, T, d, k, a->y, s));
+  // k > 2: expert outputs were staged (by assignment row on the streaming path, in dispatch
+  // order otherwise) and are combined in slot order
+  if (k > 2) MOE_TRY(moe::launch_combine(eo, streaming ? nullptr : row_pos, w, T, d, k, a->y, s));
   MOE_TRY(mark(4));
   return MOE_OK;
 }

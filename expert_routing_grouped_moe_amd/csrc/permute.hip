@@ -8,11 +8,13 @@
 //                   p in [offsets[e], offsets[e+1])
 //   row_pos[r]      inverse of sorted_rows
 //
-// One block of 1024 threads (16 wave64s) does everything, so the result needs no inter-block
-// ordering and is identical on every call. Pass 1 builds the histogram with LDS atomics (integer,
-// order-free). Pass 2 walks the rows in chunks of 1024: inside a wave, lanes with the same expert
-// get their rank from a ballot (lanes below with the same id), across waves a per-wave count
-// table in LDS gives each wave its base, and a running per-expert base carries across chunks.
+// Two phases, no atomics, the same result on every call:
+//  1. per block of 16 tokens (16*k rows): the expert histogram of the block and the rank of each
+//     row among the block's earlier rows of the same expert (written by the routing kernel, or by
+//     block_hist_kernel when only the ids are given);
+//  2. one block of 1024 threads scans the histograms in expert-major order (expert e, then block
+//     b), which yields offsets[e] and the base position of every (block, expert) pair, and then
+//     scatters: row r of block b with expert e lands at base[b][e] + rank[r].
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,101 +22,118 @@ namespace moe {
 
 namespace {
 
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / kWave;
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ row_pos,
-    int32_t* __restrict__ counts_out) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int base[kMaxE];
-  __shared__ int wcnt[kPermWaves][kMaxE];
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+__global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restrict__ ids, int T,
+                                                         int k, int E,
+                                                         int32_t* __restrict__ block_hist,
+                                                         int32_t* __restrict__ lrank) {
+  __shared__ int sids[kTokTile * kMaxK];
+  const int t0 = blockIdx.x * kTokTile;
+  const int nrows = min(kTokTile, T - t0) * k;
+  const int row0 = t0 * k;
+  for (int i = threadIdx.x; i < nrows; i += blockDim.x)
+    sids[i] = min(max(ids[row0 + i], 0), E - 1);  // out-of-range ids are outside the contract
+  __syncthreads();
+  block_hist_rank(sids, nrows, E, row0, block_hist, lrank);
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_scatter_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ block_hist,
+    const int32_t* __restrict__ lrank, int n, int k, int nb, int E, int32_t* __restrict__ base,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ row_pos, int32_t* __restrict__ counts_out) {
+  __shared__ int wsum[kScanWaves];
+  __shared__ int soff[kMaxE + 1];
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
   const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int total = nb * E;
+  const int per = (total + kScanThreads - 1) / kScanThreads;
+  const int beg = min(tid * per, total);
+  const int end = min(beg + per, total);
 
-  for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int r = tid; r < n; r += kPermThreads) {
-    const int e = min(max(ids[r], 0), E - 1);  // out-of-range ids are outside the contract
-    atomicAdd(&cnt[e], 1);
+  // expert-major element i is (e = i / nb, b = i % nb), stored at block_hist[b * E + e]
+  int s = 0;
+  for (int i = beg; i < end; ++i) s += block_hist[(i % nb) * E + i / nb];
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
   }
+  if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  // exclusive scan over E <= 256 by wave 0, four experts per lane
   if (wave == 0) {
-    int c[4];
-    int run = 0;
+    int v = lane < kScanWaves ? wsum[lane] : 0;
+    const int own = v;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      c[q] = e < E ? cnt[e] : 0;
-      run += c[q];
+    for (int o = 1; o < kScanWaves; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
     }
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    int ex = incl - run;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      if (e < E) {
-        base[e] = ex;
-        offsets[e] = ex;
-        if (counts_out) counts_out[e] = c[q];
-      }
-      ex += c[q];
-    }
-    if (lane == kWave - 1) offsets[E] = incl;
+    if (lane < kScanWaves) wsum[lane] = v - own;  // exclusive prefix of the wave totals
   }
   __syncthreads();
-
-  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int c0 = 0; c0 < n; c0 += kPermThreads) {
-    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i / E][i % E] = 0;
-    __syncthreads();
-    const int r = c0 + tid;
-    const int e = r < n ? min(max(ids[r], 0), E - 1) : -1;
-    int rank = 0;
-    unsigned long long pending = __ballot(e >= 0);
-    while (pending) {
-      const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-      const int le = __shfl(e, leader);
-      const unsigned long long same = __ballot(e == le);
-      if (e == le) {
-        rank = __popcll(same & lt_mask);
-        if (lane == leader) wcnt[wave][le] = __popcll(same);
-      }
-      pending &= ~same;
-    }
-    __syncthreads();
-    if (e >= 0) {
-      int pos = base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-      sorted_rows[pos] = r;
-      row_pos[r] = pos;
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += kPermThreads) {
-      int add = 0;
-      for (int w = 0; w < kPermWaves; ++w) add += wcnt[w][x];
-      base[x] += add;
-    }
-    __syncthreads();
+  int run = wsum[wave] + incl - s;
+  for (int i = beg; i < end; ++i) {
+    const int e = i / nb, b = i % nb;
+    const int h = block_hist[b * E + e];
+    base[b * E + e] = run;
+    if (b == 0) soff[e] = run;
+    run += h;
+  }
+  if (tid == 0) soff[E] = n;
+  __threadfence();
+  __syncthreads();
+  for (int e = tid; e <= E; e += kScanThreads) {
+    offsets[e] = soff[e];
+    if (e < E && counts_out) counts_out[e] = soff[e + 1] - soff[e];
+  }
+  const int rows_per_block = kTokTile * k;
+  for (int r = tid; r < n; r += kScanThreads) {
+    const int e = min(max(ids[r], 0), E - 1);
+    const int b = r / rows_per_block;
+    const int p = base[b * E + e] + lrank[r];
+    sorted_rows[p] = r;
+    row_pos[r] = p;
   }
 }
 
 }  // namespace
 
-hipError_t launch_permute(const int32_t* ids, const int32_t* /*counts_in*/, int n_rows, int E,
-                          int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
-                          int32_t* counts_out, hipStream_t s) {
-  permute_kernel<<<1, kPermThreads, 0, s>>>(ids, n_rows, E, offsets, sorted_rows, row_pos,
-                                            counts_out);
+size_t dispatch_scratch_bytes(int T, int E, int k) {
+  const size_t nb = (static_cast<size_t>(T) + kTokTile - 1) / kTokTile;
+  return up256(nb * E * 4) * 2 + up256(static_cast<size_t>(T) * k * 4);
+}
+
+hipError_t launch_scan_scatter(const int32_t* ids, const int32_t* block_hist,
+                               const int32_t* lrank, int T, int E, int k, int32_t* offsets,
+                               int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
+                               int32_t* base_scratch, hipStream_t s) {
+  const int nb = (T + kTokTile - 1) / kTokTile;
+  scan_scatter_kernel<<<1, kScanThreads, 0, s>>>(ids, block_hist, lrank, T * k, k, nb, E,
+                                                 base_scratch, offsets, sorted_rows, row_pos,
+                                                 counts_out);
   return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
+                          void* scratch, hipStream_t s) {
+  const int nb = (T + kTokTile - 1) / kTokTile;
+  char* p = static_cast<char*>(scratch);
+  int32_t* hist = reinterpret_cast<int32_t*>(p);
+  int32_t* base = reinterpret_cast<int32_t*>(p + up256(static_cast<size_t>(nb) * E * 4));
+  int32_t* lrank = reinterpret_cast<int32_t*>(p + 2 * up256(static_cast<size_t>(nb) * E * 4));
+  block_hist_kernel<<<nb, 256, 0, s>>>(ids, T, k, E, hist, lrank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_scan_scatter(ids, hist, lrank, T, E, k, offsets, sorted_rows, row_pos,
+                             counts_out, base, s);
 }
 
 }  // namespace moe

@@ -9,8 +9,16 @@
 // Selection order is (score descending, expert index ascending); -0.0 == +0.0 under the IEEE
 // comparison, so signed zeros fall through to the index.
 //
-// Layout of the work: a block of 256 threads owns 16 tokens; 16 lanes per token each scan every
-// 16th expert, and the per-token best is found with xor-shuffles inside the 16-lane group.
+// Work layout: a block owns 16 tokens. Selection runs on 256 threads, 16 lanes per token, each
+// lane scanning every 16th expert; the per-token best is found with xor-shuffles inside the
+// 16-lane group. The bf16 routing kernel first computes the 16 x E logit tile on the matrix cores
+// with 8 waves that split the experts (16 per MFMA tile) and, when there are few experts, the
+// d-long reduction; each wave issues the loads of 8 MFMA steps before using them. Partial tiles
+// are added in a fixed order, so the logits are the same on every call.
+//
+// The routing tail also emits, per block, the expert histogram of its 16*k assignment rows and the
+// stable rank of every row among the block's rows of the same expert; a one-block scan then
+// turns these into the grouped (dispatch) order without any atomics.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -18,9 +26,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kTokTile = 16;   // tokens per block
-constexpr int kQ = 16;         // lanes per token
-constexpr int kRouteThreads = kTokTile * kQ;
+constexpr int kQ = 16;                      // lanes per token in the selection
+constexpr int kTailThreads = kTokTile * kQ; // 256
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kBatch = 8;                   // MFMA steps whose loads are issued together
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -102,52 +112,55 @@ __device__ void select_and_weigh(const float* row, const float* sbias, int E, in
   }
 }
 
-// Shared tail of both routing kernels: selection on the LDS logit tile, outputs, histogram,
-// optional clearing of the token rows of y.
+// Selection on the LDS logit tile of the block's 16 tokens, then the outputs. Called by every
+// thread of the block (barriers inside); threads >= 256 only help with the epilogue loops.
 __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0, int T, int E,
-                           int k, int scoring, int32_t* __restrict__ ids_out,
-                           float* __restrict__ w_out, int32_t* __restrict__ counts, int* hist,
-                           float* __restrict__ zero_y, int d) {
+                           int k, int scoring, const RouteOut& o, int* hist, int* sids) {
   const int tl = threadIdx.x / kQ;
   const int q = threadIdx.x % kQ;
   const int t = t0 + tl;
-  int ids[kMaxK];
-  float w[kMaxK];
-  select_and_weigh(tile + tl * ld, sbias, E, k, scoring, q, ids, w);
-  if (t < T && q == 0) {
+  if (threadIdx.x < kTailThreads) {  // whole waves
+    int ids[kMaxK];
+    float w[kMaxK];
+    select_and_weigh(tile + tl * ld, sbias, E, k, scoring, q, ids, w);
+    if (t < T && q == 0) {
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        ids_out[static_cast<long long>(t) * k + j] = ids[j];
-        w_out[static_cast<long long>(t) * k + j] = w[j];
-        if (counts) atomicAdd(&hist[ids[j]], 1);
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+          o.ids[static_cast<long long>(t) * k + j] = ids[j];
+          o.w[static_cast<long long>(t) * k + j] = w[j];
+          sids[tl * k + j] = ids[j];
+          if (o.counts) atomicAdd(&hist[ids[j]], 1);
+        }
       }
     }
   }
   __syncthreads();
-  if (counts) {
+  if (o.counts) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      if (gridDim.x == 1) counts[e] = hist[e];
-      else if (hist[e]) atomicAdd(&counts[e], hist[e]);
+      if (gridDim.x == 1) o.counts[e] = hist[e];
+      else if (hist[e]) atomicAdd(&o.counts[e], hist[e]);
     }
   }
-  if (zero_y) {
+  if (o.block_hist || o.lrank)
+    block_hist_rank(sids, min(kTokTile, T - t0) * k, E, t0 * k, o.block_hist, o.lrank);
+  if (o.zero_y) {
     const int rows = min(kTokTile, T - t0);
-    const int vec = d / 4;
-    float4* base = reinterpret_cast<float4*>(zero_y + static_cast<long long>(t0) * d);
+    const int vec = o.d / 4;
+    float4* base = reinterpret_cast<float4*>(o.zero_y + static_cast<long long>(t0) * o.d);
     for (int i = threadIdx.x; i < rows * vec; i += blockDim.x) base[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_from_logits_kernel(
+__global__ __launch_bounds__(kTailThreads) void route_from_logits_kernel(
     const float* __restrict__ logits, const float* __restrict__ sel_bias, int T, int E, int k,
-    int scoring, int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
-    float* __restrict__ zero_y, int d) {
+    int scoring, RouteOut o) {
   extern __shared__ float smem[];
   const int ld = E + 1;
-  float* tile = smem;                      // [kTokTile][E+1]
-  float* sbias = tile + kTokTile * ld;     // [E]
-  int* hist = reinterpret_cast<int*>(sbias + E);  // [E]
+  float* tile = smem;                              // [16][E+1]
+  float* sbias = tile + kTokTile * ld;             // [E]
+  int* hist = reinterpret_cast<int*>(sbias + E);   // [E]
+  int* sids = hist + E;                            // [16 * kMaxK]
   const int t0 = blockIdx.x * kTokTile;
   for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
     const int tl = i / E, e = i % E;
@@ -159,97 +172,91 @@ __global__ __launch_bounds__(kRouteThreads) void route_from_logits_kernel(
     hist[e] = 0;
   }
   __syncthreads();
-  route_tail(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, ids, w, counts, hist,
-             zero_y, d);
+  route_tail(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist, sids);
 }
 
-// Router logits for 16 tokens on the matrix cores, then selection. The four waves split the
-// d-long dot products four ways; the partial 16 x E tiles are added in wave order (fixed, so the
-// logits are the same on every call).
-__global__ __launch_bounds__(kRouteThreads) void route_fused_bf16_kernel(
+// How the 8 waves of the fused kernel split the logit tile: `neb` 16-expert column blocks, each
+// reduced over `ksplit` slices of d (a power of two, neb * ksplit <= 8 when neb < 8).
+__host__ __device__ inline int route_ksplit(int E) {
+  const int neb = (E + 15) / 16;
+  if (neb >= kFusedWaves) return 1;
+  int ks = 1;
+  while (ks * 2 * neb <= kFusedWaves) ks *= 2;
+  return ks;
+}
+
+__global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ rb,
     const float* __restrict__ sel_bias, int T, int d, int E, int k, int scoring,
-    float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ w,
-    float* __restrict__ zero_y) {
+    float* __restrict__ logits_out, RouteOut o) {
   extern __shared__ float smem[];
   const int ld = E + 1;
-  float* tile = smem;                      // [16][E+1]
-  float* sbias = tile + kTokTile * ld;
-  int* hist = reinterpret_cast<int*>(sbias + E);
+  const int neb = (E + 15) / 16;
+  const int ksplit = route_ksplit(E);
+  float* part = smem;                                  // [ksplit][16][E+1]; part[0] = tile
+  float* sbias = part + ksplit * kTokTile * ld;        // [E]
+  int* hist = reinterpret_cast<int*>(sbias + E);       // [E]
+  int* sids = hist + E;                                // [16 * kMaxK]
   const int t0 = blockIdx.x * kTokTile;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int neb = (E + 15) / 16;
-  const int kslice = d / 4;        // d % 128 == 0 is not required; d % 64 == 0 -> kslice % 16
-  const int kbeg = wave * kslice;
   const int r16 = lane & 15;
   const int kq = (lane >> 4) * 8;
+  const int t = t0 + r16;
+  const bool tok_ok = t < T;
+  const uint16_t* xrow = x + static_cast<long long>(min(t, T - 1)) * d;
+  const int kslice = d / ksplit;  // a multiple of 8 (d % 64 == 0, ksplit <= 8)
 
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     if (sel_bias) sbias[e] = sel_bias[e];
     hist[e] = 0;
   }
 
-  f32x4 acc[16];
+  for (int task = wave; task < neb * ksplit; task += kFusedWaves) {
+    const int eb = task % neb;
+    const int ks = task / neb;
+    const int kbeg = ks * kslice;
+    const int kend = kbeg + kslice;
+    const int e = eb * 16 + r16;
+    const bool e_ok = e < E;
+    const uint16_t* wrow = wr + static_cast<long long>(min(e, E - 1)) * d;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kbeg; k0 < kend; k0 += 32 * kBatch) {
+      u32x4 a[kBatch], b[kBatch];
 #pragma unroll
-  for (int b = 0; b < 16; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int t = t0 + r16;
-  const uint16_t* xrow = x + static_cast<long long>(min(t, T - 1)) * d;
-  const bool tok_ok = t < T;
-  // kslice is a multiple of 16 (d % 64 == 0); MFMA steps consume 32 k. A slice whose length is
-  // an odd multiple of 16 ends with a half step whose upper k lanes read zeros.
-  for (int k0 = kbeg; k0 < kbeg + kslice; k0 += 32) {
-    const int kk = k0 + kq;
-    const bool k_ok = kk < kbeg + kslice;
-    u32x4 a = u32x4{0u, 0u, 0u, 0u};
-    if (tok_ok && k_ok) a = load16(xrow + kk);
-#pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      if (b < neb) {
-        const int e = b * 16 + r16;
-        u32x4 bv = u32x4{0u, 0u, 0u, 0u};
-        if (e < E && k_ok) bv = load16(wr + static_cast<long long>(e) * d + kk);
-        acc[b] = mfma16x16x32(a, bv, acc[b]);
+      for (int s = 0; s < kBatch; ++s) {
+        const int kk = k0 + 32 * s + kq;  // kend - kk is a multiple of 8: kk < kend -> 8 in range
+        const bool ok = kk < kend;
+        a[s] = (ok && tok_ok) ? load16(xrow + kk) : u32x4{0u, 0u, 0u, 0u};
+        b[s] = (ok && e_ok) ? load16(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
       }
-    }
-  }
-  // ordered reduction of the four partial tiles into LDS
-  for (int src = 0; src < 4; ++src) {
-    if (wave == src) {
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        if (b < neb) {
-          const int e = b * 16 + r16;
-          if (e < E) {
+      for (int s = 0; s < kBatch; ++s) acc = mfma16x16x32(a[s], b[s], acc);
+    }
+    if (e_ok) {
+      float* dst = part + ks * kTokTile * ld;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = (lane >> 4) * 4 + r;
-              float* dst = tile + row * ld + e;
-              *dst = (src == 0) ? acc[b][r] : (*dst + acc[b][r]);
-            }
-          }
-        }
-      }
+      for (int r = 0; r < 4; ++r) dst[((lane >> 4) * 4 + r) * ld + e] = acc[r];
     }
-    __syncthreads();
   }
-  if (rb) {
-    for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
-      const int tl = i / E, e = i % E;
-      tile[tl * ld + e] = tile[tl * ld + e] + rb[e];
-    }
-    __syncthreads();
+  __syncthreads();
+  // fixed-order sum of the d slices, then the router bias (one more fp32 rounding)
+  for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
+    const int tl = i / E, e = i % E;
+    float v = part[tl * ld + e];
+    for (int ks = 1; ks < ksplit; ++ks) v += part[(ks * kTokTile + tl) * ld + e];
+    if (rb) v = v + rb[e];
+    part[tl * ld + e] = v;
   }
+  __syncthreads();
   if (logits_out) {
     for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
       const int tl = i / E, e = i % E;
-      if (t0 + tl < T) logits_out[static_cast<long long>(t0 + tl) * E + e] = tile[tl * ld + e];
+      if (t0 + tl < T) logits_out[static_cast<long long>(t0 + tl) * E + e] = part[tl * ld + e];
     }
   }
-  if (ids == nullptr) return;  // logits only
-  route_tail(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, ids, w, nullptr, hist,
-             zero_y, d);
+  if (o.ids == nullptr) return;  // logits only (uniform across the block)
+  route_tail(part, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist, sids);
 }
 
 // fp32 router logits: one thread per (token, expert), four interleaved partial sums.
@@ -274,8 +281,14 @@ __global__ void logits_f32_kernel(const float* __restrict__ x, const float* __re
   logits[i] = s;
 }
 
-size_t route_smem(int E) {
-  return sizeof(float) * (static_cast<size_t>(kTokTile) * (E + 1) + E) + sizeof(int) * E;
+size_t tail_smem(int E) {
+  return sizeof(float) * (static_cast<size_t>(kTokTile) * (E + 1) + E) +
+         sizeof(int) * (E + kTokTile * kMaxK);
+}
+
+size_t fused_smem(int E) {
+  return sizeof(float) * (static_cast<size_t>(route_ksplit(E)) * kTokTile * (E + 1) + E) +
+         sizeof(int) * (E + kTokTile * kMaxK);
 }
 
 }  // namespace
@@ -302,32 +315,35 @@ hipError_t launch_logits_f32(const float* x, const float* wr, const float* rb, i
 }
 
 hipError_t launch_route_from_logits(const float* logits, const float* sel_bias, int T, int E,
-                                    int k, int scoring, int32_t* ids, float* w, int32_t* counts,
-                                    float* zero_y, int d, hipStream_t s) {
+                                    int k, int scoring, const RouteOut& o, hipStream_t s) {
   const int blocks = (T + kTokTile - 1) / kTokTile;
-  if (counts && blocks > 1) {
-    hipError_t err = launch_zero_i32(counts, E, s);
+  if (o.counts && blocks > 1) {
+    hipError_t err = launch_zero_i32(o.counts, E, s);
     if (err != hipSuccess) return err;
   }
-  route_from_logits_kernel<<<blocks, kRouteThreads, route_smem(E), s>>>(
-      logits, sel_bias, T, E, k, scoring, ids, w, counts, zero_y, d);
+  route_from_logits_kernel<<<blocks, kTailThreads, tail_smem(E), s>>>(logits, sel_bias, T, E, k,
+                                                                      scoring, o);
   return hipGetLastError();
 }
 
 hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const float* rb,
                                    const float* sel_bias, int T, int d, int E, int k, int scoring,
-                                   float* logits_out, int32_t* ids, float* w, float* zero_y,
-                                   hipStream_t s) {
+                                   float* logits_out, const RouteOut& o, hipStream_t s) {
   const int blocks = (T + kTokTile - 1) / kTokTile;
-  route_fused_bf16_kernel<<<blocks, kRouteThreads, route_smem(E), s>>>(
-      x, wr, rb, sel_bias, T, d, E, k, scoring, logits_out, ids, w, zero_y);
+  if (o.counts && blocks > 1) {
+    hipError_t err = launch_zero_i32(o.counts, E, s);
+    if (err != hipSuccess) return err;
+  }
+  route_fused_bf16_kernel<<<blocks, kFusedThreads, fused_smem(E), s>>>(x, wr, rb, sel_bias, T, d,
+                                                                       E, k, scoring, logits_out,
+                                                                       o);
   return hipGetLastError();
 }
 
 hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* wr, const float* rb, int T,
                               int d, int E, float* logits, hipStream_t s) {
-  return launch_route_fused_bf16(x, wr, rb, nullptr, T, d, E, 1, kSoftmax, logits, nullptr,
-                                 nullptr, nullptr, s);
+  RouteOut none{};
+  return launch_route_fused_bf16(x, wr, rb, nullptr, T, d, E, 1, kSoftmax, logits, none, s);
 }
 
 }  // namespace moe

@@ -73,10 +73,17 @@ def test_route_validation():
 
 def test_permute_combine_logits_validation():
     L = moe.LIB
-    assert L.moe_permute(FAKE, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, None) == moe.MOE_OK
-    assert L.moe_permute(FAKE, FAKE, 4, 8, 9, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_SHAPE
-    assert L.moe_permute(FAKE, None, 4, 8, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_NULL
-    assert L.moe_permute(FAKE, FAKE, 4, 8, 1, FAKE, MISALIGNED, FAKE, None) == moe.MOE_ERR_SHAPE
+    pws = L.moe_permute_workspace_size(4, 8, 1)
+    assert pws > 0 and L.moe_permute_workspace_size(0, 8, 1) == 0
+    assert L.moe_permute_workspace_size(4, 8, 9) == 0
+    perm = lambda T=4, k=1, c=FAKE, sr=FAKE, w=FAKE, n=pws: L.moe_permute(
+        FAKE, c, T, 8, k, FAKE, sr, FAKE, w, n, None)
+    assert perm(T=0) == moe.MOE_OK
+    assert perm(k=9) == moe.MOE_ERR_SHAPE
+    assert perm(c=None) == moe.MOE_ERR_NULL
+    assert perm(sr=MISALIGNED) == moe.MOE_ERR_SHAPE
+    assert perm(w=None) == moe.MOE_ERR_WORKSPACE
+    assert perm(n=pws - 1) == moe.MOE_ERR_WORKSPACE
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 6, 1, FAKE, None) == moe.MOE_ERR_SHAPE     # d % 4
     assert L.moe_combine(FAKE, None, FAKE, 4, 8, 1, FAKE, None) == moe.MOE_ERR_NULL
     assert L.moe_combine(FAKE, FAKE, FAKE, 0, 8, 1, FAKE, None) == moe.MOE_OK

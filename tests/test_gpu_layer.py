@@ -58,6 +58,11 @@ EDGE = [
     ("all-one-expert", 500, 128, 16, 1, 256, orc.SOFTMAX, "bf16", None, "hot5"),
     ("prefill-ragged", 1111, 192, 8, 2, 320, orc.SOFTMAX, "bf16", None, None),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
+    # few rows per expert with d, H multiples of 128: the weight-streaming expert kernels
+    ("stream-k3", 40, 128, 16, 3, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("stream-E256-k8", 64, 256, 256, 8, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("stream-hot-expert", 200, 128, 16, 1, 128, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("stream-max-rows", 1024, 128, 64, 2, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
 ]
 
 
