@@ -35,6 +35,41 @@ FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 STAGES = ("route", "dispatch", "gate_up", "down_combine")
 
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s vs MI355X peak"
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.md")
+# sources the expert kernels are built from; the counter-based traffic figure is only reported
+# while these are unchanged since the counters were taken
+KERNEL_SOURCES = ("expert_routing_grouped_moe_amd/csrc/ffn_bf16.hip",
+                  "expert_routing_grouped_moe_amd/csrc/common.hpp",
+                  "expert_routing_grouped_moe_amd/csrc/down_epilogue.hpp",
+                  "expert_routing_grouped_moe_amd/csrc/kernels.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter table
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or None when the
+    table has no row for it or the kernel sources changed since it was measured."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    want = kernel_source_hash()
+    with open(TRAFFIC_TABLE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) < 7 or cells[0] != kernel or cells[1] != workload:
+                continue
+            if cells[2] != want:
+                return None
+            fetch_kib, write_kib, sf, sw = (float(c) for c in cells[3:7])
+            return (fetch_kib * sf + write_kib * sw) * 1024.0
+    return None
 
 
 def _hip():
@@ -98,7 +133,22 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from the host instead of graph replay (counter runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB ten times (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 10}))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -190,8 +240,13 @@ def main():
 
     # timed region: `steps` layer steps replayed back to back
     t0 = time.perf_counter()
-    for _ in range(replays):
-        graph.replay()
+    if args.eager:
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                one_step(i % ncopies, False)
+    else:
+        for _ in range(replays):
+            graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / steps * 1e3
@@ -252,8 +307,14 @@ def main():
         ach = alg["gu_bytes"] / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "traffic": None}
-    roof["kernel"] = "gemm_decode_kernel<gate/up>" if not prefill and (T * k / E) <= 32 else \
-        "gemm_prefill_kernel<gate/up>"
+    streaming = inp.dtype == "bf16" and T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and \
+        T * k <= 32 * E
+    roof["kernel"] = "ffn_stream_kernel<true>" if streaming else (
+        "gemm_prefill_kernel<true>" if inp.dtype == "bf16" else "ffn_f32_kernel<true>")
+    traffic = measured_traffic(roof["kernel"], args.workload)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+                              if traffic is not None else "not measured for the current kernel")
     roof["avg_launch_us"] = gu_ms * 1e3
     roof["algorithmic_bytes_per_launch"] = alg["gu_bytes"]
     roof["algorithmic_flops_per_launch"] = alg["gu_flops"]
@@ -275,7 +336,8 @@ def main():
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "H": H,
                    "scoring": inp.scoring, "seed": gen.WORKLOADS[args.workload].seed,
                    "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
-                   "timing": "HIP graph replay, one step per weight copy",
+                   "timing": ("host launches" if args.eager else
+                              "HIP graph replay, one step per weight copy"),
                    "stage_events": ev_mode, "stage_event_steps": len(step_ms_ev)},
         "step_hbm_gbps": alg["step_bytes"] / step_s / 1e9,
         "step_hbm_frac": alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
