@@ -60,18 +60,17 @@ __host__ __device__ inline int max_tiles(int rows, int E, int bm) {
   return static_cast<int>(bound < rows ? bound : rows);
 }
 
-// Expert tile lookup shared by the grouped FFN kernels. Expert e owns ceil(count_e / bm) row
-// tiles; tiles are numbered expert by expert. Every thread of the block gets the same answer.
-// Needs 2 * (E + 1) ints of LDS in `sh`; every thread of the block must call it.
+// Expert tile bookkeeping shared by the grouped FFN kernels. Expert e owns ceil(count_e / bm)
+// row tiles; tiles are numbered expert by expert. tile_scan() loads the offsets and the inclusive
+// per-expert tile counts into LDS (`sh`, 2 * (E + 1) ints) and returns the number of tiles; every
+// thread of the block must call it. tile_lookup() then maps a tile index to its expert and rows.
 struct TileInfo {
   int e;      // expert, or -1 when the tile index is past the last tile
   int row0;   // first position in the grouped row order covered by the tile
   int rows;   // rows of the tile that belong to expert e (1..bm)
 };
 
-__device__ inline TileInfo find_tile(const int32_t* __restrict__ offsets, int E, int bm, int tile,
-                                     int* sh) {
-  // sh[0..E]: offsets; sh[E+1 .. 2E+1]: inclusive tile scan
+__device__ inline int tile_scan(const int32_t* __restrict__ offsets, int E, int bm, int* sh) {
   int* soff = sh;
   int* scum = sh + E + 1;
   for (int i = threadIdx.x; i <= E; i += blockDim.x) soff[i] = offsets[i];
@@ -92,7 +91,6 @@ __device__ inline TileInfo find_tile(const int32_t* __restrict__ offsets, int E,
       run += n;
       c[q] = run;
     }
-    // inclusive scan of the per-lane totals across the wave
     int tot = run;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -107,13 +105,18 @@ __device__ inline TileInfo find_tile(const int32_t* __restrict__ offsets, int E,
     }
   }
   __syncthreads();
+  return scum[E - 1];
+}
+
+__device__ inline TileInfo tile_lookup(int E, int bm, int tile, const int* sh) {
+  const int* soff = sh;
+  const int* scum = sh + E + 1;
   TileInfo ti;
   ti.e = -1;
   ti.row0 = 0;
   ti.rows = 0;
-  if (tile >= scum[E - 1]) return ti;
-  // first expert whose inclusive tile count exceeds `tile`
-  int lo = 0, hi = E - 1;
+  if (tile < 0 || tile >= scum[E - 1]) return ti;
+  int lo = 0, hi = E - 1;  // first expert whose inclusive tile count exceeds `tile`
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (scum[mid] > tile) hi = mid; else lo = mid + 1;
@@ -125,6 +128,12 @@ __device__ inline TileInfo find_tile(const int32_t* __restrict__ offsets, int E,
   ti.row0 = soff[lo] + m0;
   ti.rows = min(bm, cnt - m0);
   return ti;
+}
+
+__device__ inline TileInfo find_tile(const int32_t* __restrict__ offsets, int E, int bm, int tile,
+                                     int* sh) {
+  tile_scan(offsets, E, bm, sh);
+  return tile_lookup(E, bm, tile, sh);
 }
 
 }  // namespace moe

@@ -31,6 +31,20 @@ constexpr int kPfBN = 128;          // weight rows per tile (gate/up: 64 gate + 
 constexpr int kPfBK = 64;
 constexpr int kPfLD = kPfBK + 8;    // LDS row pitch in bf16 (144 B: 16-lane b128 reads hit all 64 banks once)
 
+// Block -> tile: column tiles fastest, then row tiles. `tiles` is the exact number of row tiles
+// (computed on the device from the offsets), so the idle blocks of the worst-case grid are the
+// highest block ids.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool prefill_tile_of_block(int ntn, int tiles, int* m, int* n) {
+  const long long total = static_cast<long long>(ntn) * tiles;
+  const long long L = blockIdx.x;
+  if (L >= total) return false;
+  *m = static_cast<int>(L / ntn);
+  *n = static_cast<int>(L % ntn);
+  return true;
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void gemm_prefill_kernel(
     const uint16_t* __restrict__ A,    // x [T, d] (gate/up) or h [T*k, H] (down)
@@ -42,15 +56,22 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kPfBM * kPfLD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPfBN * kPfLD];
 
-  const TileInfo ti = find_tile(offsets, E, kPfBM, blockIdx.y, sh_tiles);
+  const int ntn = (N + (GATEUP ? kPfBN / 2 : kPfBN) - 1) / (GATEUP ? kPfBN / 2 : kPfBN);
+  const int tiles = tile_scan(offsets, E, kPfBM, sh_tiles);
+  int mt, nt;
+  if (!prefill_tile_of_block(ntn, tiles, &mt, &nt)) return;
+  const TileInfo ti = tile_lookup(E, kPfBM, mt, sh_tiles);
   if (ti.e < 0) return;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int wm = wave & 1, wn = wave >> 1;
-  const int n0 = blockIdx.x * (GATEUP ? kPfBN / 2 : kPfBN);
+  const int n0 = nt * (GATEUP ? kPfBN / 2 : kPfBN);
 
-  // global -> LDS copy assignment: 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 i
+  // global -> LDS copy assignment: 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 i. Rows past
+  // the tile's rows read row 0 of the tile and weight rows past N read row N - 1: the products
+  // they feed land in rows/columns that are never stored (row i of the product depends only on
+  // A row i, column j only on B row j), and the loads stay unconditional.
   const int chunk = tid & 7;
   const int rbase = tid >> 3;
   const uint16_t* aptr[4];
@@ -59,31 +80,27 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = rbase + 32 * i;
-    aptr[i] = nullptr;
-    if (r < ti.rows) {
-      const int p = ti.row0 + r;
-      const long long src = GATEUP ? static_cast<long long>(sorted_rows[p] / k) : p;
-      aptr[i] = A + src * K + chunk * 8;
-    }
-    bptr[i] = nullptr;
-    if (GATEUP) {
-      const int f = n0 + (r & 63);
-      if (f < N) bptr[i] = (r < 64 ? W0 : W1) + ti.e * wstride + static_cast<long long>(f) * K + chunk * 8;
-    } else {
-      const int f = n0 + r;
-      if (f < N) bptr[i] = W0 + ti.e * wstride + static_cast<long long>(f) * K + chunk * 8;
-    }
+    const int p = ti.row0 + (r < ti.rows ? r : 0);
+    const long long src = GATEUP ? static_cast<long long>(sorted_rows[p] / k) : p;
+    aptr[i] = A + src * K + chunk * 8;
+    const int f = min(n0 + (GATEUP ? (r & 63) : r), N - 1);
+    const uint16_t* wsrc = (GATEUP && r >= 64) ? W1 : W0;
+    bptr[i] = wsrc + ti.e * wstride + static_cast<long long>(f) * K + chunk * 8;
   }
 
-  u32x4 ra[4], rb[4];
-  auto load_global = [&](int k0) {
+  // two register stages: the loads of K tile kt + 2 are in flight while tile kt is multiplied
+  // out of LDS and tile kt + 1 (loaded one step earlier) is written to the other LDS buffer
+  u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
+  const int nk = K / kPfBK;
+  auto load_global = [&](u32x4* ra, u32x4* rb, int kt) {
+    const int k0 = min(kt, nk - 1) * kPfBK;  // past the end: re-read the last tile (unused)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = aptr[i] ? load16(aptr[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-      rb[i] = bptr[i] ? load16(bptr[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+      ra[i] = load16(aptr[i] + k0);
+      rb[i] = load16(bptr[i] + k0);
     }
   };
-  auto store_lds = [&](int buf) {
+  auto store_lds = [&](const u32x4* ra, const u32x4* rb, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       store16(&As[buf][(rbase + 32 * i) * kPfLD + chunk * 8], ra[i]);
@@ -98,6 +115,8 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
     if (GATEUP) brow[cb] = (cb < 2 ? 0 : 64) + wn * 32 + (cb & 1) * 16;
     else brow[cb] = wn * 64 + cb * 16;
   }
+  // 16-row blocks of this wave that hold rows of the tile (a wave-uniform count)
+  const int live_mb = min(4, max(0, (ti.rows - wm * 64 + 15) / 16));
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -107,30 +126,42 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
 
   const int l16 = lane & 15;
   const int kq = (lane >> 4) * 8;
-  const int nk = K / kPfBK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * kPfBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kPfBK; kk += 32) {
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = load16(&As[cur][(wm * 64 + mb * 16 + l16) * kPfLD + kk + kq]);
+      u32x4 bf[4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
-        bf[cb] = load16(&Bs[cur][(brow[cb] + l16) * kPfLD + kk + kq]);
+        bf[cb] = load16(&Bs[buf][(brow[cb] + l16) * kPfLD + kk + kq]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb < live_mb) {
+          const u32x4 af = load16(&As[buf][(wm * 64 + mb * 16 + l16) * kPfLD + kk + kq]);
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[mb][cb] = mfma16x16x32(af[mb], bf[cb], acc[mb][cb]);
+          for (int cb = 0; cb < 4; ++cb) acc[mb][cb] = mfma16x16x32(af, bf[cb], acc[mb][cb]);
+        }
+      }
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+  };
+
+  load_global(ra0, rb0, 0);
+  load_global(ra1, rb1, 1);
+  store_lds(ra0, rb0, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    // step kt: LDS buffer 0 holds tile kt, ra1/rb1 tile kt + 1
+    load_global(ra0, rb0, kt + 2);
+    compute(0);
+    store_lds(ra1, rb1, 1);
+    __syncthreads();
+    // step kt + 1: LDS buffer 1 holds tile kt + 1, ra0/rb0 tile kt + 2
+    load_global(ra1, rb1, kt + 3);
+    compute(1);
+    store_lds(ra0, rb0, 0);
     __syncthreads();
   }
+  if (kt < nk) compute(0);  // odd tile count: the last tile sits in buffer 0
 
   // epilogue: lane holds rows 4 * (lane / 16) + r of each 16-row block, column lane % 16
 #pragma unroll
@@ -313,17 +344,23 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t
                                                                      rs2, nullptr, down);
     return hipGetLastError();
   }
-  // grouped GEMM over the dispatch order (rs.offsets / rs.sorted_rows)
-  const int tiles = max_tiles(rows, E, kPfBM);
-  dim3 g1((H + kPfBN / 2 - 1) / (kPfBN / 2), tiles);
-  gemm_prefill_kernel<true><<<g1, 256, 0, s>>>(x, wg, wu, d, H, E, k, rs.offsets, rs.sorted_rows,
-                                               h, none);
+  // grouped GEMM over the dispatch order (rs.offsets / rs.sorted_rows); a 1-D grid sized for
+  // the worst-case tile count, rounded up to whole XCD rounds
+  const long long tiles = max_tiles(rows, E, kPfBM);
+  auto grid_for = [&](int ntn) {
+    const long long total = tiles * ntn;
+    return static_cast<unsigned>((total + kXcds - 1) / kXcds * kXcds);
+  };
+  const int ntn1 = (H + kPfBN / 2 - 1) / (kPfBN / 2);
+  gemm_prefill_kernel<true><<<grid_for(ntn1), 256, 0, s>>>(x, wg, wu, d, H, E, k, rs.offsets,
+                                                           rs.sorted_rows, h, none);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = record_stage_event(mid_event, s)) != hipSuccess) return err;
-  dim3 g2((d + kPfBN - 1) / kPfBN, tiles);
-  gemm_prefill_kernel<false><<<g2, 256, 0, s>>>(h, wd, nullptr, H, d, E, k, rs.offsets,
-                                                rs.sorted_rows, nullptr, down);
+  const int ntn2 = (d + kPfBN - 1) / kPfBN;
+  gemm_prefill_kernel<false><<<grid_for(ntn2), 256, 0, s>>>(h, wd, nullptr, H, d, E, k,
+                                                            rs.offsets, rs.sorted_rows, nullptr,
+                                                            down);
   return hipGetLastError();
 }
 

@@ -3,7 +3,9 @@
 // stacks of zonos2.cpp INTERNALS, "Recommended: F16 spine + K-quant experts".
 //
 // Tiles: 16 grouped rows x 64 output features per block of 256 threads, K staged through LDS in
-// chunks of 32. Thread (row = tid / 16, c = tid % 16) owns features c, c+16, c+32, c+48.
+// chunks of 64 (float4 copies, all of a chunk's loads issued together, the next chunk loading
+// while the current one is used). Thread (row = tid / 16, c = tid % 16) owns features c, c+16,
+// c+32, c+48.
 #include "common.hpp"
 #include "down_epilogue.hpp"
 #include "kernels.hpp"
@@ -14,7 +16,10 @@ namespace {
 
 constexpr int kBM = 16;
 constexpr int kBN = 64;
-constexpr int kBK = 32;
+constexpr int kBK = 64;
+constexpr int kLd = kBK + 4;  // pitch in floats; keeps rows 16-byte aligned
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void ffn_f32_kernel(
@@ -24,9 +29,9 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
     int K, int N, int E, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_rows, float* __restrict__ h_out, DownArgs down) {
   __shared__ int sh_tiles[2 * (kMaxE + 1)];
-  __shared__ float As[kBM][kBK + 1];
-  __shared__ float B0[kBN][kBK + 1];
-  __shared__ float B1[GATEUP ? kBN : 1][kBK + 1];
+  __shared__ __attribute__((aligned(16))) float As[kBM * kLd];
+  __shared__ __attribute__((aligned(16))) float B0[kBN * kLd];
+  __shared__ __attribute__((aligned(16))) float B1[(GATEUP ? kBN : 1) * kLd];
   const TileInfo ti = find_tile(offsets, E, kBM, blockIdx.y, sh_tiles);
   if (ti.e < 0) return;
   const int n0 = blockIdx.x * kBN;
@@ -34,37 +39,54 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
   const int row = tid / 16;
   const int c = tid % 16;
 
-  // source row of A for each of the 16 tile rows (loaded by threads 0..15 of each pass)
-  const float* w0e = w0 + static_cast<long long>(ti.e) * N * K;
-  const float* w1e = GATEUP ? w1 + static_cast<long long>(ti.e) * N * K : nullptr;
+  // copy assignment: A row tid / 16, float4 column tid % 16; B rows tid / 16 + 16 i
+  const long long wbase = static_cast<long long>(ti.e) * N * K;
+  const float* arow = nullptr;
+  if (row < ti.rows) {
+    const int p = ti.row0 + row;
+    const long long src = GATEUP ? static_cast<long long>(sorted_rows[p] / k) : p;
+    arow = a_src + src * K;
+  }
+  const float* brow0[4];
+  const float* brow1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + row + 16 * i;
+    brow0[i] = n < N ? w0 + wbase + static_cast<long long>(n) * K : nullptr;
+    brow1[i] = (GATEUP && n < N) ? w1 + wbase + static_cast<long long>(n) * K : nullptr;
+  }
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 ra, rb0[4], rb1[4];
+  auto load = [&](int k0) {
+    const int kk = k0 + c * 4;  // K % 4 == 0: a float4 is either whole or past the end
+    const bool ok = kk < K;
+    ra = (arow && ok) ? ld4(arow + kk) : z4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rb0[i] = (brow0[i] && ok) ? ld4(brow0[i] + kk) : z4;
+      if constexpr (GATEUP) rb1[i] = (brow1[i] && ok) ? ld4(brow1[i] + kk) : z4;
+    }
+  };
 
   float acc0[4] = {0.f, 0.f, 0.f, 0.f};
   float acc1[4] = {0.f, 0.f, 0.f, 0.f};
+  load(0);
   for (int k0 = 0; k0 < K; k0 += kBK) {
-    for (int i = tid; i < kBM * kBK; i += 256) {
-      const int r = i / kBK, kk = i % kBK;
-      float v = 0.f;
-      if (r < ti.rows && k0 + kk < K) {
-        const int p = ti.row0 + r;
-        const long long src = GATEUP ? static_cast<long long>(sorted_rows[p] / k) : p;
-        v = a_src[src * K + k0 + kk];
-      }
-      As[r][kk] = v;
-    }
-    for (int i = tid; i < kBN * kBK; i += 256) {
-      const int r = i / kBK, kk = i % kBK;
-      const bool ok = (n0 + r < N) && (k0 + kk < K);
-      B0[r][kk] = ok ? w0e[static_cast<long long>(n0 + r) * K + k0 + kk] : 0.f;
-      if constexpr (GATEUP) B1[r][kk] = ok ? w1e[static_cast<long long>(n0 + r) * K + k0 + kk] : 0.f;
+    *reinterpret_cast<float4*>(&As[row * kLd + c * 4]) = ra;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4*>(&B0[(row + 16 * i) * kLd + c * 4]) = rb0[i];
+      if constexpr (GATEUP) *reinterpret_cast<float4*>(&B1[(row + 16 * i) * kLd + c * 4]) = rb1[i];
     }
     __syncthreads();
-#pragma unroll 8
+    if (k0 + kBK < K) load(k0 + kBK);  // next chunk in flight during the products
+#pragma unroll 16
     for (int kk = 0; kk < kBK; ++kk) {
-      const float a = As[row][kk];
+      const float a = As[row * kLd + kk];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc0[i] = fmaf(a, B0[c + 16 * i][kk], acc0[i]);
-        if constexpr (GATEUP) acc1[i] = fmaf(a, B1[c + 16 * i][kk], acc1[i]);
+        acc0[i] = fmaf(a, B0[(c + 16 * i) * kLd + kk], acc0[i]);
+        if constexpr (GATEUP) acc1[i] = fmaf(a, B1[(c + 16 * i) * kLd + kk], acc1[i]);
       }
     }
     __syncthreads();

@@ -30,32 +30,9 @@ struct RouteOut {
   int32_t* ids;         // [T, k]
   float* w;             // [T, k]
   int32_t* counts;      // [E], accumulated with integer atomics on a zeroed array
-  int32_t* block_hist;  // [ceil(T/16), E] expert histogram of each block's 16*k rows
-  int32_t* lrank;       // [T*k] rank of row r among its block's rows of the same expert
   float* zero_y;        // [T, d] cleared (for the two-addend atomic combine)
   int d;
 };
-
-// Stable per-block histogram and ranks of the `nrows` assignment rows whose experts sit in LDS
-// `sids` (row i of the block is assignment row row0 + i). Every thread of the block calls it.
-__device__ inline void block_hist_rank(const int* sids, int nrows, int E, int row0,
-                                       int32_t* block_hist, int32_t* lrank) {
-  if (lrank) {
-    for (int i = threadIdx.x; i < nrows; i += blockDim.x) {
-      const int e = sids[i];
-      int rank = 0;
-      for (int j = 0; j < i; ++j) rank += sids[j] == e;
-      lrank[row0 + i] = rank;
-    }
-  }
-  if (block_hist) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      int c = 0;
-      for (int j = 0; j < nrows; ++j) c += sids[j] == e;
-      block_hist[static_cast<long long>(blockIdx.x) * E + e] = c;
-    }
-  }
-}
 
 // Stage marker for the optional timing events: an external event node while `s` is being
 // captured into a graph, a plain event record otherwise (defined in moe_api.hip).
@@ -80,17 +57,10 @@ hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const 
                                    float* logits_out, const RouteOut& o, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch (permute.hip)
-// Bytes of scratch the dispatch needs for T tokens (block histograms, ranks, block bases).
-size_t dispatch_scratch_bytes(int T, int E, int k);
-// From expert ids alone (moe_permute): block histograms + ranks, then the scan/scatter.
-hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
-                          int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
-                          void* scratch, hipStream_t s);
-// The scan/scatter alone, when the routing kernel already wrote block_hist and lrank.
-hipError_t launch_scan_scatter(const int32_t* ids, const int32_t* block_hist,
-                               const int32_t* lrank, int T, int E, int k, int32_t* offsets,
-                               int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
-                               int32_t* base_scratch, hipStream_t s);
+// offsets [E+1], sorted_rows / row_pos [n_rows] from the expert ids; counts_out may be NULL.
+hipError_t launch_dispatch(const int32_t* ids, int n_rows, int E, int32_t* offsets,
+                           int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
+                           hipStream_t s);
 
 // ---------------------------------------------------------------- experts (ffn_*.hip)
 // Where a grouped FFN finds the rows of expert e:

@@ -4,7 +4,7 @@
 
 #include <cstdint>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -43,7 +43,7 @@ int check_scoring(int scoring, const float* sel_bias) {
 
 // Device workspace regions of the fused layer (the step calls use a subset).
 struct Layout {
-  size_t h, logits, ids, w, counts, offsets, sorted_rows, row_pos, dispatch, eo, total;
+  size_t h, logits, ids, w, counts, offsets, sorted_rows, row_pos, eo, total;
   Layout(int T, int d, int E, int H, int k, int dtype) {
     const size_t rows = static_cast<size_t>(T) * k;
     size_t o = 0;
@@ -55,23 +55,11 @@ struct Layout {
     offsets = o;     o += up(static_cast<size_t>(E + 1) * 4);
     sorted_rows = o; o += up(rows * 4);
     row_pos = o;     o += up(rows * 4);
-    dispatch = o;    o += up(moe::dispatch_scratch_bytes(T, E, k));
-    eo = o;          o += k > 2 ? up(rows * d * 4) : 0;
+    // fp32 expert outputs staged for the combine kernel: k > 2 always; k == 2 outside the
+    // streaming (decode) path, where the down epilogue would otherwise issue T*k*d atomic adds
+    const bool stage = k > 2 || (k == 2 && !(dtype == MOE_BF16 && moe::ffn_bf16_streaming(T, d, E, H, k)));
+    eo = o;          o += stage ? up(rows * d * 4) : 0;
     total = o;
-  }
-};
-
-// Sub-regions of the dispatch scratch: block histograms, block bases, ranks.
-struct DispatchScratch {
-  int32_t* hist;
-  int32_t* base;
-  int32_t* lrank;
-  DispatchScratch(void* p, int T, int E) {
-    const size_t nb = (static_cast<size_t>(T) + moe::kTokTile - 1) / moe::kTokTile;
-    char* c = static_cast<char*>(p);
-    hist = reinterpret_cast<int32_t*>(c);
-    base = reinterpret_cast<int32_t*>(c + up(nb * E * 4));
-    lrank = reinterpret_cast<int32_t*>(c + 2 * up(nb * E * 4));
   }
 };
 
@@ -130,11 +118,6 @@ size_t moe_workspace_size(int T, int d, int E, int H, int k, int dtype) {
   return Layout(T, d, E, H, k, dtype).total;
 }
 
-size_t moe_permute_workspace_size(int T, int E, int k) {
-  if (check_route_dims(T, E, k) != MOE_OK || T == 0) return 0;
-  return moe::dispatch_scratch_bytes(T, E, k);
-}
-
 int moe_router_logits(const void* x, const void* w_router, const float* router_bias, int T, int d,
                       int E, int dtype, float* logits, void* stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -168,14 +151,13 @@ int moe_route(const float* logits, const float* sel_bias, int T, int E, int k, i
       !aligned16(expert_counts) || (sel_bias && !aligned16(sel_bias)))
     return MOE_ERR_SHAPE;
   clear_stale_error();
-  const RouteOut o{topk_ids, topk_w, expert_counts, nullptr, nullptr, nullptr, 0};
+  const RouteOut o{topk_ids, topk_w, expert_counts, nullptr, 0};
   return hip_status(moe::launch_route_from_logits(logits, sel_bias, T, E, k, scoring, o,
                                                   static_cast<hipStream_t>(stream)));
 }
 
 int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, int E, int k,
-                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* ws,
-                size_t ws_bytes, void* stream) {
+                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* stream) {
   const int st = check_route_dims(T, E, k);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -183,11 +165,9 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, in
   if (!aligned16(topk_ids) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
       !aligned16(sorted_rows) || !aligned16(row_pos))
     return MOE_ERR_SHAPE;
-  if (!ws || ws_bytes < moe::dispatch_scratch_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
-  if (!aligned16(ws)) return MOE_ERR_SHAPE;
   clear_stale_error();
-  return hip_status(moe::launch_permute(topk_ids, T, E, k, expert_offsets, sorted_rows, row_pos,
-                                        nullptr, ws, static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_dispatch(topk_ids, T * k, E, expert_offsets, sorted_rows, row_pos,
+                                         nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* w_up,
@@ -261,11 +241,14 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   int32_t* offsets = at<int32_t>(ws, lay.offsets);
   int32_t* sorted_rows = at<int32_t>(ws, lay.sorted_rows);
   int32_t* row_pos = at<int32_t>(ws, lay.row_pos);
-  const DispatchScratch ds(at<void>(ws, lay.dispatch), T, E);
   float* eo = at<float>(ws, lay.eo);
-  float* zero_y = k == 2 ? a->y : nullptr;
   // few rows per expert (decode): the expert kernels find their rows from the ids themselves
   const bool streaming = dtype == MOE_BF16 && moe::ffn_bf16_streaming(T, d, E, H, k);
+  // k == 2 adds two weighted outputs into a cleared y with fp32 atomics (deterministic: two
+  // addends onto 0) on the streaming path; elsewhere, and for k > 2, expert outputs are staged
+  // and combined in slot order
+  const bool atomic_y = k == 2 && streaming;
+  float* zero_y = atomic_y ? a->y : nullptr;
 
   DownArgs down{};
   down.topk_w = w;
@@ -273,7 +256,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   if (k == 1) {
     down.mode = moe::kDownStoreY;
     down.out = a->y;
-  } else if (k == 2) {
+  } else if (atomic_y) {
     down.mode = moe::kDownAtomicY;
     down.out = a->y;
   } else {
@@ -281,8 +264,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
     down.out = eo;
   }
 
-  const RouteOut ro{ids, w, nullptr, streaming ? nullptr : ds.hist,
-                    streaming ? nullptr : ds.lrank, zero_y, d};
+  const RouteOut ro{ids, w, nullptr, zero_y, d};
   MOE_TRY(mark(0));
   if (dtype == MOE_BF16) {
     MOE_TRY(moe::launch_route_fused_bf16(
@@ -297,8 +279,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   }
   MOE_TRY(mark(1));
   if (!streaming)
-    MOE_TRY(moe::launch_scan_scatter(ids, ds.hist, ds.lrank, T, E, k, offsets, sorted_rows,
-                                     row_pos, counts, ds.base, s));
+    MOE_TRY(moe::launch_dispatch(ids, T * k, E, offsets, sorted_rows, row_pos, counts, s));
   MOE_TRY(mark(2));
   void* mid = ev ? ev[3] : nullptr;
   if (dtype == MOE_BF16) {
@@ -314,9 +295,10 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
         static_cast<const float*>(a->w_up), static_cast<const float*>(a->w_down), T, d, E, H, k,
         offsets, sorted_rows, at<float>(ws, lay.h), down, s, mid));
   }
-  // k > 2: expert outputs were staged (by assignment row on the streaming path, in dispatch
-  // order otherwise) and are combined in slot order
-  if (k > 2) MOE_TRY(moe::launch_combine(eo, streaming ? nullptr : row_pos, w, T, d, k, a->y, s));
+  // staged expert outputs (by assignment row on the streaming path, in dispatch order
+  // otherwise) are combined in slot order
+  if (k > 1 && !atomic_y)
+    MOE_TRY(moe::launch_combine(eo, streaming ? nullptr : row_pos, w, T, d, k, a->y, s));
   MOE_TRY(mark(4));
   return MOE_OK;
 }

@@ -15,10 +15,6 @@
 // with 8 waves that split the experts (16 per MFMA tile) and, when there are few experts, the
 // d-long reduction; each wave issues the loads of 8 MFMA steps before using them. Partial tiles
 // are added in a fixed order, so the logits are the same on every call.
-//
-// The routing tail also emits, per block, the expert histogram of its 16*k assignment rows and the
-// stable rank of every row among the block's rows of the same expert; a one-block scan then
-// turns these into the grouped (dispatch) order without any atomics.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -115,7 +111,7 @@ __device__ void select_and_weigh(const float* row, const float* sbias, int E, in
 // Selection on the LDS logit tile of the block's 16 tokens, then the outputs. Called by every
 // thread of the block (barriers inside); threads >= 256 only help with the epilogue loops.
 __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0, int T, int E,
-                           int k, int scoring, const RouteOut& o, int* hist, int* sids) {
+                           int k, int scoring, const RouteOut& o, int* hist) {
   const int tl = threadIdx.x / kQ;
   const int q = threadIdx.x % kQ;
   const int t = t0 + tl;
@@ -129,7 +125,6 @@ __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0
         if (j < k) {
           o.ids[static_cast<long long>(t) * k + j] = ids[j];
           o.w[static_cast<long long>(t) * k + j] = w[j];
-          sids[tl * k + j] = ids[j];
           if (o.counts) atomicAdd(&hist[ids[j]], 1);
         }
       }
@@ -142,8 +137,6 @@ __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0
       else if (hist[e]) atomicAdd(&o.counts[e], hist[e]);
     }
   }
-  if (o.block_hist || o.lrank)
-    block_hist_rank(sids, min(kTokTile, T - t0) * k, E, t0 * k, o.block_hist, o.lrank);
   if (o.zero_y) {
     const int rows = min(kTokTile, T - t0);
     const int vec = o.d / 4;
@@ -160,7 +153,6 @@ __global__ __launch_bounds__(kTailThreads) void route_from_logits_kernel(
   float* tile = smem;                              // [16][E+1]
   float* sbias = tile + kTokTile * ld;             // [E]
   int* hist = reinterpret_cast<int*>(sbias + E);   // [E]
-  int* sids = hist + E;                            // [16 * kMaxK]
   const int t0 = blockIdx.x * kTokTile;
   for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
     const int tl = i / E, e = i % E;
@@ -172,7 +164,7 @@ __global__ __launch_bounds__(kTailThreads) void route_from_logits_kernel(
     hist[e] = 0;
   }
   __syncthreads();
-  route_tail(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist, sids);
+  route_tail(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
 }
 
 // How the 8 waves of the fused kernel split the logit tile: `neb` 16-expert column blocks, each
@@ -196,7 +188,6 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
   float* part = smem;                                  // [ksplit][16][E+1]; part[0] = tile
   float* sbias = part + ksplit * kTokTile * ld;        // [E]
   int* hist = reinterpret_cast<int*>(sbias + E);       // [E]
-  int* sids = hist + E;                                // [16 * kMaxK]
   const int t0 = blockIdx.x * kTokTile;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -256,7 +247,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
     }
   }
   if (o.ids == nullptr) return;  // logits only (uniform across the block)
-  route_tail(part, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist, sids);
+  route_tail(part, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
 }
 
 // fp32 router logits: one thread per (token, expert), four interleaved partial sums.
@@ -283,12 +274,12 @@ __global__ void logits_f32_kernel(const float* __restrict__ x, const float* __re
 
 size_t tail_smem(int E) {
   return sizeof(float) * (static_cast<size_t>(kTokTile) * (E + 1) + E) +
-         sizeof(int) * (E + kTokTile * kMaxK);
+         sizeof(int) * E;
 }
 
 size_t fused_smem(int E) {
   return sizeof(float) * (static_cast<size_t>(route_ksplit(E)) * kTokTile * (E + 1) + E) +
-         sizeof(int) * (E + kTokTile * kMaxK);
+         sizeof(int) * E;
 }
 
 }  // namespace

@@ -30,9 +30,8 @@ MOE_SCORING_SELECTED_SOFTMAX = 1
 
 SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELECTED_SOFTMAX}
 
-EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size",
-           "moe_permute_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
+           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
 
 
 class MoeError(RuntimeError):
@@ -74,11 +73,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_route.restype = c_int
     lib.moe_route.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
                               c_void_p, c_void_p]
-    lib.moe_permute_workspace_size.restype = c_size_t
-    lib.moe_permute_workspace_size.argtypes = [c_int] * 3
     lib.moe_permute.restype = c_int
     lib.moe_permute.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
-                                c_void_p, c_void_p, c_size_t, c_void_p]
+                                c_void_p, c_void_p]
     lib.moe_expert_ffn.restype = c_int
     lib.moe_expert_ffn.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                    c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -159,10 +156,6 @@ def moe_workspace_size(T, d, E, H, k, dtype) -> int:
     return int(LIB.moe_workspace_size(T, d, E, H, k, dtype))
 
 
-def moe_permute_workspace_size(T, E, k) -> int:
-    return int(LIB.moe_permute_workspace_size(T, E, k))
-
-
 def moe_router_logits(x, w_router, router_bias=None, logits=None, stream=None):
     T, d = x.shape
     E = w_router.shape[0]
@@ -196,7 +189,7 @@ def moe_route(logits, k, scoring, sel_bias=None, topk_ids=None, topk_w=None, exp
 
 
 def moe_permute(topk_ids, expert_counts, E, expert_offsets=None, sorted_rows=None, row_pos=None,
-                workspace=None, stream=None):
+                stream=None):
     T, k = topk_ids.shape
     _need(topk_ids, "topk_ids", (T, k), torch.int32)
     _need(expert_counts, "expert_counts", (E,), torch.int32)
@@ -206,12 +199,8 @@ def moe_permute(topk_ids, expert_counts, E, expert_offsets=None, sorted_rows=Non
     _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32)
     _need(sorted_rows, "sorted_rows", (T * k,), torch.int32)
     _need(row_pos, "row_pos", (T * k,), torch.int32)
-    if workspace is None:
-        workspace = torch.empty(max(1, moe_permute_workspace_size(T, E, k)), dtype=torch.uint8,
-                                device=topk_ids.device)
     _check(LIB.moe_permute(_ptr(topk_ids), _ptr(expert_counts), T, E, k, _ptr(expert_offsets),
-                           _ptr(sorted_rows), _ptr(row_pos), _ptr(workspace), workspace.numel(),
-                           _stream(stream)), "moe_permute")
+                           _ptr(sorted_rows), _ptr(row_pos), _stream(stream)), "moe_permute")
     return expert_offsets, sorted_rows, row_pos
 
 

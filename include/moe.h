@@ -117,9 +117,6 @@ int moe_router_logits(const void* x, const void* w_router, const float* router_b
 int moe_route(const float* logits, const float* sel_bias, int T, int E, int k, int scoring,
               int32_t* topk_ids, float* topk_w, int32_t* expert_counts, void* stream);
 
-/* Bytes of device workspace moe_permute needs (0 when T == 0 or the sizes are invalid). */
-size_t moe_permute_workspace_size(int T, int E, int k);
-
 /*
  * Dispatch, step 4: groups the T*k assignment rows r = t*k + j by expert. The pages name the
  * grouped expert matmul over the expert stacks (zonos2.cpp INTERNALS, "Performance": mul_mat_id
@@ -134,12 +131,10 @@ size_t moe_permute_workspace_size(int T, int E, int k);
  *   expert_offsets[E + 1] int32  output
  *   sorted_rows   [T * k] int32  output
  *   row_pos       [T * k] int32  output
- *   ws, ws_bytes                 device workspace of at least moe_permute_workspace_size(T, E, k)
  * All results are exact integers, identical on every call.
  */
 int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, int E, int k,
-                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* ws,
-                size_t ws_bytes, void* stream);
+                int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos, void* stream);
 
 /*
  * Expert FFN, steps 5-6: for every expert e and every row at position p of its group

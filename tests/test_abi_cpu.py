@@ -48,8 +48,12 @@ def test_workspace_size():
     assert 0 < a < b
     # h (bf16) alone is T*k*H*2 bytes
     assert a >= 64 * 2816 * 2
-    # k > 2 adds the fp32 expert_out staging
-    assert L.moe_workspace_size(64, 128, 8, 256, 3, 0) > L.moe_workspace_size(64, 128, 8, 256, 2, 0) * 1.5
+    # k >= 2 outside the weight-streaming path stages fp32 expert outputs: T*k*d*4 more bytes
+    assert L.moe_workspace_size(64, 128, 8, 256, 2, 0) - L.moe_workspace_size(64, 128, 8, 256, 1, 0) \
+        >= 64 * 2 * 128 * 4
+    # the streaming path (bf16, few rows per expert, d and H multiples of 256) adds k == 2 outputs
+    # into y directly and stages nothing
+    assert L.moe_workspace_size(64, 1024, 64, 512, 2, 1) < 64 * 2 * 1024 * 4
 
 
 def test_route_validation():
@@ -73,17 +77,11 @@ def test_route_validation():
 
 def test_permute_combine_logits_validation():
     L = moe.LIB
-    pws = L.moe_permute_workspace_size(4, 8, 1)
-    assert pws > 0 and L.moe_permute_workspace_size(0, 8, 1) == 0
-    assert L.moe_permute_workspace_size(4, 8, 9) == 0
-    perm = lambda T=4, k=1, c=FAKE, sr=FAKE, w=FAKE, n=pws: L.moe_permute(
-        FAKE, c, T, 8, k, FAKE, sr, FAKE, w, n, None)
+    perm = lambda T=4, k=1, c=FAKE, sr=FAKE: L.moe_permute(FAKE, c, T, 8, k, FAKE, sr, FAKE, None)
     assert perm(T=0) == moe.MOE_OK
     assert perm(k=9) == moe.MOE_ERR_SHAPE
     assert perm(c=None) == moe.MOE_ERR_NULL
     assert perm(sr=MISALIGNED) == moe.MOE_ERR_SHAPE
-    assert perm(w=None) == moe.MOE_ERR_WORKSPACE
-    assert perm(n=pws - 1) == moe.MOE_ERR_WORKSPACE
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 6, 1, FAKE, None) == moe.MOE_ERR_SHAPE     # d % 4
     assert L.moe_combine(FAKE, None, FAKE, 4, 8, 1, FAKE, None) == moe.MOE_ERR_NULL
     assert L.moe_combine(FAKE, FAKE, FAKE, 0, 8, 1, FAKE, None) == moe.MOE_OK
