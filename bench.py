@@ -310,7 +310,7 @@ def main():
     streaming = inp.dtype == "bf16" and T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and \
         T * k <= 32 * E
     roof["kernel"] = "ffn_stream_kernel<true>" if streaming else (
-        "gemm_prefill_kernel<true>" if inp.dtype == "bf16" else "ffn_f32_kernel<true>")
+        "gemm_dma_kernel<true, 256, 128>" if inp.dtype == "bf16" else "ffn_f32_kernel<true>")
     traffic = measured_traffic(roof["kernel"], args.workload)
     roof["traffic"] = traffic
     roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"

@@ -14,8 +14,9 @@
 //    flight, with the expert's token rows read alongside from L2. The block finds its expert's
 //    rows itself (from the dispatch order, or by scanning the expert ids), so the decode layer
 //    needs no dispatch kernel.
-//  * prefill (many rows per expert): a grouped GEMM with 128 x 128 block tiles, A (gathered rows)
-//    and B (weights) staged through double-buffered LDS, 2 x 2 waves of 64 x 64 each.
+//  * prefill (many rows per expert): a grouped GEMM over the dispatch order with 256 x 128 block
+//    tiles, operands copied from global memory straight into a 3-slot LDS ring (no register
+//    staging), 8 waves of 64 x 64 each, two blocks per CU.
 #include "common.hpp"
 #include "down_epilogue.hpp"
 #include "kernels.hpp"
@@ -26,16 +27,9 @@ namespace {
 
 // ------------------------------------------------------------------------------------ prefill
 
-constexpr int kPfBM = 128;
-constexpr int kPfBN = 128;          // weight rows per tile (gate/up: 64 gate + 64 up)
-constexpr int kPfBK = 64;
-constexpr int kPfLD = kPfBK + 8;    // LDS row pitch in bf16 (144 B: 16-lane b128 reads hit all 64 banks once)
-
 // Block -> tile: column tiles fastest, then row tiles. `tiles` is the exact number of row tiles
 // (computed on the device from the offsets), so the idle blocks of the worst-case grid are the
 // highest block ids.
-constexpr int kXcds = 8;
-
 __device__ __forceinline__ bool prefill_tile_of_block(int ntn, int tiles, int* m, int* n) {
   const long long total = static_cast<long long>(ntn) * tiles;
   const long long L = blockIdx.x;
@@ -45,127 +39,185 @@ __device__ __forceinline__ bool prefill_tile_of_block(int ntn, int tiles, int* m
   return true;
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(
-    const uint16_t* __restrict__ A,    // x [T, d] (gate/up) or h [T*k, H] (down)
-    const uint16_t* __restrict__ W0,   // w_gate [E, H, d] or w_down [E, d, H]
-    const uint16_t* __restrict__ W1,   // w_up [E, H, d]
-    int K, int N, int E, int k, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_rows, uint16_t* __restrict__ h_out, DownArgs down) {
-  __shared__ int sh_tiles[2 * (kMaxE + 1)];
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kPfBM * kPfLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kPfBN * kPfLD];
+// Grouped GEMM with loads straight from global memory into LDS (global_load_lds_dwordx4: each
+// lane's 16 bytes land at base + 16 * lane, so one wave instruction fills 1 KB = 16 rows of a
+// 32-wide K step). A ring of kRing K steps lives in LDS; the loads of step kt + kRing - 1 are
+// issued right after the barrier that retires step kt - 1, so kRing - 1 steps are in flight
+// behind the products. One barrier per K step.
+// LDS rows are 64 bytes (32 bf16); the four 16-byte pieces of row r sit at position
+// piece ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3, so a fragment read (16 consecutive rows, one
+// piece) touches 16 distinct 16-byte bank groups.
+// Three slots of a 256 x 128 tile take 72 KB, so two blocks (16 waves, <= 128 VGPRs each) share
+// a CU and one block's barrier wait is covered by the other's products; measured faster than
+// 256 x 256 tiles at one block per CU despite the larger L2 traffic.
+constexpr int kDBK = 32;
+constexpr int kRing = 3;
 
-  const int ntn = (N + (GATEUP ? kPfBN / 2 : kPfBN) - 1) / (GATEUP ? kPfBN / 2 : kPfBN);
-  const int tiles = tile_scan(offsets, E, kPfBM, sh_tiles);
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `behind` steps of CPW loads each are outstanding (behind <= B)
+template <int B, int CPW>
+__device__ __forceinline__ void wait_steps_behind(int behind) {
+  if constexpr (B == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (behind >= B) wait_vmcnt<B * CPW>();
+    else wait_steps_behind<B - 1, CPW>(behind);
+  }
+}
+
+// 16 bytes per lane from `g` into LDS at byte address lds + 16 * lane (lds wave-uniform). Issued
+// as inline asm so that the compiler's own wait-count tracking (which would otherwise wait for
+// every outstanding DMA before any LDS read) leaves the pipeline alone; the waits are explicit.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool GATEUP, int BM, int BN>
+__global__ __launch_bounds__(512) void gemm_dma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
+    const uint16_t* __restrict__ W1, int K, int N, int E, int k,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
+    uint16_t* __restrict__ h_out, DownArgs down) {
+  constexpr int WMW = BM / 64;              // waves along M (64 rows each)
+  constexpr int WNW = 8 / WMW;              // waves along N
+  constexpr int WN = BN / WNW;              // columns per wave
+  constexpr int MB = 4;                     // 16-row blocks per wave
+  constexpr int NBK = WN / 16;              // 16-column blocks per wave
+  constexpr int CHA = BM / 16, CHB = BN / 16;     // 1 KB chunks per K step
+  constexpr int CPW = (CHA + CHB) / 8;            // chunks per wave per K step
+  static_assert((CHA + CHB) % 8 == 0, "chunks split over 8 waves");
+  constexpr int STAGE = (BM + BN) * kDBK;         // bf16 elements per ring slot
+  constexpr int FEAT = GATEUP ? BN / 2 : BN;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[kRing * STAGE];
+  static_assert(2 * (kMaxE + 1) * 4 <= STAGE * 2, "tile table fits one slot");
+  int* sh_tiles = reinterpret_cast<int*>(&ring[(kRing - 1) * STAGE]);
+
+  const int ntn = (N + FEAT - 1) / FEAT;
+  const int tiles = tile_scan(offsets, E, BM, sh_tiles);
   int mt, nt;
   if (!prefill_tile_of_block(ntn, tiles, &mt, &nt)) return;
-  const TileInfo ti = tile_lookup(E, kPfBM, mt, sh_tiles);
+  const TileInfo ti = tile_lookup(E, BM, mt, sh_tiles);
   if (ti.e < 0) return;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int n0 = nt * (GATEUP ? kPfBN / 2 : kPfBN);
-
-  // global -> LDS copy assignment: 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 i. Rows past
-  // the tile's rows read row 0 of the tile and weight rows past N read row N - 1: the products
-  // they feed land in rows/columns that are never stored (row i of the product depends only on
-  // A row i, column j only on B row j), and the loads stay unconditional.
-  const int chunk = tid & 7;
-  const int rbase = tid >> 3;
-  const uint16_t* aptr[4];
-  const uint16_t* bptr[4];
+  // wave w runs on SIMD w % 4; bands of 64 rows go to wave pairs (w / WNW), so a tile whose rows
+  // end within its first half still keeps every SIMD busy with one wave (the others skip)
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int n0 = nt * FEAT;
   const long long wstride = static_cast<long long>(N) * K;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = rbase + 32 * i;
-    const int p = ti.row0 + (r < ti.rows ? r : 0);
-    const long long src = GATEUP ? static_cast<long long>(sorted_rows[p] / k) : p;
-    aptr[i] = A + src * K + chunk * 8;
-    const int f = min(n0 + (GATEUP ? (r & 63) : r), N - 1);
-    const uint16_t* wsrc = (GATEUP && r >= 64) ? W1 : W0;
-    bptr[i] = wsrc + ti.e * wstride + static_cast<long long>(f) * K + chunk * 8;
-  }
 
-  // two register stages: the loads of K tile kt + 2 are in flight while tile kt is multiplied
-  // out of LDS and tile kt + 1 (loaded one step earlier) is written to the other LDS buffer
-  u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
-  const int nk = K / kPfBK;
-  auto load_global = [&](u32x4* ra, u32x4* rb, int kt) {
-    const int k0 = min(kt, nk - 1) * kPfBK;  // past the end: re-read the last tile (unused)
+  // this lane's source rows: chunk j = wave + 8 c covers LDS rows 16 j .. 16 j + 15 of the
+  // step (A rows first, then B rows); lane i fills row 16 j + i / 4, position i % 4
+  const uint16_t* src[CPW];
+  int ldsoff[CPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = load16(aptr[i] + k0);
-      rb[i] = load16(bptr[i] + k0);
+  for (int c = 0; c < CPW; ++c) {
+    const int j = wave + 8 * c;
+    const int r = 16 * j + lane / 4;        // row of the step tile (A: < BM)
+    const int pos = lane & 3;
+    if (j < CHA) {
+      const int pr = ti.row0 + (r < ti.rows ? r : 0);
+      const long long arow = GATEUP ? static_cast<long long>(sorted_rows[pr] / k) : pr;
+      src[c] = A + arow * K + ((pos ^ swz(r)) * 8);
+    } else {
+      const int rb = r - BM;
+      const int f = min(n0 + (GATEUP ? (rb % FEAT) : rb), N - 1);
+      const uint16_t* wsrc = (GATEUP && rb >= FEAT) ? W1 : W0;
+      src[c] = wsrc + ti.e * wstride + static_cast<long long>(f) * K + ((pos ^ swz(rb)) * 8);
     }
-  };
-  auto store_lds = [&](const u32x4* ra, const u32x4* rb, int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      store16(&As[buf][(rbase + 32 * i) * kPfLD + chunk * 8], ra[i]);
-      store16(&Bs[buf][(rbase + 32 * i) * kPfLD + chunk * 8], rb[i]);
-    }
-  };
-
-  // B rows read by this wave for column block cb (gate/up: cb 0,1 gate; cb 2,3 the matching up)
-  int brow[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    if (GATEUP) brow[cb] = (cb < 2 ? 0 : 64) + wn * 32 + (cb & 1) * 16;
-    else brow[cb] = wn * 64 + cb * 16;
+    ldsoff[c] = 16 * j * kDBK;              // element offset of the chunk inside a slot
   }
-  // 16-row blocks of this wave that hold rows of the tile (a wave-uniform count)
-  const int live_mb = min(4, max(0, (ti.rows - wm * 64 + 15) / 16));
-
-  f32x4 acc[4][4];
+  const int nk = K / kDBK;
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int kt) {
+    const int slot = kt % kRing;
+    const int k0 = min(kt, nk - 1) * kDBK;  // prologue past the end: re-read the last step
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CPW; ++c)
+      dma16(src[c] + k0, ring0 + 2u * static_cast<uint32_t>(slot * STAGE + ldsoff[c]));
+  };
 
+  int brow[NBK];
+#pragma unroll
+  for (int cb = 0; cb < NBK; ++cb) {
+    if (GATEUP) brow[cb] = (cb < NBK / 2 ? 0 : FEAT) + wn * (WN / 2) + (cb % (NBK / 2)) * 16;
+    else brow[cb] = wn * WN + cb * 16;
+  }
+  const int live_mb = min(MB, max(0, (ti.rows - wm * 64 + 15) / 16));
+  const bool wave_live = live_mb > 0;
   const int l16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
-  auto compute = [&](int buf) {
+  const int q = lane >> 4;                  // 16-byte piece (k 8q .. 8q+7) of the MFMA step
+  int aoff[MB], boff[NBK];
 #pragma unroll
-    for (int kk = 0; kk < kPfBK; kk += 32) {
-      u32x4 bf[4];
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = wm * 64 + mb * 16 + l16;
+    aoff[mb] = r * kDBK + ((q ^ swz(r)) * 8);
+  }
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        bf[cb] = load16(&Bs[buf][(brow[cb] + l16) * kPfLD + kk + kq]);
+  for (int cb = 0; cb < NBK; ++cb) {
+    const int r = brow[cb] + l16;
+    boff[cb] = BM * kDBK + r * kDBK + ((q ^ swz(r)) * 8);
+  }
+
+  f32x4 acc[MB][NBK];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if (mb < live_mb) {
-          const u32x4 af = load16(&As[buf][(wm * 64 + mb * 16 + l16) * kPfLD + kk + kq]);
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[mb][cb] = mfma16x16x32(af, bf[cb], acc[mb][cb]);
-        }
-      }
-    }
+    for (int j = 0; j < NBK; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot) {
+    const uint16_t* st = &ring[slot * STAGE];
+    u32x4 bf[NBK], af[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) af[mb] = load16(st + aoff[mb]);
+#pragma unroll
+    for (int cb = 0; cb < NBK; ++cb) bf[cb] = load16(st + boff[cb]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int cb = 0; cb < NBK; ++cb) acc[mb][cb] = mfma16x16x32(af[mb], bf[cb], acc[mb][cb]);
   };
 
-  load_global(ra0, rb0, 0);
-  load_global(ra1, rb1, 1);
-  store_lds(ra0, rb0, 0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    // step kt: LDS buffer 0 holds tile kt, ra1/rb1 tile kt + 1
-    load_global(ra0, rb0, kt + 2);
-    compute(0);
-    store_lds(ra1, rb1, 1);
-    __syncthreads();
-    // step kt + 1: LDS buffer 1 holds tile kt + 1, ra0/rb0 tile kt + 2
-    load_global(ra1, rb1, kt + 3);
-    compute(1);
-    store_lds(ra0, rb0, 0);
-    __syncthreads();
-  }
-  if (kt < nk) compute(0);  // odd tile count: the last tile sits in buffer 0
-
-  // epilogue: lane holds rows 4 * (lane / 16) + r of each 16-row block, column lane % 16
+  // issue order = step order; step kt is complete once at most (issued after it) * CPW of this
+  // wave's loads are outstanding, and visible to the block after the barrier that follows
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int s = 0; s < kRing - 1; ++s) issue(s);
+  int kt = 0;
+  for (; kt + kRing - 1 < nk; ++kt) {
+    wait_vmcnt<(kRing - 2) * CPW>();
+    block_barrier();                        // slot (kt - 1) % kRing is free in every wave
+    issue(kt + kRing - 1);
+    if (wave_live) compute(kt % kRing);
+  }
+  for (; kt < nk; ++kt) {                   // nothing more to issue; nk - 1 - kt steps behind
+    wait_steps_behind<kRing - 2, CPW>(nk - 1 - kt);
+    block_barrier();
+    if (wave_live) compute(kt % kRing);
+  }
+  wait_vmcnt<0>();                          // prologue re-reads (K < 3 steps) have landed too
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= live_mb) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = wm * 64 + mb * 16 + (lane >> 4) * 4 + r;
@@ -173,18 +225,18 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(
       const int p = ti.row0 + row;
       if (GATEUP) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int f = n0 + wn * 32 + cb * 16 + l16;
+        for (int cb = 0; cb < NBK / 2; ++cb) {
+          const int f = n0 + wn * (WN / 2) + cb * 16 + l16;
           if (f < N) {
-            const float hv = silu(acc[mb][cb][r]) * acc[mb][cb + 2][r];
+            const float hv = silu(acc[mb][cb][r]) * acc[mb][cb + NBK / 2][r];
             h_out[static_cast<long long>(p) * N + f] = f32_to_bf16_bits(hv);
           }
         }
       } else {
         const DownRow dr = down_row(down, sorted_rows[p], p, N);
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int f = n0 + wn * 64 + cb * 16 + l16;
+        for (int cb = 0; cb < NBK; ++cb) {
+          const int f = n0 + wn * WN + cb * 16 + l16;
           if (f < N) down_put(down, dr, f, acc[mb][cb][r]);
         }
       }
@@ -344,23 +396,18 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t
                                                                      rs2, nullptr, down);
     return hipGetLastError();
   }
-  // grouped GEMM over the dispatch order (rs.offsets / rs.sorted_rows); a 1-D grid sized for
-  // the worst-case tile count, rounded up to whole XCD rounds
-  const long long tiles = max_tiles(rows, E, kPfBM);
-  auto grid_for = [&](int ntn) {
-    const long long total = tiles * ntn;
-    return static_cast<unsigned>((total + kXcds - 1) / kXcds * kXcds);
+  // grouped GEMM over the dispatch order; 1-D grid sized for the worst-case tile count
+  auto grid_for = [&](int bm, int feat, int n) {
+    return static_cast<unsigned>(static_cast<long long>(max_tiles(rows, E, bm)) *
+                                 ((n + feat - 1) / feat));
   };
-  const int ntn1 = (H + kPfBN / 2 - 1) / (kPfBN / 2);
-  gemm_prefill_kernel<true><<<grid_for(ntn1), 256, 0, s>>>(x, wg, wu, d, H, E, k, rs.offsets,
-                                                           rs.sorted_rows, h, none);
+  gemm_dma_kernel<true, 256, 128><<<grid_for(256, 64, H), 512, 0, s>>>(
+      x, wg, wu, d, H, E, k, rs.offsets, rs.sorted_rows, h, none);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid_event && (err = record_stage_event(mid_event, s)) != hipSuccess) return err;
-  const int ntn2 = (d + kPfBN - 1) / kPfBN;
-  gemm_prefill_kernel<false><<<grid_for(ntn2), 256, 0, s>>>(h, wd, nullptr, H, d, E, k,
-                                                            rs.offsets, rs.sorted_rows, nullptr,
-                                                            down);
+  gemm_dma_kernel<false, 256, 128><<<grid_for(256, 128, d), 512, 0, s>>>(
+      h, wd, nullptr, H, d, E, k, rs.offsets, rs.sorted_rows, nullptr, down);
   return hipGetLastError();
 }
 
