@@ -9,12 +9,14 @@
 // Selection order is (score descending, expert index ascending); -0.0 == +0.0 under the IEEE
 // comparison, so signed zeros fall through to the index.
 //
-// Work layout: a block owns 16 tokens. Selection runs on 256 threads, 16 lanes per token, each
-// lane scanning every 16th expert; the per-token best is found with xor-shuffles inside the
-// 16-lane group. The bf16 routing kernel first computes the 16 x E logit tile on the matrix cores
-// with 8 waves that split the experts (16 per MFMA tile) and, when there are few experts, the
-// d-long reduction; each wave issues the loads of 8 MFMA steps before using them. Partial tiles
-// are added in a fixed order, so the logits are the same on every call.
+// Work layout: a block owns 16 tokens. Selection runs on 256 threads: the 16 lanes of one DPP row
+// serve one token, lane q holding the scores of experts q, q + 16, ... in registers; each slot's
+// winner, the softmax maximum and the softmax sum are reduced across the row with DPP row
+// rotations (8, 4, 2, 1), after which every lane of the row holds the same value. The bf16
+// routing kernel first computes the 16 x E logit tile on the matrix cores with 16 waves that split
+// the experts (16 per MFMA tile) and, when there are few experts, the d-long reduction, so that
+// each wave issues all of its loads at once; partial tiles are added in a fixed order, so the
+// logits are the same on every call.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,11 +24,13 @@ namespace moe {
 
 namespace {
 
-constexpr int kQ = 16;                      // lanes per token in the selection
+constexpr int kQ = 16;                      // lanes per token in the selection (one DPP row)
+static_assert(kMaxE / 16 <= 16, "at most 16 experts per selection lane");
 constexpr int kTailThreads = kTokTile * kQ; // 256
-constexpr int kFusedWaves = 8;
+constexpr int kFusedWaves = 16;
 constexpr int kFusedThreads = kFusedWaves * kWave;
 constexpr int kBatch = 8;                   // MFMA steps whose loads are issued together
+static_assert(kFusedThreads >= kMaxE, "one thread per expert for the bias preload");
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -47,58 +51,121 @@ __device__ __forceinline__ bool ahead(float s, int e, float bs, int be) {
   return s > bs || (s == bs && e < be);
 }
 
+// Value of lane (i - N) mod 16 of the caller's 16-lane row (DPP row rotation; every lane of the
+// wave must be active).
+template <int N>
+__device__ __forceinline__ int row_ror(int v) {
+  static_assert(N >= 1 && N <= 15, "row rotation");
+  return __builtin_amdgcn_update_dpp(0, v, 0x120 + N, 0xF, 0xF, false);
+}
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(row_ror<N>(__float_as_int(v)));
+}
+
+// (score, expert, raw logit) of the better of this lane's candidate and lane (i - N)'s
+template <int N>
+__device__ __forceinline__ void argmax_step(float& bs, int& be, float& bl) {
+  const float os = row_ror<N>(bs);
+  const int oe = row_ror<N>(be);
+  const float ol = row_ror<N>(bl);
+  const bool take = ahead(os, oe, bs, be);
+  bs = take ? os : bs;
+  be = take ? oe : be;
+  bl = take ? ol : bl;
+}
+// After rotations 8, 4, 2, 1 each lane has combined all 16; lanes i and i + 2^m hold equal values
+// after every step, so the row agrees (also for the floating-point sum).
+__device__ __forceinline__ void row_argmax(float& bs, int& be, float& bl) {
+  argmax_step<8>(bs, be, bl);
+  argmax_step<4>(bs, be, bl);
+  argmax_step<2>(bs, be, bl);
+  argmax_step<1>(bs, be, bl);
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v = v + row_ror<8>(v);
+  v = v + row_ror<4>(v);
+  v = v + row_ror<2>(v);
+  return v + row_ror<1>(v);
+}
+
 // Selection + weights for the token whose logits are `row` (LDS). All kQ lanes of the token's
-// group call this with the same arguments and get the same ids/weights. `sbias` is LDS or NULL.
-// A NaN score is ranked as -inf so that every slot names a valid expert.
+// DPP row call this with the same arguments and get the same ids/weights. `sbias` is LDS or NULL.
+// L >= ceil(E / kQ) bounds the experts per lane; every lane reads its L entries unconditionally
+// (clamped index) so the reads issue together, and a validity mask keeps the clamped copies out.
+// A NaN score is ranked as -inf so that every slot names a valid expert (k <= E).
+template <int L>
 __device__ void select_and_weigh(const float* row, const float* sbias, int E, int k, int scoring,
                                  int q, int* ids, float* w) {
-  uint32_t taken = 0;  // bit i: expert q + kQ*i already chosen
-  const int nloc = (E - q + kQ - 1) / kQ;
+  float lg[L], sc[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) lg[i] = row[min(q + kQ * i, E - 1)];
+  if (sbias) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) sc[i] = sbias[min(q + kQ * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < L; ++i) sc[i] = __fadd_rn(lg[i], sc[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L; ++i) sc[i] = lg[i];
+  }
+  uint32_t avail = 0;  // bit i: expert q + kQ*i exists and is not chosen yet
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool ok = q + kQ * i < E;
+    if (sc[i] != sc[i]) sc[i] = -INFINITY;
+    lg[i] = ok ? lg[i] : -INFINITY;
+    avail |= (ok ? 1u : 0u) << i;
+  }
+  float lw[kMaxK];  // raw logit of each chosen expert
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
+    lw[j] = 0.f;
     if (j < k) {
-      float bs = -INFINITY;
+      float bs = -INFINITY, bl = 0.f;
       int be = 0x7fffffff;
-      for (int i = 0; i < nloc; ++i) {
-        if ((taken >> i) & 1u) continue;
-        const int e = q + kQ * i;
-        float s = row[e];
-        if (sbias) s = __fadd_rn(s, sbias[e]);
-        if (s != s) s = -INFINITY;
-        if (ahead(s, e, bs, be)) { bs = s; be = e; }
-      }
 #pragma unroll
-      for (int m = 1; m < kQ; m <<= 1) {
-        const float os = __shfl_xor(bs, m);
-        const int oe = __shfl_xor(be, m);
-        if (ahead(os, oe, bs, be)) { bs = os; be = oe; }
+      for (int i = 0; i < L; ++i) {
+        const int e = q + kQ * i;
+        const bool take = ((avail >> i) & 1u) && ahead(sc[i], e, bs, be);
+        bs = take ? sc[i] : bs;
+        be = take ? e : be;
+        bl = take ? lg[i] : bl;
       }
+      row_argmax(bs, be, bl);
       ids[j] = be;
-      if ((be % kQ) == q) taken |= 1u << (be / kQ);
+      lw[j] = bl;
+      if (be < E && (be % kQ) == q) avail &= ~(1u << (be / kQ));
     }
   }
   if (scoring == kSoftmax) {
     float m = -INFINITY;
-    for (int i = 0; i < nloc; ++i) m = fmaxf(m, row[q + kQ * i]);
 #pragma unroll
-    for (int o = 1; o < kQ; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    for (int i = 0; i < L; ++i) m = fmaxf(m, lg[i]);
+    m = row_max(m);
     float z = 0.f;
-    for (int i = 0; i < nloc; ++i) z += expf(row[q + kQ * i] - m);
 #pragma unroll
-    for (int o = 1; o < kQ; o <<= 1) z += __shfl_xor(z, o);
+    for (int i = 0; i < L; ++i) z += (q + kQ * i < E) ? expf(lg[i] - m) : 0.f;
+    z = row_sum(z);
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < k) w[j] = expf(row[ids[j]] - m) / z;
+      if (j < k) w[j] = expf(lw[j] - m) / z;
   } else {
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < k) m = fmaxf(m, row[ids[j]]);
+      if (j < k) m = fmaxf(m, lw[j]);
     float z = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        w[j] = expf(row[ids[j]] - m);
+        w[j] = expf(lw[j] - m);
         z += w[j];
       }
     }
@@ -110,6 +177,7 @@ __device__ void select_and_weigh(const float* row, const float* sbias, int E, in
 
 // Selection on the LDS logit tile of the block's 16 tokens, then the outputs. Called by every
 // thread of the block (barriers inside); threads >= 256 only help with the epilogue loops.
+template <int L>
 __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0, int T, int E,
                            int k, int scoring, const RouteOut& o, int* hist) {
   const int tl = threadIdx.x / kQ;
@@ -118,7 +186,7 @@ __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0
   if (threadIdx.x < kTailThreads) {  // whole waves
     int ids[kMaxK];
     float w[kMaxK];
-    select_and_weigh(tile + tl * ld, sbias, E, k, scoring, q, ids, w);
+    select_and_weigh<L>(tile + tl * ld, sbias, E, k, scoring, q, ids, w);
     if (t < T && q == 0) {
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) {
@@ -145,6 +213,7 @@ __device__ void route_tail(const float* tile, int ld, const float* sbias, int t0
   }
 }
 
+template <int L>
 __global__ __launch_bounds__(kTailThreads) void route_from_logits_kernel(
     const float* __restrict__ logits, const float* __restrict__ sel_bias, int T, int E, int k,
     int scoring, RouteOut o) {
@@ -164,19 +233,21 @@ __global__ __launch_bounds__(kTailThreads) void route_from_logits_kernel(
     hist[e] = 0;
   }
   __syncthreads();
-  route_tail(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
+  route_tail<L>(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
 }
 
-// How the 8 waves of the fused kernel split the logit tile: `neb` 16-expert column blocks, each
-// reduced over `ksplit` slices of d (a power of two, neb * ksplit <= 8 when neb < 8).
-__host__ __device__ inline int route_ksplit(int E) {
+// How the waves of the fused kernel split the logit tile: `neb` 16-expert column blocks, each
+// reduced over `ksplit` slices of d (a power of two, neb * ksplit <= kFusedWaves when
+// neb < kFusedWaves; every slice a whole number of 8-element loads).
+__host__ __device__ inline int route_ksplit(int E, int d) {
   const int neb = (E + 15) / 16;
   if (neb >= kFusedWaves) return 1;
   int ks = 1;
-  while (ks * 2 * neb <= kFusedWaves) ks *= 2;
+  while (ks * 2 * neb <= kFusedWaves && d % (16 * ks) == 0) ks *= 2;
   return ks;
 }
 
+template <int L>
 __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ rb,
     const float* __restrict__ sel_bias, int T, int d, int E, int k, int scoring,
@@ -184,10 +255,11 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
   extern __shared__ float smem[];
   const int ld = E + 1;
   const int neb = (E + 15) / 16;
-  const int ksplit = route_ksplit(E);
+  const int ksplit = route_ksplit(E, d);
   float* part = smem;                                  // [ksplit][16][E+1]; part[0] = tile
   float* sbias = part + ksplit * kTokTile * ld;        // [E]
-  int* hist = reinterpret_cast<int*>(sbias + E);       // [E]
+  float* srb = sbias + E;                              // [E]
+  int* hist = reinterpret_cast<int*>(srb + E);         // [E]
   const int t0 = blockIdx.x * kTokTile;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -198,10 +270,11 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
   const uint16_t* xrow = x + static_cast<long long>(min(t, T - 1)) * d;
   const int kslice = d / ksplit;  // a multiple of 8 (d % 64 == 0, ksplit <= 8)
 
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    if (sel_bias) sbias[e] = sel_bias[e];
-    hist[e] = 0;
-  }
+  // the per-expert vectors are loaded now and stored to LDS after the products, so their latency
+  // hides behind the tile loads
+  const int ex = threadIdx.x;
+  const float sb_v = (sel_bias && ex < E) ? sel_bias[ex] : 0.f;
+  const float rb_v = (rb && ex < E) ? rb[ex] : 0.f;
 
   for (int task = wave; task < neb * ksplit; task += kFusedWaves) {
     const int eb = task % neb;
@@ -230,13 +303,18 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
       for (int r = 0; r < 4; ++r) dst[((lane >> 4) * 4 + r) * ld + e] = acc[r];
     }
   }
+  if (ex < E) {
+    sbias[ex] = sb_v;
+    srb[ex] = rb_v;
+    hist[ex] = 0;
+  }
   __syncthreads();
   // fixed-order sum of the d slices, then the router bias (one more fp32 rounding)
   for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
     const int tl = i / E, e = i % E;
     float v = part[tl * ld + e];
     for (int ks = 1; ks < ksplit; ++ks) v += part[(ks * kTokTile + tl) * ld + e];
-    if (rb) v = v + rb[e];
+    if (rb) v = v + srb[e];
     part[tl * ld + e] = v;
   }
   __syncthreads();
@@ -247,7 +325,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
     }
   }
   if (o.ids == nullptr) return;  // logits only (uniform across the block)
-  route_tail(part, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
+  route_tail<L>(part, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
 }
 
 // fp32 router logits: one thread per (token, expert), four interleaved partial sums.
@@ -272,13 +350,30 @@ __global__ void logits_f32_kernel(const float* __restrict__ x, const float* __re
   logits[i] = s;
 }
 
+// Experts per selection lane, rounded up to a power of two (the template bound of the selection).
+int lane_experts(int E) {
+  const int need = (E + kQ - 1) / kQ;
+  int L = 1;
+  while (L < need) L *= 2;
+  return L;
+}
+
+#define MOE_ROUTE_DISPATCH_L(E, LAUNCH) \
+  switch (lane_experts(E)) {            \
+    case 1: LAUNCH(1); break;           \
+    case 2: LAUNCH(2); break;           \
+    case 4: LAUNCH(4); break;           \
+    case 8: LAUNCH(8); break;           \
+    default: LAUNCH(16); break;         \
+  }
+
 size_t tail_smem(int E) {
   return sizeof(float) * (static_cast<size_t>(kTokTile) * (E + 1) + E) +
          sizeof(int) * E;
 }
 
-size_t fused_smem(int E) {
-  return sizeof(float) * (static_cast<size_t>(route_ksplit(E)) * kTokTile * (E + 1) + E) +
+size_t fused_smem(int E, int d) {
+  return sizeof(float) * (static_cast<size_t>(route_ksplit(E, d)) * kTokTile * (E + 1) + 2 * E) +
          sizeof(int) * E;
 }
 
@@ -312,8 +407,11 @@ hipError_t launch_route_from_logits(const float* logits, const float* sel_bias, 
     hipError_t err = launch_zero_i32(o.counts, E, s);
     if (err != hipSuccess) return err;
   }
-  route_from_logits_kernel<<<blocks, kTailThreads, tail_smem(E), s>>>(logits, sel_bias, T, E, k,
-                                                                      scoring, o);
+#define MOE_LAUNCH_TAIL(L)                                                                  \
+  route_from_logits_kernel<L><<<blocks, kTailThreads, tail_smem(E), s>>>(logits, sel_bias, T, E, \
+                                                                         k, scoring, o)
+  MOE_ROUTE_DISPATCH_L(E, MOE_LAUNCH_TAIL)
+#undef MOE_LAUNCH_TAIL
   return hipGetLastError();
 }
 
@@ -325,9 +423,11 @@ hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const 
     hipError_t err = launch_zero_i32(o.counts, E, s);
     if (err != hipSuccess) return err;
   }
-  route_fused_bf16_kernel<<<blocks, kFusedThreads, fused_smem(E), s>>>(x, wr, rb, sel_bias, T, d,
-                                                                       E, k, scoring, logits_out,
-                                                                       o);
+#define MOE_LAUNCH_FUSED(L)                                                                \
+  route_fused_bf16_kernel<L><<<blocks, kFusedThreads, fused_smem(E, d), s>>>(              \
+      x, wr, rb, sel_bias, T, d, E, k, scoring, logits_out, o)
+  MOE_ROUTE_DISPATCH_L(E, MOE_LAUNCH_FUSED)
+#undef MOE_LAUNCH_FUSED
   return hipGetLastError();
 }
 
