@@ -7,10 +7,16 @@ HBM before timing. The default workload is the ZONOS2-shaped decode step (T=64 t
 
 Cold weights: the layer's expert weights are kept in several identical copies and consecutive
 steps rotate through them, so that no step finds its weights in the 256 MB Infinity Cache left
-over from the step before (the copies together exceed 1.5 GB). The steps are replayed from a HIP
-graph (the decode loop of the pages replays a captured graph) holding one step per copy, with
-a HIP event at every stage boundary; the per-stage durations come from those events, recorded
-on the stream the kernels run on, over the same timed region.
+over from the step before (the copies together exceed 1.5 GB). The timed steps are replayed from
+a HIP graph (the decode loop of the pages replays a captured graph) holding one step per copy;
+`value` and `ms_per_step` come from the wall clock around them, bracketed by synchronizations.
+
+Stage durations come from a second pass over the same steps, on the same stream, with the
+layer's profiling events (moe_layer_args.prof_events): a graph with event nodes when the runtime
+times those, else eager launches. In that pass the gate/up kernel, the roofline's dominant
+kernel, is launched with its own start/stop events (hipExtLaunchKernelGGL), so its duration is the
+kernel's alone; "dispatch" is the time from the end of routing to the start of that kernel (the
+dispatch kernel on the grouped-GEMM path, plus launch gaps).
 
 Prints one JSON line (see the `result` dict at the end of main()).
 """

@@ -379,17 +379,15 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
 hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                            const uint16_t* wd, int T, int d, int E, int H, int k,
                            const RowSource& rs, uint16_t* h, const DownArgs& down, hipStream_t s,
-                           void* mid_event) {
+                           const StageMarks& gu) {
   const int rows = T * k;
   if (rows <= 0) return hipSuccess;
   DownArgs none{};
   hipError_t err;
   if (ffn_bf16_streaming(T, d, E, H, k)) {
-    ffn_stream_kernel<true><<<dim3(H / kStFeat, E), kWave, 0, s>>>(x, wg, wu, d, H, k, rs, h,
-                                                                    none);
-    err = hipGetLastError();
+    err = launch_marked(ffn_stream_kernel<true>, dim3(H / kStFeat, E), dim3(kWave), s, gu, x, wg,
+                        wu, d, H, k, rs, h, none);
     if (err != hipSuccess) return err;
-    if (mid_event && (err = record_stage_event(mid_event, s)) != hipSuccess) return err;
     RowSource rs2 = rs;
     rs2.counts_out = nullptr;
     ffn_stream_kernel<false><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
@@ -401,11 +399,9 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t
     return static_cast<unsigned>(static_cast<long long>(max_tiles(rows, E, bm)) *
                                  ((n + feat - 1) / feat));
   };
-  gemm_dma_kernel<true, 256, 128><<<grid_for(256, 64, H), 512, 0, s>>>(
-      x, wg, wu, d, H, E, k, rs.offsets, rs.sorted_rows, h, none);
-  err = hipGetLastError();
+  err = launch_marked(gemm_dma_kernel<true, 256, 128>, dim3(grid_for(256, 64, H)), dim3(512), s,
+                      gu, x, wg, wu, d, H, E, k, rs.offsets, rs.sorted_rows, h, none);
   if (err != hipSuccess) return err;
-  if (mid_event && (err = record_stage_event(mid_event, s)) != hipSuccess) return err;
   gemm_dma_kernel<false, 256, 128><<<grid_for(256, 128, d), 512, 0, s>>>(
       h, wd, nullptr, H, d, E, k, rs.offsets, rs.sorted_rows, nullptr, down);
   return hipGetLastError();

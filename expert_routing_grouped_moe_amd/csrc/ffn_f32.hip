@@ -114,19 +114,15 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
 hipError_t launch_ffn_f32(const float* x, const float* wg, const float* wu, const float* wd,
                           int T, int d, int E, int H, int k, const int32_t* offsets,
                           const int32_t* sorted_rows, float* h, const DownArgs& down,
-                          hipStream_t s, void* mid_event) {
+                          hipStream_t s, const StageMarks& gu) {
   const int rows = T * k;
   const int tiles = max_tiles(rows, E, kBM);
   if (tiles == 0) return hipSuccess;
   DownArgs none{};
   dim3 g1((H + kBN - 1) / kBN, tiles);
-  ffn_f32_kernel<true><<<g1, 256, 0, s>>>(x, wg, wu, d, H, E, k, offsets, sorted_rows, h, none);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_marked(ffn_f32_kernel<true>, g1, dim3(256), s, gu, x, wg, wu, d, H, E,
+                                 k, offsets, sorted_rows, h, none);
   if (err != hipSuccess) return err;
-  if (mid_event) {
-    err = record_stage_event(mid_event, s);
-    if (err != hipSuccess) return err;
-  }
   dim3 g2((d + kBN - 1) / kBN, tiles);
   ffn_f32_kernel<false><<<g2, 256, 0, s>>>(h, wd, nullptr, H, d, E, k, offsets, sorted_rows,
                                            nullptr, down);

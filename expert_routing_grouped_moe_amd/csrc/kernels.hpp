@@ -2,6 +2,7 @@
 // hipGetLastError() of its launches. Arguments are validated by the C-ABI layer before these run.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,6 +38,33 @@ struct RouteOut {
 // Stage marker for the optional timing events: an external event node while `s` is being
 // captured into a graph, a plain event record otherwise (defined in moe_api.hip).
 hipError_t record_stage_event(void* ev, hipStream_t s);
+// True while `s` is being captured into a graph (defined in moe_api.hip).
+bool stream_capturing(hipStream_t s);
+
+// Optional timing events around one kernel (hipEvent_t handles, or NULL).
+struct StageMarks {
+  void* start;
+  void* end;
+};
+
+// Launches `kernel` on `s`. With both marks set and `s` not being captured, the launch goes
+// through hipExtLaunchKernelGGL so that the two events take the kernel's own start and end times;
+// otherwise the marks that are set are recorded before and after the launch.
+template <typename... Params, typename... Args>
+hipError_t launch_marked(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                         const StageMarks& m, Args... args) {
+  hipError_t err;
+  if (m.start && m.end && !stream_capturing(s)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<hipEvent_t>(m.start),
+                          static_cast<hipEvent_t>(m.end), 0, args...);
+    return hipGetLastError();
+  }
+  if (m.start && (err = record_stage_event(m.start, s)) != hipSuccess) return err;
+  kernel<<<grid, block, 0, s>>>(args...);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (m.end && (err = record_stage_event(m.end, s)) != hipSuccess) return err;
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------- routing (route.hip)
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
@@ -79,16 +107,15 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k);
 // Largest T*k the by-ids row scan supports.
 constexpr int kMaxScanRows = 2048;
 
-// h is the [T*k, H] intermediate (bf16 bits or fp32). `mid_event` (a hipEvent_t or NULL) is
-// recorded on `s` between the gate/up and the down launches.
+// h is the [T*k, H] intermediate (bf16 bits or fp32). `gu` marks the gate/up launch (timing).
 hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                            const uint16_t* wd, int T, int d, int E, int H, int k,
                            const RowSource& rs, uint16_t* h, const DownArgs& down, hipStream_t s,
-                           void* mid_event);
+                           const StageMarks& gu);
 hipError_t launch_ffn_f32(const float* x, const float* wg, const float* wu, const float* wd,
                           int T, int d, int E, int H, int k, const int32_t* offsets,
                           const int32_t* sorted_rows, float* h, const DownArgs& down,
-                          hipStream_t s, void* mid_event);
+                          hipStream_t s, const StageMarks& gu);
 
 // ---------------------------------------------------------------- combine (combine.hip)
 // row_pos == NULL: expert_out is indexed by the assignment row itself.

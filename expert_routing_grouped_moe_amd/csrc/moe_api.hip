@@ -95,6 +95,10 @@ hipError_t record_event(void* ev, hipStream_t s) {
 
 namespace moe {
 hipError_t record_stage_event(void* ev, hipStream_t s) { return record_event(ev, s); }
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
 }  // namespace moe
 
 extern "C" {
@@ -193,12 +197,12 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
     return hip_status(moe::launch_ffn_bf16(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
         static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), T, d, E, H, k,
-        rs, at<uint16_t>(ws, lay.h), down, s, nullptr));
+        rs, at<uint16_t>(ws, lay.h), down, s, moe::StageMarks{}));
   }
   return hip_status(moe::launch_ffn_f32(
       static_cast<const float*>(x), static_cast<const float*>(w_gate),
       static_cast<const float*>(w_up), static_cast<const float*>(w_down), T, d, E, H, k,
-      expert_offsets, sorted_rows, at<float>(ws, lay.h), down, s, nullptr));
+      expert_offsets, sorted_rows, at<float>(ws, lay.h), down, s, moe::StageMarks{}));
 }
 
 int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
@@ -280,20 +284,20 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   MOE_TRY(mark(1));
   if (!streaming)
     MOE_TRY(moe::launch_dispatch(ids, T * k, E, offsets, sorted_rows, row_pos, counts, s));
-  MOE_TRY(mark(2));
-  void* mid = ev ? ev[3] : nullptr;
+  // [2], [3]: the gate/up kernel's own start and end (see moe_layer_args.prof_events)
+  const moe::StageMarks gu{ev ? ev[2] : nullptr, ev ? ev[3] : nullptr};
   if (dtype == MOE_BF16) {
     const RowSource rs = streaming ? RowSource{ids, T * k, nullptr, nullptr, counts}
                                    : RowSource{nullptr, T * k, offsets, sorted_rows, nullptr};
     MOE_TRY(moe::launch_ffn_bf16(
         static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_gate),
         static_cast<const uint16_t*>(a->w_up), static_cast<const uint16_t*>(a->w_down), T, d, E,
-        H, k, rs, at<uint16_t>(ws, lay.h), down, s, mid));
+        H, k, rs, at<uint16_t>(ws, lay.h), down, s, gu));
   } else {
     MOE_TRY(moe::launch_ffn_f32(
         static_cast<const float*>(a->x), static_cast<const float*>(a->w_gate),
         static_cast<const float*>(a->w_up), static_cast<const float*>(a->w_down), T, d, E, H, k,
-        offsets, sorted_rows, at<float>(ws, lay.h), down, s, mid));
+        offsets, sorted_rows, at<float>(ws, lay.h), down, s, gu));
   }
   // staged expert outputs (by assignment row on the streaming path, in dispatch order
   // otherwise) are combined in slot order

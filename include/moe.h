@@ -186,11 +186,12 @@ typedef struct moe_layer_args {
   float* topk_w;             /* [T, k]                                                    */
   int32_t* expert_counts;    /* [E]                                                       */
   /* Optional stage timing (NULL = none): an array of MOE_PROF_EVENTS hipEvent_t handles passed
-     as void*. an event record of prof_events[i] is enqueued at each stage boundary
-     (an external event node, hipEventRecordExternal, while the stream is being captured):
-     [0] before routing, [1] after routing (logits, top-k, weights), [2] after dispatch,
-     [3] after gate/up + SwiGLU, [4] after down projection and combine. The events are owned by
-     the caller. */
+     as void*, owned by the caller. [0] before routing, [1] after routing (logits, top-k,
+     weights), [2] start and [3] end of the gate/up + SwiGLU kernel, [4] after the down projection
+     and combine. Outside graph capture [2] and [3] are taken by the gate/up launch itself
+     (hipExtLaunchKernelGGL start/stop events), so [2] -> [3] is that kernel's duration; the
+     others, and all five while the stream is being captured, are event records enqueued at the
+     stage boundary (external event nodes, hipEventRecordExternal, during capture). */
   void* const* prof_events;
 } moe_layer_args;
 
