@@ -8,7 +8,7 @@
 
 namespace moe {
 
-enum Scoring { kSoftmax = 0, kSelectedSoftmax = 1 };
+enum Scoring { kSoftmax = 0, kSelectedSoftmax = 1, kSigmoid = 2 };
 
 constexpr int kTokTile = 16;  // tokens per routing block; also the dispatch block of rows
 

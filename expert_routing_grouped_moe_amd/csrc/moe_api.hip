@@ -36,8 +36,11 @@ int check_route_dims(int T, int E, int k) {
 }
 
 int check_scoring(int scoring, const float* sel_bias) {
-  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SELECTED_SOFTMAX) return MOE_ERR_UNSUPPORTED;
-  if (scoring == MOE_SCORING_SOFTMAX && sel_bias != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SELECTED_SOFTMAX &&
+      scoring != MOE_SCORING_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  // a selection bias is defined for SELECTED_SOFTMAX only
+  if (scoring != MOE_SCORING_SELECTED_SOFTMAX && sel_bias != nullptr) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -6,6 +6,9 @@
 //                     (no renormalisation over the chosen set)
 //   SELECTED_SOFTMAX  rank by fp32(logit + sel_bias), weight = softmax over the k chosen raw
 //                     logits
+//   SIGMOID           rank by logit, weight = sigmoid(logit) of the chosen expert, no
+//                     renormalisation (audio.cpp PR #1271, "Framework change": the pre-ranking
+//                     sigmoid mode)
 // Selection order is (score descending, expert index ascending); -0.0 == +0.0 under the IEEE
 // comparison, so signed zeros fall through to the index.
 //
@@ -156,6 +159,10 @@ __device__ void select_and_weigh(const float* row, const float* sbias, int E, in
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
       if (j < k) w[j] = expf(lw[j] - m) / z;
+  } else if (scoring == kSigmoid) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) w[j] = 1.f / (1.f + expf(-lw[j]));
   } else {
     float m = -INFINITY;
 #pragma unroll

@@ -65,6 +65,10 @@ WORKLOADS = {
     "zonos2-skewed-prefill": Workload("zonos2-skewed-prefill", T=8192, d=2048, E=16, k=1, H=2816,
                                       scoring=SOFTMAX, dtype="bf16", seed=4,
                                       skew_hot_share=0.40, skew_dead=(14, 15), shape="prefill"),
+    # ZONOS2's one top-2 layer (zonos2.cpp INTERNALS, "Model architecture" table, MoE row: top-2
+    # only on layer 26), prob-weighted with no renormalisation: the SOFTMAX mode at k = 2
+    "zonos2-layer26-decode": Workload("zonos2-layer26-decode", T=64, d=2048, E=16, k=2, H=2816,
+                                      scoring=SOFTMAX, dtype="bf16", seed=5, shape="decode"),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

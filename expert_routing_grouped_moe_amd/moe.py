@@ -27,8 +27,10 @@ MOE_BF16 = 1
 
 MOE_SCORING_SOFTMAX = 0
 MOE_SCORING_SELECTED_SOFTMAX = 1
+MOE_SCORING_SIGMOID = 2
 
-SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELECTED_SOFTMAX}
+SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELECTED_SOFTMAX,
+           "sigmoid": MOE_SCORING_SIGMOID}
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
   MOE_OK = 0,
@@ -74,7 +74,13 @@ enum moe_scoring {
   /* ZONOS3-Mini (audio.cpp PR #1271, "Framework change"): rank by fp32(logit + sel_bias[e])
      (one round-to-nearest-even add), take the top k, weight them by the softmax of their raw
      logits over the k selected experts only (weights sum to 1; k = 1 gives exactly 1). */
-  MOE_SCORING_SELECTED_SOFTMAX = 1
+  MOE_SCORING_SELECTED_SOFTMAX = 1,
+  /* Sigmoid scoring, the other pre-ranking mode that audio.cpp's MoE routing already has (audio.cpp
+     PR #1271, "Framework change": the existing modes apply softmax or sigmoid before ranking):
+     rank by logit (the order of sigmoid(logit) in exact arithmetic; fp32 sigmoid saturates to 1
+     and would create ties), weight each chosen expert by sigmoid(logit) = 1 / (1 + exp(-logit)),
+     no renormalisation (the weights need not sum to 1). sel_bias must be NULL. Added in ABI 2. */
+  MOE_SCORING_SIGMOID = 2
 };
 
 /* Returns MOE_ABI_VERSION of the built library. */

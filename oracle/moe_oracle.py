@@ -15,6 +15,9 @@ What the layer computes (one token t, E experts, k of them selected):
                      SELECTED_SOFTMAX (ZONOS3-Mini): rank by raw logit plus selection bias, then
                      softmax over the selected experts' logits only; the bias does not enter the
                      weights (audio.cpp PR #1271, "Framework change", MoeScoring::SelectedSoftmax).
+                     SIGMOID: rank by logit, weight each selected expert by sigmoid(logit), no
+                     renormalisation (same page and section: the pre-ranking sigmoid mode; ranking
+                     on the logit is ranking on sigmoid(logit) in exact arithmetic).
   5. dispatch        counts, exclusive-scan offsets, assignment rows r = t*k + j grouped by
                      expert in ascending r, and the inverse position of every row
   6. expert FFN      SwiGLU: o = Wd[e] (silu(Wg[e] x) * (Wu[e] x)), silu(z) = z / (1 + e^-z)
@@ -43,6 +46,7 @@ f64 = np.float64
 
 SOFTMAX = "softmax"
 SELECTED_SOFTMAX = "selected_softmax"
+SIGMOID = "sigmoid"
 
 
 # ----------------------------------------------------------------------------- routing (steps 1-4)
@@ -91,6 +95,9 @@ def routing_weights_ref(logits, ids, scoring):
             m = sel.max(axis=1, keepdims=True)
             q = np.exp(sel - m)
             return q / q.sum(axis=1, keepdims=True)
+        if scoring == SIGMOID:
+            sel = np.take_along_axis(L, ids, axis=1)
+            return 1.0 / (1.0 + np.exp(-sel))
     raise ValueError(f"unknown scoring {scoring}")
 
 
@@ -103,7 +110,7 @@ def expert_counts_ref(ids, E):
 
 def route_ref(logits32, sel_bias, k, scoring):
     """The routing call on given fp32 logits: ids [T,k], fp64 weights [T,k], counts [E]."""
-    if scoring == SOFTMAX and sel_bias is not None:
+    if scoring != SELECTED_SOFTMAX and sel_bias is not None:
         raise ValueError("a selection bias is only defined for SelectedSoftmax")
     s = rank_scores_fp32(logits32, sel_bias)
     ids = select_topk_ref(s, k)
@@ -184,7 +191,7 @@ def layer_ref(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None, s
               selection=None):
     """Steps 1-7 in fp64. ``selection`` ([T,k] expert ids) replaces step 3 when given: it is how a
     near-tied token is re-evaluated at the choice another implementation made."""
-    if scoring == SOFTMAX and sel_bias is not None:
+    if scoring != SELECTED_SOFTMAX and sel_bias is not None:
         raise ValueError("a selection bias is only defined for SelectedSoftmax")
     E = np.asarray(w_router).shape[0]
     L = router_logits_ref(x, w_router, router_bias)
@@ -227,6 +234,10 @@ def dense_bruteforce_ref(x, w_router, w_gate, w_up, w_down, k, scoring, router_b
             m = max(L)
             z = sum(math.exp(v - m) for v in L)
             wt = {e: math.exp(L[e] - m) / z for e in chosen}
+        elif scoring == SIGMOID:
+            # sigmoid(v) written without overflow either side: e^v / (1 + e^v) for v < 0
+            wt = {e: (1.0 / (1.0 + math.exp(-L[e])) if L[e] >= 0
+                      else math.exp(L[e]) / (1.0 + math.exp(L[e]))) for e in chosen}
         else:
             m = max(L[e] for e in chosen)
             z = sum(math.exp(L[e] - m) for e in chosen)

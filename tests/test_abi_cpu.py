@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5):
         assert moe.moe_status_string(st) and moe.moe_status_string(st) != "unknown status"
     assert moe.moe_status_string(7) == "unknown status"
@@ -125,6 +125,8 @@ def test_layer_forward_validation():
     assert run(_args(T=0)) == moe.MOE_OK
     assert run(_args(k=3, E=2)) == moe.MOE_ERR_SHAPE
     assert run(_args(scoring=4)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(scoring=3)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(scoring=2, sel_bias=FAKE.value)) == moe.MOE_ERR_UNSUPPORTED  # sigmoid: no bias
     assert run(_args(sel_bias=FAKE.value)) == moe.MOE_ERR_UNSUPPORTED
     assert run(_args(x=None)) == moe.MOE_ERR_NULL
     assert run(_args(y=MISALIGNED.value)) == moe.MOE_ERR_SHAPE

@@ -63,6 +63,10 @@ EDGE = [
     ("stream-E256-k8", 64, 256, 256, 8, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
     ("stream-hot-expert", 200, 128, 16, 1, 128, orc.SOFTMAX, "bf16", None, "hot5"),
     ("stream-max-rows", 1024, 128, 64, 2, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    # sigmoid scoring on the three expert-kernel families
+    ("sigmoid-stream", 64, 512, 16, 2, 512, orc.SIGMOID, "bf16", None, None),
+    ("sigmoid-prefill", 700, 256, 8, 2, 256, orc.SIGMOID, "bf16", None, None),
+    ("sigmoid-f32", 48, 64, 8, 3, 128, orc.SIGMOID, "f32", None, None),
 ]
 
 

@@ -31,7 +31,7 @@ def _check(L32, k, scoring, sel_bias=None):
 @pytest.mark.parametrize("kind", ["normal", "ties", "equal", "signed_zero", "neg_inf"])
 @pytest.mark.parametrize("E,k", [(1, 1), (8, 1), (8, 8), (16, 1), (16, 2), (64, 2), (64, 8),
                                  (256, 1), (256, 8), (5, 3), (100, 4)])
-@pytest.mark.parametrize("scoring", [orc.SOFTMAX, orc.SELECTED_SOFTMAX])
+@pytest.mark.parametrize("scoring", [orc.SOFTMAX, orc.SELECTED_SOFTMAX, orc.SIGMOID])
 def test_route_bit_exact(kind, E, k, scoring):
     T = 197
     L = gen.make_logits(T, E, seed=1000 + E * 10 + k, kind=kind)
@@ -52,6 +52,18 @@ def test_route_token_counts(T):
     sb = np.random.default_rng(3).standard_normal(64).astype(np.float32)
     _check(L, 2, orc.SELECTED_SOFTMAX, sb)
     _check(L[:, :16].copy(), 1, orc.SOFTMAX)
+    _check(L[:, :16].copy(), 2, orc.SIGMOID)
+
+
+def test_route_sigmoid_saturation():
+    # fp32 sigmoid is 1.0 for every logit above ~17; the ranking still follows the logits
+    L = np.array([[20.0, 30.0, 25.0, -40.0, 0.0]], dtype=np.float32)
+    ids, w, _ = _route_gpu(L, 3, orc.SIGMOID)
+    assert ids[0].tolist() == [1, 2, 0]
+    assert (w[0] == 1.0).all()
+    ids, w, _ = _route_gpu(L, 5, orc.SIGMOID)
+    assert ids[0].tolist() == [1, 2, 0, 4, 3]
+    assert w[0, 3] == 0.5 and 0.0 <= w[0, 4] < 1e-17
 
 
 def test_route_rounding_of_bias_add():

@@ -57,6 +57,16 @@ def test_hand_selected_softmax(hand):
         np.testing.assert_allclose(w[0], [_ev(v) for v in case["w"]], rtol=0, atol=1e-7)
 
 
+def test_hand_sigmoid_no_renorm(hand):
+    c = hand["sigmoid_no_renorm"]
+    L = _arr(c["logits"])[None, :].astype(np.float32)
+    for case in c["cases"]:
+        ids, w, counts = orc.route_ref(L, None, case["k"], orc.SIGMOID)
+        assert ids[0].tolist() == case["ids"]
+        np.testing.assert_allclose(w[0], [_ev(v) for v in case["w"]], rtol=0, atol=1e-7)
+        assert counts.sum() == case["k"]
+
+
 def test_hand_fp32_rank_add(hand):
     c = hand["fp32_rank_add"]
     L32 = _arr(c["logits"])[None, :].astype(np.float32)
@@ -164,6 +174,28 @@ def test_selected_softmax_weight_invariants():
         np.testing.assert_array_equal(w, w_nobias)
 
 
+def test_sigmoid_weight_invariants():
+    rng = np.random.default_rng(10)
+    for E in (1, 2, 16, 64):
+        L = rng.standard_normal((32, E)).astype(np.float32) * 4
+        for k in range(1, min(E, 8) + 1):
+            ids, w, _ = orc.route_ref(L, None, k, orc.SIGMOID)
+            assert ((w > 0) & (w < 1)).all()
+            assert (np.diff(w, axis=1) <= 0).all()          # slot order = weight order
+            # sigmoid(-z) = 1 - sigmoid(z): the lowest logits of -L are the highest of L
+            ids_n, w_n, _ = orc.route_ref(-L, None, E, orc.SIGMOID)
+            w_all = orc.routing_weights_ref(L, ids_n, orc.SIGMOID)
+            np.testing.assert_allclose(w_n + w_all, 1.0, rtol=0, atol=1e-15)
+    # two experts, the second at logit 0: the top-1 sigmoid weight is the top-1 softmax probability
+    a = rng.standard_normal(64).astype(np.float32) * 3
+    L = np.stack([np.abs(a), np.zeros(64, np.float32)], axis=1)
+    _, ws, _ = orc.route_ref(L, None, 1, orc.SIGMOID)
+    _, wp, _ = orc.route_ref(L, None, 1, orc.SOFTMAX)
+    np.testing.assert_allclose(ws, wp, rtol=1e-14)
+    with pytest.raises(ValueError):
+        orc.route_ref(L, np.zeros(2, np.float32), 1, orc.SIGMOID)
+
+
 def test_mode_equivalence_k_equals_E():
     rng = np.random.default_rng(9)
     L = rng.standard_normal((16, 8)).astype(np.float32)
@@ -245,7 +277,9 @@ def test_zero_up_gives_zero_and_linear_in_down():
 @pytest.mark.parametrize("scoring,k,rb,sb", [(orc.SOFTMAX, 1, False, False), (orc.SOFTMAX, 2, True, False),
                                              (orc.SELECTED_SOFTMAX, 2, False, True),
                                              (orc.SELECTED_SOFTMAX, 3, True, True),
-                                             (orc.SOFTMAX, 8, False, False)])
+                                             (orc.SOFTMAX, 8, False, False),
+                                             (orc.SIGMOID, 2, True, False),
+                                             (orc.SIGMOID, 5, False, False)])
 def test_layer_equals_dense_bruteforce(scoring, k, rb, sb):
     inp = _case(T=24, d=32, E=8, k=k, H=40, scoring=scoring, seed=20 + k, with_rb=rb, with_sb=sb)
     y = _layer(inp)["y"]
@@ -334,12 +368,14 @@ def _pins_pass():
             hand = json.load(f)
         test_hand_softmax_no_renorm(hand)
         test_hand_selected_softmax(hand)
+        test_hand_sigmoid_no_renorm(hand)
         test_hand_fp32_rank_add(hand)
         test_hand_swiglu_layer(hand, "swiglu_one_expert")
         test_hand_swiglu_layer(hand, "swiglu_two_experts_top1")
         test_select_matches_python_sort("ties", 16, 2)
         test_softmax_weight_invariants()
         test_selected_softmax_weight_invariants()
+        test_sigmoid_weight_invariants()
         test_permute_invariants(64, 64, 2)
         test_layer_equals_dense_bruteforce(orc.SELECTED_SOFTMAX, 2, False, True)
         test_single_expert_is_dense_swiglu_torch()
@@ -369,6 +405,13 @@ MUTATIONS = {
     # combine reads the wrong row of the grouped output
     "combine_sorted": ("combine_ref", lambda orig: (lambda eo, row_pos, w, k: orig(
         eo, np.arange(len(row_pos)), w, k))),
+    # sigmoid with a sign slip: 1 / (1 + e^z)
+    "sigmoid_sign": ("routing_weights_ref", lambda orig: (lambda L, ids, scoring: (
+        1.0 - orig(L, ids, scoring) if scoring == orc.SIGMOID else orig(L, ids, scoring)))),
+    # sigmoid weights renormalised over the selected experts
+    "sigmoid_renorm": ("routing_weights_ref", lambda orig: (lambda L, ids, scoring: (
+        (lambda w: w / w.sum(axis=1, keepdims=True))(orig(L, ids, scoring))
+        if scoring == orc.SIGMOID else orig(L, ids, scoring)))),
     # rank on the fp64 sum instead of the binary32 add
     "rank_fp64": ("rank_scores_fp32", lambda orig: (lambda L, b=None: np.asarray(L, np.float64) + (
         0 if b is None else np.asarray(b, np.float64)[None, :]))),
