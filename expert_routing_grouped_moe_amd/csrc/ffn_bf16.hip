@@ -264,17 +264,18 @@ __device__ int scan_rows(const int32_t* __restrict__ ids, int n, int e, int* lr)
   return total;
 }
 
-// One group of up to 16 rows (entries m0 .. of the expert's row list) against this wave's 16
-// features over the whole reduction length K, with no barrier and no LDS staging:
+// Up to NG groups of 16 rows (entries m0 .. of the expert's row list) against this wave's 16
+// features over the whole reduction length K, with no barrier and no LDS staging; the groups
+// share every weight load, so an expert with up to 16 NG rows reads its weights once:
 //  * per 128-k block a lane loads four 16-byte pieces of its weight row (and of its up row for the
 //    gate/up product) at k = 32 c + 8 (lane / 16), the MFMA operand layout, so that each load
-//    instruction reads 64 contiguous bytes of each of 16 rows, and the same pieces of its A row
-//    (a token row of x or a row of h, both L2-resident);
+//    instruction reads 64 contiguous bytes of each of 16 rows, and the same pieces of its A row in
+//    every group (a token row of x or a row of h, both L2-resident);
 //  * two blocks are in flight ahead of use;
 //  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
 //    that concurrent waves spread over the HBM channels instead of reading the same offset of
 //    their rows. The sum order is fixed per wave, so results repeat exactly.
-template <bool GATEUP>
+template <bool GATEUP, int NG>
 __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
                                             const uint16_t* __restrict__ W0,
                                             const uint16_t* __restrict__ W1, int K, int N, int k,
@@ -287,32 +288,44 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   const long long wofs = static_cast<long long>(e) * N * K + static_cast<long long>(f) * K + kq;
   const uint16_t* pg = W0 + wofs;
   const uint16_t* pu = GATEUP ? W1 + wofs : nullptr;
-  // lanes past the group's rows read row 0 of the group: their output rows are never stored
-  // (row i of the product depends only on A row i), and the duplicate reads coalesce
-  const int li_a = m0 + (l16 < rows ? l16 : 0);
-  const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
-  const uint16_t* pa = A + arow * K + kq;
+  // lanes past a group's rows read row 0 of that group (never stored: row i of the product
+  // depends only on A row i; the duplicate reads coalesce); a group past all rows repeats group 0
+  const uint16_t* pa[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int gr = rows - 16 * g;           // rows of group g (may be <= 0 for NG > 1)
+    const int li_a = m0 + (gr > 0 ? 16 * g + (l16 < gr ? l16 : 0) : 0);
+    const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
+    pa[g] = A + arow * K + kq;
+  }
   const int nb = K / 128;                     // even: K % 256 == 0 on this path
   const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
 
-  u32x4 a0[4], bg0[4], bu0[4], a1[4], bg1[4], bu1[4];
-  auto load = [&](u32x4* a, u32x4* bg, u32x4* bu, int sq) {
+  u32x4 a0[NG][4], bg0[4], bu0[4], a1[NG][4], bg1[4], bu1[4];
+  auto load = [&](u32x4 (*a)[4], u32x4* bg, u32x4* bu, int sq) {
     const int kb = ((min(sq, nb - 1) + rot) % nb) * 128;  // past the end: re-read the last block
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bg[c] = load16(pg + kb + c * 32);
       if constexpr (GATEUP) bu[c] = load16(pu + kb + c * 32);
-      a[c] = load16(pa + kb + c * 32);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) a[g][c] = load16(pa[g] + kb + c * 32);
     }
   };
-  f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const u32x4* a, const u32x4* bg, const u32x4* bu) {
+  f32x4 accg[NG], accu[NG];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      accg = mfma16x16x32(a[c], bg[c], accg);
-      if constexpr (GATEUP) accu = mfma16x16x32(a[c], bu[c], accu);
-    }
+  for (int g = 0; g < NG; ++g) {
+    accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](u32x4 (*a)[4], const u32x4* bg, const u32x4* bu) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        accg[g] = mfma16x16x32(a[g][c], bg[c], accg[g]);
+        if constexpr (GATEUP) accu[g] = mfma16x16x32(a[g][c], bu[c], accu[g]);
+      }
   };
   load(a0, bg0, bu0, 0);
   load(a1, bg1, bu1, 1);
@@ -329,25 +342,29 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   }
 
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = (lane >> 4) * 4 + r;  // row of this group
-    if (i >= rows) continue;
-    const int li = m0 + i;              // entry of the expert's row list
-    const int hrow = hbase >= 0 ? hbase + li : lr[li];
-    if constexpr (GATEUP) {
-      const float hv = silu(accg[r]) * accu[r];
-      h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
-    } else {
-      const DownRow dr = down_row(down, lr[li], hrow, N);
-      down_put(down, dr, f, accg[r]);
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * g + (lane >> 4) * 4 + r;  // row of this pass
+      if (i >= rows) continue;
+      const int li = m0 + i;                     // entry of the expert's row list
+      const int hrow = hbase >= 0 ? hbase + li : lr[li];
+      if constexpr (GATEUP) {
+        const float hv = silu(accg[g][r]) * accu[g][r];
+        h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
+      } else {
+        const DownRow dr = down_row(down, lr[li], hrow, N);
+        down_put(down, dr, f, accg[g][r]);
+      }
     }
   }
 }
 
 // Grid (N / 16, E), one wave per block: block (x, e) computes features [16 x, 16 x + 16) of
-// expert e for all of the expert's rows, 16 rows per pass (a second pass over the same weights
-// mostly hits the caches).
-template <bool GATEUP>
+// expert e for all of the expert's rows, up to 16 MAXG rows per pass over the weights (a further
+// pass mostly hits the caches). MAXG = 2 lets an expert with 17..32 rows, common under a
+// selection bias, read its weights once, at the cost of registers (fewer resident waves).
+template <bool GATEUP, int MAXG>
 __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
     const uint16_t* __restrict__ W1, int K, int N, int k, RowSource rs,
@@ -365,8 +382,14 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
     for (int i = threadIdx.x; i < count; i += blockDim.x) lr[i] = rs.sorted_rows[hbase + i];
     __syncthreads();
   }
-  for (int m0 = 0; m0 < count; m0 += 16)
-    stream_tile<GATEUP>(A, W0, W1, K, N, k, e, lr, m0, min(16, count - m0), hbase, h_out, down);
+  // passes of up to 16 MAXG rows: the 16-row groups of a pass share each weight load
+  for (int m0 = 0; m0 < count; m0 += 16 * MAXG) {
+    const int rows = min(16 * MAXG, count - m0);
+    if (MAXG > 1 && rows > 16)
+      stream_tile<GATEUP, MAXG>(A, W0, W1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
+    else
+      stream_tile<GATEUP, 1>(A, W0, W1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
+  }
 }
 
 }  // namespace
@@ -385,13 +408,22 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t
   DownArgs none{};
   hipError_t err;
   if (ffn_bf16_streaming(T, d, E, H, k)) {
-    err = launch_marked(ffn_stream_kernel<true>, dim3(H / kStFeat, E), dim3(kWave), s, gu, x, wg,
-                        wu, d, H, k, rs, h, none);
+    // two-group passes where every block of the grid stays resident at their lower occupancy
+    // (gate/up: 154 VGPRs, 12 waves per CU; down: 120 VGPRs, 16 waves per CU)
+    const bool g2 = (H / kStFeat) * E <= 2048;
+    err = g2 ? launch_marked(ffn_stream_kernel<true, 2>, dim3(H / kStFeat, E), dim3(kWave), s, gu,
+                             x, wg, wu, d, H, k, rs, h, none)
+             : launch_marked(ffn_stream_kernel<true, 1>, dim3(H / kStFeat, E), dim3(kWave), s, gu,
+                             x, wg, wu, d, H, k, rs, h, none);
     if (err != hipSuccess) return err;
     RowSource rs2 = rs;
     rs2.counts_out = nullptr;
-    ffn_stream_kernel<false><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
-                                                                     rs2, nullptr, down);
+    if ((d / kStFeat) * E <= 4096)
+      ffn_stream_kernel<false, 2><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
+                                                                          rs2, nullptr, down);
+    else
+      ffn_stream_kernel<false, 1><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
+                                                                          rs2, nullptr, down);
     return hipGetLastError();
   }
   // grouped GEMM over the dispatch order; 1-D grid sized for the worst-case tile count
