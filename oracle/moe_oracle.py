@@ -26,9 +26,16 @@ What the layer computes (one token t, E experts, k of them selected):
   7. combine         y[t] = sum_j w[t,j] * o[t,j], fp32 output stream in the library
                      (zonos2.cpp INTERNALS, "Notes": activation/residual streams are F32).
 
-Everything floating is fp64 with no intermediate rounding, except the one place where the library
-contract fixes fp32: ranking on given fp32 logits, where ``L + sel_bias`` is one fp32
-round-to-nearest-even add (numpy float32 addition is exactly that).
+Everything floating is fp64 with no intermediate rounding, except where the library contract fixes
+fp32: ranking on given fp32 logits, where ``L + sel_bias`` is one fp32 round-to-nearest-even add
+(numpy float32 addition is exactly that), and the int8 weight quantisation below, whose scale and
+quotient are fp32 operations so that the integer codes are defined exactly.
+
+Quantised expert weights (decode path; the ZONOS2-4bit MLX card and zonos2.cpp INTERNALS run
+quantised expert stacks, "Performance notes" / "Recommended: F16 spine + K-quant experts"): each
+weight row (one output feature of one expert) is quantised symmetrically to int8,
+  s = fl32(max_i |w_i| / 127),   q_i = clamp(rint(fl32(w_i / s)), -127, 127)   (ties to even),
+an all-zero row getting s = 0, q = 0; the layer then uses the weights s * q exactly.
 
 Pins (checked by the CPU tests against values the mathematics fixes, not against this code):
 brute-force selection, closed-form softmax weights, exact fp32 rounding cases, dispatch
@@ -116,6 +123,33 @@ def route_ref(logits32, sel_bias, k, scoring):
     ids = select_topk_ref(s, k)
     w = routing_weights_ref(np.asarray(logits32, dtype=np.float32), ids, scoring)
     return ids, w, expert_counts_ref(ids, np.asarray(logits32).shape[1])
+
+
+# ------------------------------------------------------------------ int8 expert weights (decode)
+
+def quantize_rows_i8_ref(w):
+    """Per-row symmetric int8 codes of a [..., K] weight stack: q (int8, same shape) and s (fp32,
+    shape [...]). The scale and the quotient are fp32 operations (numpy float32 division is the
+    IEEE round-to-nearest-even quotient), the rounding is to nearest with ties to even."""
+    w32 = np.asarray(w, dtype=np.float32)
+    rows = w32.reshape(-1, w32.shape[-1])
+    q = np.zeros(rows.shape, dtype=np.int8)
+    s = np.zeros(rows.shape[0], dtype=np.float32)
+    for r in range(rows.shape[0]):
+        m = np.float32(np.max(np.abs(rows[r]))) if rows.shape[1] else np.float32(0)
+        if m == 0:
+            continue
+        sc = np.float32(m / np.float32(127))
+        s[r] = sc
+        for i in range(rows.shape[1]):
+            v = np.rint(np.float32(rows[r, i] / sc))
+            q[r, i] = int(min(127.0, max(-127.0, float(v))))
+    return q.reshape(w32.shape), s.reshape(w32.shape[:-1])
+
+
+def dequantize_rows_ref(q, s):
+    """The weights the int8 layer computes with: s * q per row, exactly (fp64)."""
+    return np.asarray(q, dtype=f64) * np.asarray(s, dtype=f64)[..., None]
 
 
 # ------------------------------------------------------------------------------ dispatch (step 5)

@@ -67,6 +67,15 @@ def test_hand_sigmoid_no_renorm(hand):
         assert counts.sum() == case["k"]
 
 
+def test_hand_int8_quantisation(hand):
+    c = hand["int8_row_quantisation"]
+    W = np.array([[_ev(v) for v in row["w"]] for row in c["rows"]], dtype=np.float32)
+    q, s = orc.quantize_rows_i8_ref(W)
+    for i, row in enumerate(c["rows"]):
+        assert q[i].tolist() == row["q"]
+        assert float(s[i]) == _ev(row["s"])
+
+
 def test_hand_fp32_rank_add(hand):
     c = hand["fp32_rank_add"]
     L32 = _arr(c["logits"])[None, :].astype(np.float32)
@@ -194,6 +203,48 @@ def test_sigmoid_weight_invariants():
     np.testing.assert_allclose(ws, wp, rtol=1e-14)
     with pytest.raises(ValueError):
         orc.route_ref(L, np.zeros(2, np.float32), 1, orc.SIGMOID)
+
+
+def test_int8_quantisation_invariants():
+    rng = np.random.default_rng(12)
+    W = gen.bf16_bits_to_f32(gen.bf16_round_bits(rng.standard_normal((3, 40, 96)).astype(np.float32)))
+    W[1, 7] = 0.0                                         # an all-zero row
+    q, s = orc.quantize_rows_i8_ref(W)
+    assert q.dtype == np.int8 and q.shape == W.shape and s.shape == W.shape[:2]
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    assert s[1, 7] == 0 and (q[1, 7] == 0).all()
+    nz = s > 0
+    amax = np.abs(W).argmax(axis=-1)
+    qmax = np.take_along_axis(q, amax[..., None], axis=-1)[..., 0].astype(np.int32)
+    assert (np.abs(qmax[nz]) == 127).all()              # the extreme element takes the full code
+    err = np.abs(W.astype(np.float64) - orc.dequantize_rows_ref(q, s))
+    # |w/s - q| <= 1/2 plus the rounding of the fp32 quotient (<= 127 * 2^-24 relative to s)
+    assert (err <= s.astype(np.float64)[..., None] * (0.5 + 127 * 2.0 ** -24)).all()
+    # codes of rows that are already s * integer (s a power of two) come back unchanged
+    qi = rng.integers(-127, 128, size=(16, 64)).astype(np.float32)
+    qi[:, 0] = 127
+    Wexact = qi * np.float32(2.0 ** -5)
+    q2, s2 = orc.quantize_rows_i8_ref(Wexact)
+    assert (s2 == np.float32(2.0 ** -5)).all()
+    np.testing.assert_array_equal(q2.astype(np.float32), qi)
+
+
+def test_int8_layer_on_exact_weights_equals_bf16_layer():
+    # weights that are exactly s * q: quantising and dequantising them changes nothing, so the
+    # int8 layer is the plain layer on the same weights (independent of the quantiser's rounding)
+    inp = _case(T=16, d=32, E=4, k=2, H=48, scoring=orc.SOFTMAX, seed=14)
+    rng = np.random.default_rng(14)
+    for key in ("w_gate", "w_up", "w_down"):
+        a = getattr(inp, key)
+        qi = rng.integers(-127, 128, size=a.shape).astype(np.float32)
+        qi[..., 0] = -127
+        setattr(inp, key, qi * np.float32(2.0 ** -9))
+    deq = {key: orc.dequantize_rows_ref(*orc.quantize_rows_i8_ref(getattr(inp, key)))
+           for key in ("w_gate", "w_up", "w_down")}
+    y_q = orc.layer_ref(inp.x, inp.w_router, deq["w_gate"], deq["w_up"], deq["w_down"], inp.k,
+                        inp.scoring)["y"]
+    y = orc.layer_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k, inp.scoring)["y"]
+    np.testing.assert_array_equal(y_q, y)
 
 
 def test_mode_equivalence_k_equals_E():
@@ -369,6 +420,7 @@ def _pins_pass():
         test_hand_softmax_no_renorm(hand)
         test_hand_selected_softmax(hand)
         test_hand_sigmoid_no_renorm(hand)
+        test_hand_int8_quantisation(hand)
         test_hand_fp32_rank_add(hand)
         test_hand_swiglu_layer(hand, "swiglu_one_expert")
         test_hand_swiglu_layer(hand, "swiglu_two_experts_top1")
@@ -376,6 +428,7 @@ def _pins_pass():
         test_softmax_weight_invariants()
         test_selected_softmax_weight_invariants()
         test_sigmoid_weight_invariants()
+        test_int8_quantisation_invariants()
         test_permute_invariants(64, 64, 2)
         test_layer_equals_dense_bruteforce(orc.SELECTED_SOFTMAX, 2, False, True)
         test_single_expert_is_dense_swiglu_torch()
@@ -412,6 +465,15 @@ MUTATIONS = {
     "sigmoid_renorm": ("routing_weights_ref", lambda orig: (lambda L, ids, scoring: (
         (lambda w: w / w.sum(axis=1, keepdims=True))(orig(L, ids, scoring))
         if scoring == orc.SIGMOID else orig(L, ids, scoring)))),
+    # int8 codes rounded half away from zero instead of half to even
+    "q8_half_away": ("quantize_rows_i8_ref", lambda orig: (lambda w: (lambda q, s: (
+        np.clip(np.trunc(np.float32(np.asarray(w, np.float32) / np.where(s == 0, 1, s)[..., None])
+                         + np.copysign(0.5, np.asarray(w, np.float32))), -127, 127).astype(np.int8), s))(
+        *orig(w)))),
+    # scale from max / 128 (the extreme element no longer takes the full code)
+    "q8_scale_128": ("quantize_rows_i8_ref", lambda orig: (lambda w: (lambda q, s: (
+        np.clip(np.rint(np.asarray(w, np.float32) / np.where(s == 0, 1, s * np.float32(128 / 127))[..., None]),
+                -127, 127).astype(np.int8), (s * np.float32(128 / 127)).astype(np.float32)))(*orig(w)))),
     # rank on the fp64 sum instead of the binary32 add
     "rank_fp64": ("rank_scores_fp32", lambda orig: (lambda L, b=None: np.asarray(L, np.float64) + (
         0 if b is None else np.asarray(b, np.float64)[None, :]))),
