@@ -87,16 +87,20 @@ def _hip():
     return lib
 
 
-def algorithmic(inp, counts):
-    """Bytes and FLOPs the step must move/do (touched experts only; intermediates excluded)."""
+def algorithmic(inp, counts, int8_weights=False):
+    """Bytes and FLOPs the step must move/do (touched experts only; intermediates excluded).
+    int8 expert weights: one byte per weight plus the fp32 row scales of the touched experts."""
     T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
-    wb = 2 if inp.dtype == "bf16" else 4
+    ab = 2 if inp.dtype == "bf16" else 4             # activations and router weights
+    wb = 1 if int8_weights else ab                   # expert weights
+    sb = 4 if int8_weights else 0                    # one fp32 scale per expert weight row
     touched = int((counts > 0).sum())
     rows = T * k
-    step_bytes = touched * 3 * d * H * wb + T * d * wb + E * d * wb + T * d * 4 + rows * 8
+    step_bytes = (touched * (3 * d * H * wb + (2 * H + d) * sb) + T * d * ab + E * d * ab +
+                  T * d * 4 + rows * 8)
     step_flops = 6 * d * H * rows + 2 * T * d * E
-    # the gate/up kernel alone: its weights, the gathered x rows, the bf16 h it writes
-    gu_bytes = touched * 2 * d * H * wb + rows * d * wb + rows * H * wb
+    # the gate/up kernel alone: its weights (and scales), the gathered x rows, the bf16 h it writes
+    gu_bytes = touched * (2 * d * H * wb + 2 * H * sb) + rows * d * ab + rows * H * ab
     gu_flops = 4 * d * H * rows
     return dict(touched=touched, step_bytes=step_bytes, step_flops=step_flops, gu_bytes=gu_bytes,
                 gu_flops=gu_flops)
@@ -139,6 +143,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
+    ap.add_argument("--weights", choices=("native", "int8"), default="native",
+                    help="expert weights as given (bf16/fp32) or int8 codes with per-row scales "
+                         "(moe_quantize_rows_i8; decode shapes only)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -180,6 +187,12 @@ def main():
     x = up("x")
     wr = up("w_router")
     base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
+    int8 = args.weights == "int8"
+    if int8:
+        qs = {key: moe.moe_quantize_rows_i8(t) for key, t in base.items()}
+        base = {key: v[0] for key, v in qs.items()}
+        base.update({key + "_scale": v[1] for key, v in qs.items()})
+        torch.cuda.synchronize()
     wbytes = sum(t.numel() * t.element_size() for t in base.values())
     ncopies = 1 if args.warm else max(2, min(16, math.ceil(1.6e9 / wbytes)))
     copies = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(ncopies - 1)]
@@ -204,9 +217,11 @@ def main():
         arr = (ctypes.c_void_p * nev)(*[e.value for e in evs])
         events.append(evs)
         ev_arrays.append(arr)
+        scales = ((copies[c]["w_gate_scale"], copies[c]["w_up_scale"], copies[c]["w_down_scale"])
+                  if int8 else None)
         a = moe.make_layer_args(x, wr, copies[c]["w_gate"], copies[c]["w_up"],
                                 copies[c]["w_down"], k, inp.scoring, y, rb, sb,
-                                expert_counts=counts)
+                                expert_counts=counts, w_scales=scales)
         arg_list.append(a)
 
     stream = torch.cuda.Stream()
@@ -301,7 +316,7 @@ def main():
     step_ms_ev = [sum(stage_ms[s_][i] for s_ in STAGES) for i in range(len(stage_ms["route"]))]
 
     cnt = counts.cpu().numpy()
-    alg = algorithmic(inp, cnt)
+    alg = algorithmic(inp, cnt, int8)
     med = {s: statistics.median(v) for s, v in stage_ms.items()}
     gu_ms = statistics.mean(stage_ms["gate_up"])
     prefill = gen.WORKLOADS[args.workload].shape == "prefill"
@@ -317,7 +332,7 @@ def main():
         T * k <= 32 * E
     roof["kernel"] = "ffn_stream_kernel<true>" if streaming else (
         "gemm_dma_kernel<true, 256, 128>" if inp.dtype == "bf16" else "ffn_f32_kernel<true>")
-    traffic = measured_traffic(roof["kernel"], args.workload)
+    traffic = measured_traffic(roof["kernel"], args.workload + ("/int8" if int8 else ""))
     roof["traffic"] = traffic
     roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
                               if traffic is not None else "not measured for the current kernel")
@@ -342,6 +357,7 @@ def main():
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "H": H,
                    "scoring": inp.scoring, "seed": gen.WORKLOADS[args.workload].seed,
                    "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
+                   "expert_weights": "int8, fp32 row scales" if int8 else inp.dtype,
                    "timing": ("host launches" if args.eager else
                               "HIP graph replay, one step per weight copy"),
                    "stage_events": ev_mode, "stage_event_steps": len(step_ms_ev)},

@@ -264,30 +264,54 @@ __device__ int scan_rows(const int32_t* __restrict__ ids, int n, int e, int* lr)
   return total;
 }
 
+// 8 int8 codes (two dwords, lowest k first) as 8 bf16 values (exact: |code| <= 127 needs 7
+// significand bits): sign-extend, convert to fp32, keep the upper halves.
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t v, int sh) {
+  const float lo = static_cast<float>(static_cast<int8_t>(v >> sh));
+  const float hi = static_cast<float>(static_cast<int8_t>(v >> (sh + 8)));
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 16), i8pair_to_bf16x2(w1, 0),
+               i8pair_to_bf16x2(w1, 16)};
+}
+
 // Up to NG groups of 16 rows (entries m0 .. of the expert's row list) against this wave's 16
 // features over the whole reduction length K, with no barrier and no LDS staging; the groups
 // share every weight load, so an expert with up to 16 NG rows reads its weights once:
-//  * per 128-k block a lane loads four 16-byte pieces of its weight row (and of its up row for the
-//    gate/up product) at k = 32 c + 8 (lane / 16), the MFMA operand layout, so that each load
-//    instruction reads 64 contiguous bytes of each of 16 rows, and the same pieces of its A row in
-//    every group (a token row of x or a row of h, both L2-resident);
+//  * per 128-k block, MFMA step c (c = 0..3) and lane group g = lane / 16 cover 8 consecutive k;
+//    bf16 weights: k = 32 c + 8 g, so each load instruction reads 64 contiguous bytes of each of
+//    16 rows; int8 weights (W8): k = 32 g + 8 c, so a lane's 32 code bytes of the block are
+//    contiguous (two 16-byte loads), converted to bf16 right before the MFMA and scaled per row
+//    in the epilogue. The A rows (a token row of x or a row of h, both L2-resident) are read
+//    with the same k layout, one piece per step, for every group;
 //  * two blocks are in flight ahead of use;
 //  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
 //    that concurrent waves spread over the HBM channels instead of reading the same offset of
 //    their rows. The sum order is fixed per wave, so results repeat exactly.
-template <bool GATEUP, int NG>
+template <bool GATEUP, int NG, bool W8>
 __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
-                                            const uint16_t* __restrict__ W0,
-                                            const uint16_t* __restrict__ W1, int K, int N, int k,
+                                            const void* __restrict__ W0,
+                                            const void* __restrict__ W1,
+                                            const float* __restrict__ S0,
+                                            const float* __restrict__ S1, int K, int N, int k,
                                             int e, const int* lr, int m0, int rows, int hbase,
                                             uint16_t* __restrict__ h_out, const DownArgs& down) {
+  constexpr int WR = W8 ? 2 : 4;              // weight registers (u32x4) per matrix per block
   const int lane = lane_id();
   const int l16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
+  const int grp = lane >> 4;
+  const int kq = W8 ? 32 * grp : 8 * grp;     // lane's first k inside a 128-k block
   const int f = blockIdx.x * kStFeat + l16;  // weight row (N % 16 == 0)
-  const long long wofs = static_cast<long long>(e) * N * K + static_cast<long long>(f) * K + kq;
-  const uint16_t* pg = W0 + wofs;
-  const uint16_t* pu = GATEUP ? W1 + wofs : nullptr;
+  const long long row0 = static_cast<long long>(e) * N + f;
+  const long long wofs = row0 * K + kq;      // elements (bf16) or bytes (int8)
+  const char* pg = static_cast<const char*>(W0) + (W8 ? wofs : 2 * wofs);
+  const char* pu = GATEUP ? static_cast<const char*>(W1) + (W8 ? wofs : 2 * wofs) : nullptr;
+  float sg = 1.f, su = 1.f;
+  if constexpr (W8) {
+    sg = S0[row0];
+    if constexpr (GATEUP) su = S1[row0];
+  }
   // lanes past a group's rows read row 0 of that group (never stored: row i of the product
   // depends only on A row i; the duplicate reads coalesce); a group past all rows repeats group 0
   const uint16_t* pa[NG];
@@ -301,15 +325,26 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   const int nb = K / 128;                     // even: K % 256 == 0 on this path
   const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
 
-  u32x4 a0[NG][4], bg0[4], bu0[4], a1[NG][4], bg1[4], bu1[4];
+  u32x4 a0[NG][4], bg0[WR], bu0[WR], a1[NG][4], bg1[WR], bu1[WR];
   auto load = [&](u32x4 (*a)[4], u32x4* bg, u32x4* bu, int sq) {
     const int kb = ((min(sq, nb - 1) + rot) % nb) * 128;  // past the end: re-read the last block
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bg[c] = load16(pg + kb + c * 32);
-      if constexpr (GATEUP) bu[c] = load16(pu + kb + c * 32);
+    for (int c = 0; c < WR; ++c) {
+      const int off = W8 ? kb + 16 * c : 2 * (kb + 32 * c);  // bytes
+      bg[c] = load16(pg + off);
+      if constexpr (GATEUP) bu[c] = load16(pu + off);
+    }
 #pragma unroll
-      for (int g = 0; g < NG; ++g) a[g][c] = load16(pa[g] + kb + c * 32);
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) a[g][c] = load16(pa[g] + kb + (W8 ? 8 * c : 32 * c));
+  };
+  auto wop = [&](const u32x4* b, int c) -> u32x4 {
+    if constexpr (W8) {
+      const u32x4 v = b[c >> 1];
+      return (c & 1) ? i8x8_to_bf16x8(v[2], v[3]) : i8x8_to_bf16x8(v[0], v[1]);
+    } else {
+      return b[c];
     }
   };
   f32x4 accg[NG], accu[NG];
@@ -320,12 +355,16 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   }
   auto compute = [&](u32x4 (*a)[4], const u32x4* bg, const u32x4* bu) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 wg = wop(bg, c);
+      u32x4 wu = wg;
+      if constexpr (GATEUP) wu = wop(bu, c);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        accg[g] = mfma16x16x32(a[g][c], bg[c], accg[g]);
-        if constexpr (GATEUP) accu[g] = mfma16x16x32(a[g][c], bu[c], accu[g]);
+        accg[g] = mfma16x16x32(a[g][c], wg, accg[g]);
+        if constexpr (GATEUP) accu[g] = mfma16x16x32(a[g][c], wu, accu[g]);
       }
+    }
   };
   load(a0, bg0, bu0, 0);
   load(a1, bg1, bu1, 1);
@@ -350,11 +389,11 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
       const int li = m0 + i;                     // entry of the expert's row list
       const int hrow = hbase >= 0 ? hbase + li : lr[li];
       if constexpr (GATEUP) {
-        const float hv = silu(accg[g][r]) * accu[g][r];
+        const float hv = silu(sg * accg[g][r]) * (su * accu[g][r]);
         h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
       } else {
         const DownRow dr = down_row(down, lr[li], hrow, N);
-        down_put(down, dr, f, accg[g][r]);
+        down_put(down, dr, f, sg * accg[g][r]);
       }
     }
   }
@@ -364,11 +403,12 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
 // expert e for all of the expert's rows, up to 16 MAXG rows per pass over the weights (a further
 // pass mostly hits the caches). MAXG = 2 lets an expert with 17..32 rows, common under a
 // selection bias, read its weights once, at the cost of registers (fewer resident waves).
-template <bool GATEUP, int MAXG>
+// W8: int8 weight codes with fp32 row scales S0 (gate or down) and S1 (up).
+template <bool GATEUP, int MAXG, bool W8>
 __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
-    const uint16_t* __restrict__ W1, int K, int N, int k, RowSource rs,
-    uint16_t* __restrict__ h_out, DownArgs down) {
+    const uint16_t* __restrict__ A, const void* __restrict__ W0, const void* __restrict__ W1,
+    const float* __restrict__ S0, const float* __restrict__ S1, int K, int N, int k,
+    RowSource rs, uint16_t* __restrict__ h_out, DownArgs down) {
   __shared__ int lr[kMaxScanRows];
   const int e = blockIdx.y;
   int count, hbase;
@@ -386,9 +426,10 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
   for (int m0 = 0; m0 < count; m0 += 16 * MAXG) {
     const int rows = min(16 * MAXG, count - m0);
     if (MAXG > 1 && rows > 16)
-      stream_tile<GATEUP, MAXG>(A, W0, W1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
+      stream_tile<GATEUP, MAXG, W8>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase, h_out,
+                                    down);
     else
-      stream_tile<GATEUP, 1>(A, W0, W1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
+      stream_tile<GATEUP, 1, W8>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
   }
 }
 
@@ -399,43 +440,56 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
   return rows <= kMaxScanRows && d % 256 == 0 && H % 256 == 0 && rows <= 32ll * E;
 }
 
-hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
-                           const uint16_t* wd, int T, int d, int E, int H, int k,
-                           const RowSource& rs, uint16_t* h, const DownArgs& down, hipStream_t s,
-                           const StageMarks& gu) {
+hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, const void* wd,
+                           int T, int d, int E, int H, int k, const RowSource& rs, uint16_t* h,
+                           const DownArgs& down, hipStream_t s, const StageMarks& gu,
+                           const WeightScales& q8) {
   const int rows = T * k;
   if (rows <= 0) return hipSuccess;
   DownArgs none{};
   hipError_t err;
+  const bool w8 = q8.gate != nullptr;
   if (ffn_bf16_streaming(T, d, E, H, k)) {
     // two-group passes where every block of the grid stays resident at their lower occupancy
-    // (gate/up: 154 VGPRs, 12 waves per CU; down: 120 VGPRs, 16 waves per CU)
+    // (gate/up: ~154 VGPRs, 12 waves per CU; down: ~120 VGPRs, 16 waves per CU)
     const bool g2 = (H / kStFeat) * E <= 2048;
-    err = g2 ? launch_marked(ffn_stream_kernel<true, 2>, dim3(H / kStFeat, E), dim3(kWave), s, gu,
-                             x, wg, wu, d, H, k, rs, h, none)
-             : launch_marked(ffn_stream_kernel<true, 1>, dim3(H / kStFeat, E), dim3(kWave), s, gu,
-                             x, wg, wu, d, H, k, rs, h, none);
+    const dim3 g_gu(H / kStFeat, E), g_dn(d / kStFeat, E);
+#define MOE_GU(MG, W)                                                                    \
+  launch_marked(ffn_stream_kernel<true, MG, W>, g_gu, dim3(kWave), s, gu, x, wg, wu, q8.gate, \
+                q8.up, d, H, k, rs, h, none)
+    err = w8 ? (g2 ? MOE_GU(2, true) : MOE_GU(1, true)) : (g2 ? MOE_GU(2, false) : MOE_GU(1, false));
+#undef MOE_GU
     if (err != hipSuccess) return err;
     RowSource rs2 = rs;
     rs2.counts_out = nullptr;
-    if ((d / kStFeat) * E <= 4096)
-      ffn_stream_kernel<false, 2><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
-                                                                          rs2, nullptr, down);
-    else
-      ffn_stream_kernel<false, 1><<<dim3(d / kStFeat, E), kWave, 0, s>>>(h, wd, nullptr, H, d, k,
-                                                                          rs2, nullptr, down);
+    const bool g2d = (d / kStFeat) * E <= 4096;
+#define MOE_DN(MG, W)                                                                        \
+  ffn_stream_kernel<false, MG, W><<<g_dn, kWave, 0, s>>>(h, wd, nullptr, q8.down, nullptr, H, d, k, \
+                                                         rs2, nullptr, down)
+    if (w8) {
+      if (g2d) MOE_DN(2, true);
+      else MOE_DN(1, true);
+    } else {
+      if (g2d) MOE_DN(2, false);
+      else MOE_DN(1, false);
+    }
+#undef MOE_DN
     return hipGetLastError();
   }
+  if (w8) return hipErrorInvalidValue;  // int8 weights: weight-streaming shapes only (checked above)
   // grouped GEMM over the dispatch order; 1-D grid sized for the worst-case tile count
   auto grid_for = [&](int bm, int feat, int n) {
     return static_cast<unsigned>(static_cast<long long>(max_tiles(rows, E, bm)) *
                                  ((n + feat - 1) / feat));
   };
+  const uint16_t* wg16 = static_cast<const uint16_t*>(wg);
+  const uint16_t* wu16 = static_cast<const uint16_t*>(wu);
+  const uint16_t* wd16 = static_cast<const uint16_t*>(wd);
   err = launch_marked(gemm_dma_kernel<true, 256, 128>, dim3(grid_for(256, 64, H)), dim3(512), s,
-                      gu, x, wg, wu, d, H, E, k, rs.offsets, rs.sorted_rows, h, none);
+                      gu, x, wg16, wu16, d, H, E, k, rs.offsets, rs.sorted_rows, h, none);
   if (err != hipSuccess) return err;
   gemm_dma_kernel<false, 256, 128><<<grid_for(256, 128, d), 512, 0, s>>>(
-      h, wd, nullptr, H, d, E, k, rs.offsets, rs.sorted_rows, nullptr, down);
+      h, wd16, nullptr, H, d, E, k, rs.offsets, rs.sorted_rows, nullptr, down);
   return hipGetLastError();
 }
 

@@ -107,15 +107,28 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k);
 // Largest T*k the by-ids row scan supports.
 constexpr int kMaxScanRows = 2048;
 
+// Row scales of int8 expert weights ([E,H], [E,H], [E,d]); all NULL for bf16 weights.
+struct WeightScales {
+  const float* gate;
+  const float* up;
+  const float* down;
+};
+
 // h is the [T*k, H] intermediate (bf16 bits or fp32). `gu` marks the gate/up launch (timing).
-hipError_t launch_ffn_bf16(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
-                           const uint16_t* wd, int T, int d, int E, int H, int k,
-                           const RowSource& rs, uint16_t* h, const DownArgs& down, hipStream_t s,
-                           const StageMarks& gu);
+// wg, wu, wd are bf16 bits, or int8 codes when `q8.gate` is set (weight-streaming shapes only).
+hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, const void* wd,
+                           int T, int d, int E, int H, int k, const RowSource& rs, uint16_t* h,
+                           const DownArgs& down, hipStream_t s, const StageMarks& gu,
+                           const WeightScales& q8);
 hipError_t launch_ffn_f32(const float* x, const float* wg, const float* wu, const float* wd,
                           int T, int d, int E, int H, int k, const int32_t* offsets,
                           const int32_t* sorted_rows, float* h, const DownArgs& down,
                           hipStream_t s, const StageMarks& gu);
+
+// ---------------------------------------------------------------- int8 weights (quant.hip)
+// Per-row symmetric int8 codes of a [rows, K] matrix (bf16 bits or fp32), K % 16 == 0.
+hipError_t launch_quantize_rows_i8(const void* w, long long rows, int K, bool bf16, int8_t* q,
+                                   float* scales, hipStream_t s);
 
 // ---------------------------------------------------------------- combine (combine.hip)
 // row_pos == NULL: expert_out is indexed by the assignment row itself.

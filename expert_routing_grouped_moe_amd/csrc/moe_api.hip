@@ -197,15 +197,26 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
   clear_stale_error();
   if (dtype == MOE_BF16) {
     const RowSource rs{nullptr, T * k, expert_offsets, sorted_rows, nullptr};
-    return hip_status(moe::launch_ffn_bf16(
-        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
-        static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), T, d, E, H, k,
-        rs, at<uint16_t>(ws, lay.h), down, s, moe::StageMarks{}));
+    return hip_status(moe::launch_ffn_bf16(static_cast<const uint16_t*>(x), w_gate, w_up, w_down, T,
+                                           d, E, H, k, rs, at<uint16_t>(ws, lay.h), down, s,
+                                           moe::StageMarks{}, moe::WeightScales{}));
   }
   return hip_status(moe::launch_ffn_f32(
       static_cast<const float*>(x), static_cast<const float*>(w_gate),
       static_cast<const float*>(w_up), static_cast<const float*>(w_down), T, d, E, H, k,
       expert_offsets, sorted_rows, at<float>(ws, lay.h), down, s, moe::StageMarks{}));
+}
+
+int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* q, float* scales,
+                         void* stream) {
+  if (rows < 0 || K < 1 || K % 16 != 0) return MOE_ERR_SHAPE;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !scales) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return MOE_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(moe::launch_quantize_rows_i8(w, rows, K, dtype == MOE_BF16, q, scales,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
@@ -222,12 +233,25 @@ int moe_combine(const float* expert_out, const int32_t* row_pos, const float* to
 
 int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
   if (!a) return MOE_ERR_NULL;
-  if (a->struct_size < sizeof(moe_layer_args)) return MOE_ERR_UNSUPPORTED;
+  if (a->struct_size < MOE_LAYER_ARGS_V1_SIZE) return MOE_ERR_UNSUPPORTED;
   const int T = a->T, d = a->d, E = a->E, H = a->H, k = a->k, dtype = a->dtype;
   int st = check_dims(T, d, E, H, k, dtype);
   if (st != MOE_OK) return st;
   st = check_scoring(a->scoring, a->sel_bias);
   if (st != MOE_OK) return st;
+  // expert weight type: 0 (a zero-initialised struct) or the ABI-1 layout means the activation
+  // dtype
+  const bool abi2 = a->struct_size >= sizeof(moe_layer_args);
+  const int w_dtype = (abi2 && a->w_dtype != 0) ? a->w_dtype : dtype;
+  moe::WeightScales q8{};
+  if (w_dtype != dtype) {
+    if (w_dtype != MOE_I8 || dtype != MOE_BF16 || !moe::ffn_bf16_streaming(T, d, E, H, k))
+      return MOE_ERR_UNSUPPORTED;
+    if (!a->w_gate_scale || !a->w_up_scale || !a->w_down_scale) return MOE_ERR_NULL;
+    if (!aligned16(a->w_gate_scale) || !aligned16(a->w_up_scale) || !aligned16(a->w_down_scale))
+      return MOE_ERR_SHAPE;
+    q8 = moe::WeightScales{a->w_gate_scale, a->w_up_scale, a->w_down_scale};
+  }
   if (T == 0) return MOE_OK;
   if (!a->x || !a->w_router || !a->w_gate || !a->w_up || !a->w_down || !a->y) return MOE_ERR_NULL;
   const void* ptrs[] = {a->x, a->w_router, a->router_bias, a->sel_bias, a->w_gate, a->w_up,
@@ -292,10 +316,9 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   if (dtype == MOE_BF16) {
     const RowSource rs = streaming ? RowSource{ids, T * k, nullptr, nullptr, counts}
                                    : RowSource{nullptr, T * k, offsets, sorted_rows, nullptr};
-    MOE_TRY(moe::launch_ffn_bf16(
-        static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_gate),
-        static_cast<const uint16_t*>(a->w_up), static_cast<const uint16_t*>(a->w_down), T, d, E,
-        H, k, rs, at<uint16_t>(ws, lay.h), down, s, gu));
+    MOE_TRY(moe::launch_ffn_bf16(static_cast<const uint16_t*>(a->x), a->w_gate, a->w_up,
+                                 a->w_down, T, d, E, H, k, rs, at<uint16_t>(ws, lay.h), down, s,
+                                 gu, q8));
   } else {
     MOE_TRY(moe::launch_ffn_f32(
         static_cast<const float*>(a->x), static_cast<const float*>(a->w_gate),

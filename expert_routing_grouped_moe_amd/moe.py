@@ -24,6 +24,7 @@ MOE_ERR_HIP = -5
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_I8 = 2
 
 MOE_SCORING_SOFTMAX = 0
 MOE_SCORING_SELECTED_SOFTMAX = 1
@@ -33,7 +34,8 @@ SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELEC
            "sigmoid": MOE_SCORING_SIGMOID}
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
-           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+           "moe_quantize_rows_i8")
 
 
 class MoeError(RuntimeError):
@@ -52,6 +54,8 @@ class MoeLayerArgs(Structure):
         ("logits", c_void_p), ("topk_ids", c_void_p), ("topk_w", c_void_p),
         ("expert_counts", c_void_p),
         ("prof_events", c_void_p),   # void* const*: MOE_PROF_EVENTS hipEvent_t handles or NULL
+        ("w_dtype", c_int32),
+        ("w_gate_scale", c_void_p), ("w_up_scale", c_void_p), ("w_down_scale", c_void_p),
     ]
 
 
@@ -87,6 +91,9 @@ def _load() -> ctypes.CDLL:
                                 c_void_p]
     lib.moe_layer_forward.restype = c_int
     lib.moe_layer_forward.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_size_t, c_void_p]
+    lib.moe_quantize_rows_i8.restype = c_int
+    lib.moe_quantize_rows_i8.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
+                                         c_void_p, c_void_p]
     return lib
 
 
@@ -243,14 +250,24 @@ def moe_combine(expert_out, row_pos, topk_w, y=None, stream=None):
 
 
 def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias=None,
-                    sel_bias=None, logits=None, topk_ids=None, topk_w=None, expert_counts=None):
+                    sel_bias=None, logits=None, topk_ids=None, topk_w=None, expert_counts=None,
+                    w_scales=None):
+    """``w_scales`` = (gate, up, down) fp32 row scales when the expert weights are int8 codes
+    (moe_quantize_rows_i8)."""
     T, d = x.shape
     E, H, _ = w_gate.shape
+    wt = torch.int8 if w_gate.dtype == torch.int8 else x.dtype
     _need(x, "x", (T, d))
     _need(w_router, "w_router", (E, d), x.dtype)
-    _need(w_gate, "w_gate", (E, H, d), x.dtype)
-    _need(w_up, "w_up", (E, H, d), x.dtype)
-    _need(w_down, "w_down", (E, d, H), x.dtype)
+    _need(w_gate, "w_gate", (E, H, d), wt)
+    _need(w_up, "w_up", (E, H, d), wt)
+    _need(w_down, "w_down", (E, d, H), wt)
+    if wt == torch.int8:
+        if w_scales is None:
+            raise ValueError("int8 expert weights need w_scales = (gate, up, down)")
+        _need(w_scales[0], "w_gate_scale", (E, H), torch.float32)
+        _need(w_scales[1], "w_up_scale", (E, H), torch.float32)
+        _need(w_scales[2], "w_down_scale", (E, d), torch.float32)
     _need(router_bias, "router_bias", (E,), torch.float32)
     _need(sel_bias, "sel_bias", (E,), torch.float32)
     _need(y, "y", (T, d), torch.float32)
@@ -262,6 +279,9 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
     a.struct_size = ctypes.sizeof(MoeLayerArgs)
     a.T, a.d, a.E, a.H, a.k = T, d, E, H, k
     a.dtype = _dtype_code(x)
+    a.w_dtype = MOE_I8 if wt == torch.int8 else a.dtype
+    if wt == torch.int8:
+        a.w_gate_scale, a.w_up_scale, a.w_down_scale = (t.data_ptr() for t in w_scales)
     a.scoring = _scoring_code(scoring)
     for name, t in (("x", x), ("w_router", w_router), ("router_bias", router_bias),
                     ("sel_bias", sel_bias), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down),
@@ -273,17 +293,34 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
 
 def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
                       sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
-                      expert_counts=None, workspace=None, stream=None, args=None):
-    """The fused layer. Returns y [T, d] fp32. Optional outputs are written when passed."""
+                      expert_counts=None, workspace=None, stream=None, args=None, w_scales=None):
+    """The fused layer. Returns y [T, d] fp32. Optional outputs are written when passed. With
+    int8 expert weights (codes from moe_quantize_rows_i8) pass their row scales as w_scales."""
     T, d = x.shape
     E, H, _ = w_gate.shape
     y = _empty((T, d), torch.float32, x) if y is None else y
     if args is None:
         args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias,
-                               sel_bias, logits, topk_ids, topk_w, expert_counts)
+                               sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales)
     ws_bytes = moe_workspace_size(T, d, E, H, k, args.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     _check(LIB.moe_layer_forward(ctypes.byref(args), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "moe_layer_forward")
     return y
+
+
+def moe_quantize_rows_i8(w, q=None, scales=None, stream=None):
+    """Per-row symmetric int8 codes of w [..., K] (bf16 or fp32): returns (q int8 [..., K],
+    scales fp32 [...])."""
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    q = torch.empty(w.shape, dtype=torch.int8, device=w.device) if q is None else q
+    scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device) if scales is None else scales
+    _need(q, "q", tuple(w.shape), torch.int8)
+    _need(scales, "scales", tuple(w.shape[:-1]), torch.float32)
+    _check(LIB.moe_quantize_rows_i8(_ptr(w), rows, K, _dtype_code(w), _ptr(q), _ptr(scales),
+                                    _stream(stream)), "moe_quantize_rows_i8")
+    return q, scales

@@ -64,7 +64,13 @@ enum moe_status {
   MOE_ERR_HIP = -5          /* a HIP launch failed                                           */
 };
 
-enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  /* int8 expert weights with one fp32 scale per weight row (moe_quantize_rows_i8). Only as
+     moe_layer_args.w_dtype, with bf16 activations, on the decode path. Added in ABI 2. */
+  MOE_I8 = 2
+};
 
 enum moe_scoring {
   /* ZONOS2 (zonos2.cpp INTERNALS, "Model architecture", Router row): rank experts by logit
@@ -199,7 +205,23 @@ typedef struct moe_layer_args {
      others, and all five while the stream is being captured, are event records enqueued at the
      stage boundary (external event nodes, hipEventRecordExternal, during capture). */
   void* const* prof_events;
+  /* ABI 2. w_dtype = 0, or a struct_size that ends before w_dtype (MOE_LAYER_ARGS_V1_SIZE),
+     means the expert weights have the activation dtype (as does w_dtype = dtype).
+     w_dtype = MOE_I8: w_gate, w_up and w_down hold int8 codes in the same [E,H,d] / [E,d,H]
+     layouts, and the scale arrays hold their fp32 row scales ([E,H], [E,H], [E,d]) as written
+     by moe_quantize_rows_i8; the layer computes with the weights scale * code. This quantised
+     decode path (bytes per weight halved: the pages run quantised expert stacks for decode,
+     ZONOS2-4bit MLX card, "Performance notes"; zonos2.cpp INTERNALS, "Recommended: F16 spine +
+     K-quant experts") needs dtype = MOE_BF16 and the weight-streaming regime (T*k <= 2048,
+     T*k <= 32*E, d and H multiples of 256): anything else returns MOE_ERR_UNSUPPORTED. Missing
+     scales: MOE_ERR_NULL. Scales must be 16-byte aligned. */
+  int32_t w_dtype;
+  const float* w_gate_scale;  /* [E, H] */
+  const float* w_up_scale;    /* [E, H] */
+  const float* w_down_scale;  /* [E, d] */
 } moe_layer_args;
+
+#define MOE_LAYER_ARGS_V1_SIZE offsetof(moe_layer_args, w_dtype)
 
 #define MOE_PROF_EVENTS 5
 
@@ -211,6 +233,21 @@ typedef struct moe_layer_args {
  * matmul where that stays deterministic (k <= 2). ws must hold moe_workspace_size(...) bytes.
  */
 int moe_layer_forward(const moe_layer_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Symmetric per-row int8 codes of a row-major [rows, K] weight matrix (an expert stack is
+ * rows = E * N rows of length K): for each row r,
+ *   scales[r] = fp32(max_i |w[r,i]| / 127)                       (one IEEE round-to-nearest-even
+ *   q[r,i]    = clamp(rint(fp32(w[r,i] / scales[r])), -127, 127)    division each; rint = ties to
+ *                                                                   even)
+ * and an all-zero row gets scale 0 and codes 0. Codes and scales are defined exactly by these
+ * fp32 operations. w: device, dtype MOE_BF16 or MOE_F32; q: device int8 [rows, K]; scales: device
+ * fp32 [rows]. 1 <= K, K % 16 == 0; rows >= 0 (0 is a no-op); pointers 16-byte aligned. Non-finite
+ * weights are outside the contract. Asynchronous on `stream`, capturable, allocates nothing.
+ * Added in ABI 2.
+ */
+int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* q, float* scales,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ MISALIGNED = ctypes.c_void_p(0x100004)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_bound_entry_points():
@@ -133,6 +133,41 @@ def test_layer_forward_validation():
     assert run(_args(logits=MISALIGNED.value)) == moe.MOE_ERR_SHAPE
     assert run(_args(), n=ws - 256) == moe.MOE_ERR_WORKSPACE
     assert run(_args(), w=None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_layer_int8_weight_validation():
+    L = moe.LIB
+    # a decode shape of the weight-streaming path (d, H multiples of 256, few rows per expert)
+    T, d, E, H = 16, 256, 8, 256
+    ws = L.moe_workspace_size(T, d, E, H, 1, 1)
+    run = lambda a, n=ws: L.moe_layer_forward(ctypes.byref(a), FAKE, n, None)
+    q8 = dict(T=T, d=d, E=E, H=H, w_dtype=moe.MOE_I8, w_gate_scale=FAKE.value,
+              w_up_scale=FAKE.value, w_down_scale=FAKE.value)
+    assert run(_args(**{**q8, "T": 0})) == moe.MOE_OK
+    assert run(_args(**{**q8, "w_up_scale": None})) == moe.MOE_ERR_NULL
+    assert run(_args(**{**q8, "w_down_scale": MISALIGNED.value})) == moe.MOE_ERR_SHAPE
+    assert run(_args(**{**q8, "dtype": 0})) == moe.MOE_ERR_UNSUPPORTED          # fp32 activations
+    assert run(_args(**{**q8, "d": 128, "H": 128})) == moe.MOE_ERR_UNSUPPORTED  # not streaming
+    assert run(_args(**{**q8, "T": 2048, "k": 2}), n=1 << 40) == moe.MOE_ERR_UNSUPPORTED  # prefill
+    assert run(_args(**{**q8, "w_dtype": 7})) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(**{**q8, "w_dtype": 0}), n=0) == moe.MOE_ERR_WORKSPACE      # 0: weights in dtype
+    # the ABI-1 layout (no w_dtype field) is still accepted, and means weights in dtype
+    assert run(_args(**{**q8, "struct_size": moe.MoeLayerArgs.w_dtype.offset}), n=0) == \
+        moe.MOE_ERR_WORKSPACE
+    assert run(_args(struct_size=moe.MoeLayerArgs.w_dtype.offset - 4)) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_quantize_validation():
+    L = moe.LIB
+    q = lambda w=FAKE, rows=4, K=64, dt=1, qq=FAKE, s=FAKE: L.moe_quantize_rows_i8(w, rows, K, dt, qq, s, None)
+    assert q(rows=0) == moe.MOE_OK
+    assert q(rows=-1) == moe.MOE_ERR_SHAPE
+    assert q(K=0) == moe.MOE_ERR_SHAPE
+    assert q(K=40) == moe.MOE_ERR_SHAPE
+    assert q(dt=2) == moe.MOE_ERR_UNSUPPORTED
+    assert q(w=None) == moe.MOE_ERR_NULL
+    assert q(s=None) == moe.MOE_ERR_NULL
+    assert q(qq=MISALIGNED) == moe.MOE_ERR_SHAPE
 
 
 def test_binding_checks_shapes_before_calling():
