@@ -129,22 +129,17 @@ def route_ref(logits32, sel_bias, k, scoring):
 
 def quantize_rows_i8_ref(w):
     """Per-row symmetric int8 codes of a [..., K] weight stack: q (int8, same shape) and s (fp32,
-    shape [...]). The scale and the quotient are fp32 operations (numpy float32 division is the
-    IEEE round-to-nearest-even quotient), the rounding is to nearest with ties to even."""
+    shape [...]). The scale and the quotient are fp32 operations (numpy float32 array division is
+    the elementwise IEEE round-to-nearest-even quotient), the rounding is to nearest with ties to
+    even (np.rint)."""
     w32 = np.asarray(w, dtype=np.float32)
-    rows = w32.reshape(-1, w32.shape[-1])
-    q = np.zeros(rows.shape, dtype=np.int8)
-    s = np.zeros(rows.shape[0], dtype=np.float32)
-    for r in range(rows.shape[0]):
-        m = np.float32(np.max(np.abs(rows[r]))) if rows.shape[1] else np.float32(0)
-        if m == 0:
-            continue
-        sc = np.float32(m / np.float32(127))
-        s[r] = sc
-        for i in range(rows.shape[1]):
-            v = np.rint(np.float32(rows[r, i] / sc))
-            q[r, i] = int(min(127.0, max(-127.0, float(v))))
-    return q.reshape(w32.shape), s.reshape(w32.shape[:-1])
+    m = np.max(np.abs(w32), axis=-1)                       # exact
+    s = np.where(m > 0, m / np.float32(127), np.float32(0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    quot = (w32 / safe[..., None]).astype(np.float32)
+    q = np.clip(np.rint(quot), -127, 127)
+    q = np.where(s[..., None] > 0, q, 0).astype(np.int8)
+    return q, s
 
 
 def dequantize_rows_ref(q, s):
