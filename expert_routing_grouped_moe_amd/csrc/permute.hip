@@ -9,8 +9,8 @@
 //   row_pos[r]      inverse of sorted_rows
 //
 // One block per expert, no inter-block communication, the same result on every call:
-//  pass 1  every block histograms all T*k ids in LDS (integer atomics, order-free) and so knows
-//          offsets[e] for its own expert;
+//  pass 1  every block counts, over all T*k ids, those below its expert (= offsets[e]) and those
+//          equal to it (= counts[e]): plain compares and a block reduction, no atomics;
 //  pass 2  thread i owns a contiguous run of rows (runs in thread order = rows in ascending
 //          order); a block-wide exclusive scan of the per-thread match counts places each of the
 //          block's rows, which it writes to sorted_rows and row_pos.
@@ -33,40 +33,99 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_rows, int32_t* __restrict__ row_pos,
     int32_t* __restrict__ counts_out) {
-  __shared__ int hist[kMaxE];
   __shared__ int wsum[kDispWaves];
+  __shared__ int wless[kDispWaves];
   __shared__ int s_base;
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
 
-  for (int i = tid; i < E; i += kDispThreads) hist[i] = 0;
-  __syncthreads();
-  // pass 1: histogram of all rows
+  if (n <= kRound) {
+    // one round: the ids are read once, and one barrier serves both the counts and the scan
+    int v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = tid * kPer + i;
+      v[i] = r < n ? clamp_id(ids[r], E) : E;
+    }
+    int less = 0, mine = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      less += v[i] < e;
+      mine += v[i] == e;
+    }
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) less += __shfl_xor(less, o);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    if (lane == 0) wless[wave] = less;
+    __syncthreads();
+    int base = 0, before = 0, total = 0;
+    for (int w = 0; w < kDispWaves; ++w) {
+      const int t = wsum[w];
+      base += wless[w];
+      if (w < wave) before += t;
+      total += t;
+    }
+    if (tid == 0) {
+      offsets[e] = base;
+      if (counts_out) counts_out[e] = total;
+      if (e == E - 1) offsets[E] = n;
+    }
+    int p = base + before + incl - mine;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (v[i] == e) {
+        const int r = tid * kPer + i;
+        sorted_rows[p] = r;
+        row_pos[r] = p;
+        ++p;
+      }
+    }
+    return;
+  }
+
+  // pass 1: rows with a smaller expert id, and rows of this expert
+  int less = 0, mine_all = 0;
   for (int base = 0; base < n; base += kRound) {
     int v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int r = base + tid * kPer + i;
-      v[i] = r < n ? ids[r] : -1;
+      v[i] = r < n ? clamp_id(ids[r], E) : E;   // past the end: counts nowhere
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (base + tid * kPer + i < n) atomicAdd(&hist[clamp_id(v[i], E)], 1);
+    for (int i = 0; i < kPer; ++i) {
+      less += v[i] < e;
+      mine_all += v[i] == e;
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    less += __shfl_xor(less, o);
+    mine_all += __shfl_xor(mine_all, o);
+  }
+  if (lane == 0) {
+    wless[wave] = less;
+    wsum[wave] = mine_all;
   }
   __syncthreads();
-  if (wave == 0) {
-    int s = 0;
-    for (int i = lane; i < e; i += kWave) s += hist[i];
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) {
-      s_base = s;
-      offsets[e] = s;
-      if (counts_out) counts_out[e] = hist[e];
-      if (e == E - 1) offsets[E] = n;
+  if (tid == 0) {
+    int tl = 0, tm = 0;
+    for (int w = 0; w < kDispWaves; ++w) {
+      tl += wless[w];
+      tm += wsum[w];
     }
+    s_base = tl;
+    offsets[e] = tl;
+    if (counts_out) counts_out[e] = tm;
+    if (e == E - 1) offsets[E] = n;
   }
   __syncthreads();
   // pass 2: stable placement of this expert's rows

@@ -36,6 +36,7 @@ def test_router_logits_within_bound(name):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (64, 8, 1), (64, 64, 2), (1000, 16, 1), (8192, 16, 1),
+                                   (6000, 16, 2), (20000, 8, 1),
                                    (4096, 64, 2), (333, 256, 8), (3000, 5, 3)])
 def test_permute_bit_exact(T, E, k):
     import torch
