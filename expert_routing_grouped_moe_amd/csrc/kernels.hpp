@@ -79,6 +79,17 @@ hipError_t launch_logits_bf16(const uint16_t* x, const uint16_t* wr, const float
 hipError_t launch_route_from_logits(const float* logits, const float* sel_bias, int T, int E,
                                     int k, int scoring, const RouteOut& o, hipStream_t s);
 
+// Small batches (T <= kRouteSplitMaxT) with a large router matrix route in two kernels: partial
+// logit tiles over d-slices spread across many CUs, then the sum and the selection.
+// route_split_ks() is the number of slices (0: the fused router is used); `part` holds
+// ks * T * E floats.
+constexpr int kRouteSplitMaxT = 256;
+int route_split_ks(int T, int d, int E);
+hipError_t launch_route_split_bf16(const uint16_t* x, const uint16_t* wr, const float* rb,
+                                   const float* sel_bias, int T, int d, int E, int k, int scoring,
+                                   float* logits_out, float* part, const RouteOut& o,
+                                   hipStream_t s);
+
 // logits on MFMA + top-k + weights in one kernel (bf16 x / router weight); logits_out optional.
 hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const float* rb,
                                    const float* sel_bias, int T, int d, int E, int k, int scoring,

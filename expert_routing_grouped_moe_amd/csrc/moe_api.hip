@@ -46,7 +46,7 @@ int check_scoring(int scoring, const float* sel_bias) {
 
 // Device workspace regions of the fused layer (the step calls use a subset).
 struct Layout {
-  size_t h, logits, ids, w, counts, offsets, sorted_rows, row_pos, eo, total;
+  size_t h, logits, ids, w, counts, offsets, sorted_rows, row_pos, eo, rpart, total;
   Layout(int T, int d, int E, int H, int k, int dtype) {
     const size_t rows = static_cast<size_t>(T) * k;
     size_t o = 0;
@@ -62,6 +62,9 @@ struct Layout {
     // streaming (decode) path, where the down epilogue would otherwise issue T*k*d atomic adds
     const bool stage = k > 2 || (k == 2 && !(dtype == MOE_BF16 && moe::ffn_bf16_streaming(T, d, E, H, k)));
     eo = o;          o += stage ? up(rows * d * 4) : 0;
+    // partial logit tiles of the split router (bf16, small batches)
+    const int rks = dtype == MOE_BF16 ? moe::route_split_ks(T, d, E) : 0;
+    rpart = o;       o += up(static_cast<size_t>(rks) * T * E * 4);
     total = o;
   }
 };
@@ -298,9 +301,15 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   const RouteOut ro{ids, w, nullptr, zero_y, d};
   MOE_TRY(mark(0));
   if (dtype == MOE_BF16) {
-    MOE_TRY(moe::launch_route_fused_bf16(
-        static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_router),
-        a->router_bias, a->sel_bias, T, d, E, k, a->scoring, a->logits, ro, s));
+    if (moe::route_split_ks(T, d, E) > 0)
+      MOE_TRY(moe::launch_route_split_bf16(
+          static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_router),
+          a->router_bias, a->sel_bias, T, d, E, k, a->scoring, a->logits, at<float>(ws, lay.rpart),
+          ro, s));
+    else
+      MOE_TRY(moe::launch_route_fused_bf16(
+          static_cast<const uint16_t*>(a->x), static_cast<const uint16_t*>(a->w_router),
+          a->router_bias, a->sel_bias, T, d, E, k, a->scoring, a->logits, ro, s));
   } else {
     float* logits = a->logits ? a->logits : at<float>(ws, lay.logits);
     MOE_TRY(moe::launch_logits_f32(static_cast<const float*>(a->x),

@@ -335,6 +335,87 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
   route_tail<L>(part, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
 }
 
+// ---------------------------------------------------------------- split router (small T)
+// With few tokens the fused kernel runs on only T/16 CUs, each pulling all router weights. The
+// split router spreads the logit tile instead: kernel A, one wave per (16 tokens, 16 experts,
+// d-slice), writes partial 16 x 16 tiles (each wave issues all its loads at once); kernel B, one
+// block per 16 tokens, adds the slices in slice order, adds the router bias and selects.
+
+__global__ __launch_bounds__(kWave) void logit_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    int slice, float* __restrict__ part) {
+  const int t0 = blockIdx.x * kTokTile, e0 = blockIdx.y * 16, ks = blockIdx.z;
+  const int kbeg = ks * slice, kend = min(d, kbeg + slice);
+  const int lane = lane_id();
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  // rows past T or E read a valid row; their products are never stored
+  const uint16_t* xrow = x + static_cast<long long>(min(t0 + r16, T - 1)) * d;
+  const uint16_t* wrow = wr + static_cast<long long>(min(e0 + r16, E - 1)) * d;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kbeg; k0 < kend; k0 += 32 * kBatch) {
+    u32x4 a[kBatch], b[kBatch];
+#pragma unroll
+    for (int st = 0; st < kBatch; ++st) {
+      const int kk = k0 + 32 * st + kq;  // kend - kk is a multiple of 8: kk < kend -> 8 in range
+      const bool ok = kk < kend;
+      a[st] = ok ? load16(xrow + kk) : u32x4{0u, 0u, 0u, 0u};
+      b[st] = ok ? load16(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int st = 0; st < kBatch; ++st) acc = mfma16x16x32(a[st], b[st], acc);
+  }
+  const int e = e0 + r16;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + (lane >> 4) * 4 + r;
+    if (t < T && e < E) part[(static_cast<long long>(ks) * T + t) * E + e] = acc[r];
+  }
+}
+
+constexpr int kPartThreads = 1024;
+constexpr int kMaxSlices = 16;
+
+template <int L>
+__global__ __launch_bounds__(kPartThreads) void route_from_partials_kernel(
+    const float* __restrict__ part, int nks, const float* __restrict__ rb,
+    const float* __restrict__ sel_bias, int T, int E, int k, int scoring,
+    float* __restrict__ logits_out, RouteOut o) {
+  extern __shared__ float smem[];
+  const int ld = E + 1;
+  float* tile = smem;                              // [16][E+1]
+  float* sbias = tile + kTokTile * ld;             // [E]
+  int* hist = reinterpret_cast<int*>(sbias + E);   // [E]
+  const int t0 = blockIdx.x * kTokTile;
+  for (int i = threadIdx.x; i < kTokTile * E; i += blockDim.x) {
+    const int tl = i / E, e = i % E;
+    const int t = min(t0 + tl, T - 1);
+    // every slice's partial is loaded before the sum (fixed order: slice 0, 1, ..., then the
+    // router bias, one more fp32 rounding)
+    float p[kMaxSlices];
+#pragma unroll
+    for (int ks = 0; ks < kMaxSlices; ++ks)
+      p[ks] = ks < nks ? part[(static_cast<long long>(ks) * T + t) * E + e] : 0.f;
+    float v = p[0];
+#pragma unroll
+    for (int ks = 1; ks < kMaxSlices; ++ks)
+      if (ks < nks) v += p[ks];
+    if (rb) v = v + rb[e];
+    if (t0 + tl < T) {
+      if (logits_out) logits_out[static_cast<long long>(t) * E + e] = v;
+    } else {
+      v = 0.f;
+    }
+    tile[tl * ld + e] = v;
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    if (sel_bias) sbias[e] = sel_bias[e];
+    hist[e] = 0;
+  }
+  __syncthreads();
+  route_tail<L>(tile, ld, sel_bias ? sbias : nullptr, t0, T, E, k, scoring, o, hist);
+}
+
 // fp32 router logits: one thread per (token, expert), four interleaved partial sums.
 __global__ void logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr,
                                   const float* __restrict__ rb, int T, int d, int E,
@@ -435,6 +516,46 @@ hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const 
       x, wr, rb, sel_bias, T, d, E, k, scoring, logits_out, o)
   MOE_ROUTE_DISPATCH_L(E, MOE_LAUNCH_FUSED)
 #undef MOE_LAUNCH_FUSED
+  return hipGetLastError();
+}
+
+int route_split_slice(int d) {
+  // 256-wide slices (8 MFMA steps, one batch of loads per lane), wider for d > 4096 so that at
+  // most 16 slices exist; always a multiple of 64
+  int slice = 256;
+  while ((d + slice - 1) / slice > kMaxSlices) slice += 64;
+  return slice;
+}
+
+int route_split_ks(int T, int d, int E) {
+  // worth a second launch only when every fused block would pull a large router matrix
+  // (>= 128 KB of bf16: 64 experts x 1024 measured 9.4 us split against 11.7 us fused; 16 x 2048
+  // measured 8.7 us split against 7.4 us fused)
+  if (T > kRouteSplitMaxT || static_cast<long long>(E) * d < 65536) return 0;
+  const int slice = route_split_slice(d);
+  return (d + slice - 1) / slice;
+}
+
+hipError_t launch_route_split_bf16(const uint16_t* x, const uint16_t* wr, const float* rb,
+                                   const float* sel_bias, int T, int d, int E, int k, int scoring,
+                                   float* logits_out, float* part, const RouteOut& o,
+                                   hipStream_t s) {
+  const int blocks = (T + kTokTile - 1) / kTokTile;
+  if (o.counts && blocks > 1) {
+    hipError_t err = launch_zero_i32(o.counts, E, s);
+    if (err != hipSuccess) return err;
+  }
+  const int slice = route_split_slice(d);
+  const int nks = (d + slice - 1) / slice;
+  logit_partial_kernel<<<dim3(blocks, (E + 15) / 16, nks), kWave, 0, s>>>(x, wr, T, d, E, slice,
+                                                                           part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+#define MOE_LAUNCH_PART(L)                                                                    \
+  route_from_partials_kernel<L><<<blocks, kPartThreads, tail_smem(E), s>>>(                   \
+      part, nks, rb, sel_bias, T, E, k, scoring, logits_out, o)
+  MOE_ROUTE_DISPATCH_L(E, MOE_LAUNCH_PART)
+#undef MOE_LAUNCH_PART
   return hipGetLastError();
 }
 

@@ -63,6 +63,10 @@ EDGE = [
     ("stream-E256-k8", 64, 256, 256, 8, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
     ("stream-hot-expert", 200, 128, 16, 1, 128, orc.SOFTMAX, "bf16", None, "hot5"),
     ("stream-max-rows", 1024, 128, 64, 2, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    # the split router (few tokens, router matrix >= 64K elements): ragged T, and d wide enough
+    # for slices wider than 256
+    ("split-router-ragged", 37, 1024, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("split-router-wide-d", 20, 4608, 16, 1, 256, orc.SOFTMAX, "bf16", None, None),
     # sigmoid scoring on the three expert-kernel families
     ("sigmoid-stream", 64, 512, 16, 2, 512, orc.SIGMOID, "bf16", None, None),
     ("sigmoid-prefill", 700, 256, 8, 2, 256, orc.SIGMOID, "bf16", None, None),
