@@ -15,6 +15,8 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
+MOE_ABI_VERSION = 2  # include/moe.h; the library must report the same value
+
 MOE_OK = 0
 MOE_ERR_NULL = -1
 MOE_ERR_SHAPE = -2
@@ -94,6 +96,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_rows_i8.restype = c_int
     lib.moe_quantize_rows_i8.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
                                          c_void_p, c_void_p]
+    if lib.moe_abi_version() != MOE_ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH} reports ABI {lib.moe_abi_version()}, the binding expects "
+                          f"{MOE_ABI_VERSION}; rebuild the library")
     return lib
 
 

@@ -32,7 +32,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 2 == moe.MOE_ABI_VERSION
+    hdr = re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read())
+    assert hdr and int(hdr.group(1)) == moe.MOE_ABI_VERSION
     for st in (0, -1, -2, -3, -4, -5):
         assert moe.moe_status_string(st) and moe.moe_status_string(st) != "unknown status"
     assert moe.moe_status_string(7) == "unknown status"
