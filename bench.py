@@ -339,7 +339,7 @@ def main():
         maxg = 2 if (H // 16) * E <= 2048 else 1
         roof["kernel"] = "ffn_stream_kernel<true, %d, %s>" % (maxg, "true" if int8 else "false")
     else:
-        roof["kernel"] = ("gemm_dma_kernel<true, 256, 128>" if inp.dtype == "bf16"
+        roof["kernel"] = ("gemm_dma_kernel<true, 256, 128, 3, 64>" if inp.dtype == "bf16"
                           else "ffn_f32_kernel<true>")
     traffic = measured_traffic(roof["kernel"], args.workload + ("/int8" if int8 else ""))
     roof["traffic"] = traffic

@@ -57,6 +57,8 @@ EDGE = [
     ("E256-k8", 64, 128, 256, 8, 64, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
     ("all-one-expert", 500, 128, 16, 1, 256, orc.SOFTMAX, "bf16", None, "hot5"),
     ("prefill-ragged", 1111, 192, 8, 2, 320, orc.SOFTMAX, "bf16", None, None),
+    # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
+    ("prefill-xcd-hot-expert", 2000, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
     # few rows per expert with d, H multiples of 128: the weight-streaming expert kernels
     ("stream-k3", 40, 128, 16, 3, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
