@@ -36,6 +36,13 @@ quantised expert stacks, "Performance notes" / "Recommended: F16 spine + K-quant
 weight row (one output feature of one expert) is quantised symmetrically to int8,
   s = fl32(max_i |w_i| / 127),   q_i = clamp(rint(fl32(w_i / s)), -127, 127)   (ties to even),
 an all-zero row getting s = 0, q = 0; the layer then uses the weights s * q exactly.
+The 4-bit form follows the same card's recipe for the experts (affine, 4 bits, groups of 64 along
+the reduction index, ZONOS2-4bit card, "Quantization recipe"). The pages name the scheme but do not
+spell out its arithmetic; the reading taken is the plain affine one, with the scale and bias kept as
+bf16 (the model's dtype):
+  lo, hi = min, max of the group;  s = bf16(fl32(fl32(hi - lo) / 15));  b = bf16(lo);
+  q_i = clamp(rint(fl32(fl32(w_i - b) / s)), 0, 15)   (ties to even; s = 0 gives q = 0),
+and the layer computes with the weights s * q + b exactly. bf16() is round-to-nearest-even.
 
 Pins (checked by the CPU tests against values the mathematics fixes, not against this code):
 brute-force selection, closed-form softmax weights, exact fp32 rounding cases, dispatch
@@ -145,6 +152,67 @@ def quantize_rows_i8_ref(w):
 def dequantize_rows_ref(q, s):
     """The weights the int8 layer computes with: s * q per row, exactly (fp64)."""
     return np.asarray(q, dtype=f64) * np.asarray(s, dtype=f64)[..., None]
+
+
+def bf16_round_ref(v):
+    """fp32 values rounded to the nearest bf16 (ties to even), returned as fp32."""
+    bits = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return (rounded.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_groups_q4_ref(w, group=64):
+    """4-bit affine codes of a [..., K] weight stack, groups of `group` along K: q (uint8, values
+    0..15, same shape), s and b (fp32 holding bf16 values, shape [..., K / group]). Every step is
+    the fp32 (or bf16) operation named in the module docstring, applied to whole arrays."""
+    w32 = np.asarray(w, dtype=np.float32)
+    K = w32.shape[-1]
+    assert K % group == 0
+    g = w32.reshape(w32.shape[:-1] + (K // group, group))
+    lo = g.min(axis=-1)
+    hi = g.max(axis=-1)
+    span = (hi - lo).astype(np.float32)
+    s = bf16_round_ref((span / np.float32(15)).astype(np.float32))
+    b = bf16_round_ref(lo)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    diff = (g - b[..., None]).astype(np.float32)
+    quot = (diff / safe[..., None]).astype(np.float32)
+    q = np.clip(np.rint(quot), 0, 15)
+    q = np.where(s[..., None] > 0, q, 0).astype(np.uint8)
+    return q.reshape(w32.shape), s, b
+
+
+def pack_q4_ref(q):
+    """The library's storage order of 4-bit codes ([..., K] values 0..15, K a multiple of 128)
+    as bytes [..., K / 2]: block j of 128 k holds 64 bytes; bytes 16 g .. 16 g + 15 of it are
+    four little-endian dwords c = 0..3, dword c holding k = 128 j + 32 c + 8 g + i (i = 0..7) with
+    i = 2 m in bits 4 m .. 4 m + 3 and i = 2 m + 1 in bits 16 + 4 m .. 19 + 4 m."""
+    q = np.asarray(q, dtype=np.uint32)
+    K = q.shape[-1]
+    assert K % 128 == 0
+    # [..., j, c, g, i] -> [..., j, g, c, i]
+    v = q.reshape(q.shape[:-1] + (K // 128, 4, 4, 8)).swapaxes(-3, -2)
+    dw = np.zeros(v.shape[:-1], dtype=np.uint32)
+    for m in range(4):
+        dw |= v[..., 2 * m] << np.uint32(4 * m)
+        dw |= v[..., 2 * m + 1] << np.uint32(16 + 4 * m)
+    return dw.astype("<u4").view(np.uint8).reshape(q.shape[:-1] + (K // 2,))
+
+
+def pack_q4_params_ref(s, b):
+    """Per-group (scale, bias) as one uint32: bf16 bits of s in the low half, of b in the high."""
+    sb = np.asarray(s, dtype=np.float32).view(np.uint32) >> np.uint32(16)
+    bb = np.asarray(b, dtype=np.float32).view(np.uint32) >> np.uint32(16)
+    return (sb | (bb << np.uint32(16))).astype(np.uint32)
+
+
+def dequantize_groups_q4_ref(q, s, b, group=64):
+    """The weights the 4-bit layer computes with: s * q + b per group, exactly (fp64)."""
+    q64 = np.asarray(q, dtype=f64)
+    K = q64.shape[-1]
+    g = q64.reshape(q64.shape[:-1] + (K // group, group))
+    out = g * np.asarray(s, dtype=f64)[..., None] + np.asarray(b, dtype=f64)[..., None]
+    return out.reshape(q64.shape)
 
 
 # ------------------------------------------------------------------------------ dispatch (step 5)

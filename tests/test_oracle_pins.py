@@ -76,6 +76,39 @@ def test_hand_int8_quantisation(hand):
         assert float(s[i]) == _ev(row["s"])
 
 
+def _q4_hand_row(c):
+    """One weight row of the 4-bit hand case: each group is its head values, then its fill."""
+    row = []
+    for g in c["groups"]:
+        vals = [_ev(v) for v in g["head"]]
+        row += vals + [_ev(g["fill"])] * (64 - len(vals))
+    return np.array(row, dtype=np.float32)[None, :]
+
+
+def test_hand_q4_groups(hand):
+    c = hand["q4_affine_groups"]
+    q, s, b = orc.quantize_groups_q4_ref(_q4_hand_row(c))
+    for i, g in enumerate(c["groups"]):
+        codes = q[0, 64 * i:64 * (i + 1)].tolist()
+        n = len(g["head"])
+        assert codes[:n] == g["q_head"], (i, codes[:n])
+        assert all(v == g["q_fill"] for v in codes[n:]), i
+        assert float(s[0, i]) == _ev(g["s"]) and float(b[0, i]) == _ev(g["b"]), i
+
+
+def test_hand_q4_packing(hand):
+    c = hand["q4_affine_groups"]["packing"]
+    q = (np.arange(128) % 16).astype(np.uint8)[None, :]
+    packed = orc.pack_q4_ref(q)
+    assert packed.shape == (1, 64) and packed.dtype == np.uint8
+    for off, want in c["bytes_at"].items():
+        o = int(off)
+        assert packed[0, o:o + 4].tolist() == want, off
+    # every code appears exactly once in the packed row
+    nib = np.concatenate([packed[0] & 15, packed[0] >> 4])
+    assert sorted(nib.tolist()) == sorted(q[0].tolist())
+
+
 def test_hand_fp32_rank_add(hand):
     c = hand["fp32_rank_add"]
     L32 = _arr(c["logits"])[None, :].astype(np.float32)
@@ -227,6 +260,61 @@ def test_int8_quantisation_invariants():
     q2, s2 = orc.quantize_rows_i8_ref(Wexact)
     assert (s2 == np.float32(2.0 ** -5)).all()
     np.testing.assert_array_equal(q2.astype(np.float32), qi)
+
+
+def test_q4_quantisation_invariants():
+    rng = np.random.default_rng(13)
+    W = gen.bf16_bits_to_f32(gen.bf16_round_bits(
+        (rng.standard_normal((3, 8, 256)) * 0.05).astype(np.float32)))
+    W[1, 2, 64:128] = 0.125                               # a constant group
+    q, s, b = orc.quantize_groups_q4_ref(W)
+    assert q.dtype == np.uint8 and q.shape == W.shape and s.shape == b.shape == (3, 8, 4)
+    assert q.max() <= 15
+    assert s[1, 2, 1] == 0 and b[1, 2, 1] == np.float32(0.125) and (q[1, 2, 64:128] == 0).all()
+    # scale and bias are bf16 values
+    for v in (s, b):
+        assert (v.view(np.uint32) & 0xFFFF == 0).all()
+    g = W.reshape(3, 8, 4, 64).astype(np.float64)
+    lo, hi = g.min(-1), g.max(-1)
+    s64, b64 = s.astype(np.float64), b.astype(np.float64)
+    # s and b are within a bf16 rounding (2^-8 relative: 8 significant bits) of (hi - lo) / 15
+    # (itself one binary32 rounding away) and of lo
+    assert (np.abs(s64 - (hi - lo) / 15) <= 2.0 ** -8 * (hi - lo) / 15 * 1.0001 + 1e-30).all()
+    assert (np.abs(b64 - lo) <= 2.0 ** -8 * np.abs(lo)).all()
+    err = np.abs(g - orc.dequantize_groups_q4_ref(q, s, b).reshape(g.shape))
+    bound = s64 / 2 + 15 * np.abs(s64 - (hi - lo) / 15) + np.abs(b64 - lo) + 2.0 ** -20 * (np.abs(lo) + np.abs(hi))
+    assert (err <= bound[..., None]).all()
+    # groups that are already s * q + b (s a power of two, b a bf16 value, codes spanning 0..15)
+    # come back unchanged
+    qi = rng.integers(0, 16, size=(16, 256))
+    qi[:, ::64] = 0
+    qi[:, 1::64] = 15
+    bb = gen.bf16_bits_to_f32(gen.bf16_round_bits(rng.standard_normal((16, 4)).astype(np.float32)))
+    Wexact = (qi.reshape(16, 4, 64) * np.float32(2.0 ** -6) + bb[..., None]).reshape(16, 256).astype(np.float32)
+    q2, s2, b2 = orc.quantize_groups_q4_ref(Wexact)
+    assert (s2 == np.float32(2.0 ** -6)).all() and (b2 == bb).all()
+    np.testing.assert_array_equal(q2, qi)
+
+
+def test_q4_layer_on_exact_weights_equals_plain_layer():
+    # weights that are exactly s * q + b: the 4-bit layer is the plain layer on the same weights
+    inp = _case(T=16, d=128, E=4, k=2, H=128, scoring=orc.SOFTMAX, seed=15)
+    rng = np.random.default_rng(15)
+    for key in ("w_gate", "w_up", "w_down"):
+        a = getattr(inp, key)
+        K = a.shape[-1]
+        qi = rng.integers(0, 16, size=a.shape)
+        qi[..., ::64] = 0
+        qi[..., 1::64] = 15
+        bb = rng.integers(-64, 64, size=a.shape[:-1] + (K // 64,)).astype(np.float32) * np.float32(2.0 ** -9)
+        w = qi.reshape(a.shape[:-1] + (K // 64, 64)) * np.float32(2.0 ** -9) + bb[..., None]
+        setattr(inp, key, w.reshape(a.shape).astype(np.float32))
+    deq = {key: orc.dequantize_groups_q4_ref(*orc.quantize_groups_q4_ref(getattr(inp, key)))
+           for key in ("w_gate", "w_up", "w_down")}
+    y_q = orc.layer_ref(inp.x, inp.w_router, deq["w_gate"], deq["w_up"], deq["w_down"], inp.k,
+                        inp.scoring)["y"]
+    y = orc.layer_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k, inp.scoring)["y"]
+    np.testing.assert_array_equal(y_q, y)
 
 
 def test_int8_layer_on_exact_weights_equals_bf16_layer():
@@ -421,6 +509,8 @@ def _pins_pass():
         test_hand_selected_softmax(hand)
         test_hand_sigmoid_no_renorm(hand)
         test_hand_int8_quantisation(hand)
+        test_hand_q4_groups(hand)
+        test_hand_q4_packing(hand)
         test_hand_fp32_rank_add(hand)
         test_hand_swiglu_layer(hand, "swiglu_one_expert")
         test_hand_swiglu_layer(hand, "swiglu_two_experts_top1")
@@ -429,6 +519,7 @@ def _pins_pass():
         test_selected_softmax_weight_invariants()
         test_sigmoid_weight_invariants()
         test_int8_quantisation_invariants()
+        test_q4_quantisation_invariants()
         test_permute_invariants(64, 64, 2)
         test_layer_equals_dense_bruteforce(orc.SELECTED_SOFTMAX, 2, False, True)
         test_single_expert_is_dense_swiglu_torch()
@@ -474,6 +565,32 @@ MUTATIONS = {
     "q8_scale_128": ("quantize_rows_i8_ref", lambda orig: (lambda w: (lambda q, s: (
         np.clip(np.rint(np.asarray(w, np.float32) / np.where(s == 0, 1, s * np.float32(128 / 127))[..., None]),
                 -127, 127).astype(np.int8), (s * np.float32(128 / 127)).astype(np.float32)))(*orig(w)))),
+    # 4-bit codes rounded half away from zero (all codes are >= 0 here)
+    "q4_half_away": ("quantize_groups_q4_ref", lambda orig: (lambda w, group=64: (lambda q, s, b: (
+        np.where(s.repeat(group, -1) > 0, np.clip(np.floor(
+            ((np.asarray(w, np.float32) - b.repeat(group, -1)) / np.where(s == 0, 1, s).repeat(group, -1)
+             ).astype(np.float32) + 0.5), 0, 15), 0).astype(np.uint8), s, b))(*orig(w, group)))),
+    # scale kept in binary32 instead of rounded to bf16
+    "q4_scale_unrounded": ("quantize_groups_q4_ref", lambda orig: (lambda w, group=64: (
+        lambda g: (lambda lo, hi: (lambda s, b: (
+            np.where(s[..., None] > 0, np.clip(np.rint(((g - b[..., None]) / np.where(s == 0, 1, s)[..., None]
+                                                        ).astype(np.float32)), 0, 15), 0).astype(np.uint8)
+            .reshape(np.shape(w)), s, b))(((hi - lo) / np.float32(15)).astype(np.float32),
+                                          orc.bf16_round_ref(lo)))(g.min(-1), g.max(-1)))(
+        np.asarray(w, np.float32).reshape(np.shape(w)[:-1] + (np.shape(w)[-1] // group, group))))),
+    # scale from (max - min) / 16
+    "q4_scale_16": ("quantize_groups_q4_ref", lambda orig: (lambda w, group=64: (lambda q, s, b: (
+        np.where(s.repeat(group, -1) > 0, np.clip(np.rint(
+            ((np.asarray(w, np.float32) - b.repeat(group, -1)) /
+             np.where(s == 0, 1, orc.bf16_round_ref(s * np.float32(15 / 16))).repeat(group, -1)).astype(np.float32)),
+            0, 15), 0).astype(np.uint8), orc.bf16_round_ref(s * np.float32(15 / 16)), b))(*orig(w, group)))),
+    # bias kept in binary32 instead of rounded to bf16
+    "q4_bias_unrounded": ("quantize_groups_q4_ref", lambda orig: (lambda w, group=64: (lambda q, s, b: (
+        q, s, np.asarray(w, np.float32).reshape(np.shape(w)[:-1] + (np.shape(w)[-1] // group, group)).min(-1)))(
+        *orig(w, group)))),
+    # packed nibbles of odd and even k swapped
+    "q4_pack_swap": ("pack_q4_ref", lambda orig: (lambda q: (lambda p: ((p & 15) << 4 | (p >> 4)).astype(np.uint8))(
+        orig(q)))),
     # rank on the fp64 sum instead of the binary32 add
     "rank_fp64": ("rank_scores_fp32", lambda orig: (lambda L, b=None: np.asarray(L, np.float64) + (
         0 if b is None else np.asarray(b, np.float64)[None, :]))),
