@@ -88,13 +88,16 @@ def _hip():
     return lib
 
 
-def algorithmic(inp, counts, int8_weights=False):
+def algorithmic(inp, counts, weights="native"):
     """Bytes and FLOPs the step must move/do (touched experts only; intermediates excluded).
-    int8 expert weights: one byte per weight plus the fp32 row scales of the touched experts."""
+    int8 expert weights: one byte per weight plus the fp32 row scales of the touched experts;
+    q4: half a byte per weight plus one 4-byte (scale, bias) pair per group of 64."""
     T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
     ab = 2 if inp.dtype == "bf16" else 4             # activations and router weights
-    wb = 1 if int8_weights else ab                   # expert weights
-    sb = 4 if int8_weights else 0                    # one fp32 scale per expert weight row
+    wb = {"int8": 1, "q4": 0.5}.get(weights, ab)     # expert weights
+    sb = 4 if weights == "int8" else 0               # one fp32 scale per expert weight row
+    if weights == "q4":
+        wb += 4 / 64                                 # (scale, bias) pair per group of 64
     touched = int((counts > 0).sum())
     rows = T * k
     step_bytes = (touched * (3 * d * H * wb + (2 * H + d) * sb) + T * d * ab + E * d * ab +
@@ -144,9 +147,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
-    ap.add_argument("--weights", choices=("native", "int8"), default="native",
-                    help="expert weights as given (bf16/fp32) or int8 codes with per-row scales "
-                         "(moe_quantize_rows_i8; decode shapes only)")
+    ap.add_argument("--weights", choices=("native", "int8", "q4"), default="native",
+                    help="expert weights as given (bf16/fp32), int8 codes with per-row scales "
+                         "(moe_quantize_rows_i8) or 4-bit affine codes in groups of 64 "
+                         "(moe_quantize_groups_q4); quantised weights on decode shapes only")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -188,9 +192,10 @@ def main():
     x = up("x")
     wr = up("w_router")
     base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
-    int8 = args.weights == "int8"
-    if int8:
-        qs = {key: moe.moe_quantize_rows_i8(t) for key, t in base.items()}
+    quant = args.weights != "native"
+    if quant:
+        qfn = moe.moe_quantize_rows_i8 if args.weights == "int8" else moe.moe_quantize_groups_q4
+        qs = {key: qfn(t) for key, t in base.items()}
         base = {key: v[0] for key, v in qs.items()}
         base.update({key + "_scale": v[1] for key, v in qs.items()})
         torch.cuda.synchronize()
@@ -219,7 +224,7 @@ def main():
         events.append(evs)
         ev_arrays.append(arr)
         scales = ((copies[c]["w_gate_scale"], copies[c]["w_up_scale"], copies[c]["w_down_scale"])
-                  if int8 else None)
+                  if quant else None)
         a = moe.make_layer_args(x, wr, copies[c]["w_gate"], copies[c]["w_up"],
                                 copies[c]["w_down"], k, inp.scoring, y, rb, sb,
                                 expert_counts=counts, w_scales=scales)
@@ -317,7 +322,7 @@ def main():
     step_ms_ev = [sum(stage_ms[s_][i] for s_ in STAGES) for i in range(len(stage_ms["route"]))]
 
     cnt = counts.cpu().numpy()
-    alg = algorithmic(inp, cnt, int8)
+    alg = algorithmic(inp, cnt, args.weights)
     med = {s: statistics.median(v) for s, v in stage_ms.items()}
     gu_ms = statistics.mean(stage_ms["gate_up"])
     prefill = gen.WORKLOADS[args.workload].shape == "prefill"
@@ -337,11 +342,12 @@ def main():
     # the whole grid stays resident: (H / 16) * E <= 2048 blocks)
     if streaming:
         maxg = 2 if (H // 16) * E <= 2048 else 1
-        roof["kernel"] = "ffn_stream_kernel<true, %d, %s>" % (maxg, "true" if int8 else "false")
+        roof["kernel"] = "ffn_stream_kernel<true, %d, %d>" % (
+            maxg, {"native": 0, "int8": 1, "q4": 2}[args.weights])
     else:
         roof["kernel"] = ("gemm_dma_kernel<true, 256, 128, 3, 64>" if inp.dtype == "bf16"
                           else "ffn_f32_kernel<true>")
-    traffic = measured_traffic(roof["kernel"], args.workload + ("/int8" if int8 else ""))
+    traffic = measured_traffic(roof["kernel"], args.workload + ("/" + args.weights if quant else ""))
     roof["traffic"] = traffic
     roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
                               if traffic is not None else "not measured for the current kernel")
@@ -366,7 +372,9 @@ def main():
         "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "H": H,
                    "scoring": inp.scoring, "seed": gen.WORKLOADS[args.workload].seed,
                    "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
-                   "expert_weights": "int8, fp32 row scales" if int8 else inp.dtype,
+                   "expert_weights": {"int8": "int8, fp32 row scales",
+                                      "q4": "4-bit affine, groups of 64, bf16 scale and bias"
+                                      }.get(args.weights, inp.dtype),
                    "timing": ("host launches" if args.eager else
                               "HIP graph replay, one step per weight copy"),
                    "stage_events": ev_mode, "stage_event_steps": len(step_ms_ev)},

@@ -439,15 +439,162 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   }
 }
 
+// Two 4-bit codes per 16-bit half: bits 4 m and 16 + 4 m of a packed word (see
+// moe_quantize_groups_q4) become the bf16 values 128 + code, exact (8 significant bits), with one
+// shift, one mask and one OR per pair.
+__device__ __forceinline__ u32x4 q4x8_to_bf16x8(uint32_t v) {
+  constexpr uint32_t kMask = 0x000F000Fu, kBase = 0x43004300u;  // bf16 128.0 in both halves
+  return u32x4{(v & kMask) | kBase, ((v >> 4) & kMask) | kBase, ((v >> 8) & kMask) | kBase,
+               ((v >> 12) & kMask) | kBase};
+}
+
+// stream_tile for 4-bit affine weights (groups of 64 along K, one bf16 (scale, bias) pair per
+// group, codes packed so that a lane's 16 bytes of a 128-k block are its four 8-k runs at
+// k = 32 c + 8 g: the bf16 k layout, so each MFMA step lies inside one group).
+// The MFMA sums x * (128 + q) over a group (R) and, against a B operand of ones, x alone (X);
+// with scale s and bias b the group's contribution is s * R + (b - 128 s) * X, folded into the
+// fp32 accumulator in the group's order. Codes are requested kQ4Ahead blocks ahead of use, token
+// rows two blocks ahead; passes, rotation and the epilogue are as in stream_tile.
+constexpr int kQ4Ahead = 2;  // even: a block's token rows sit in slot (block % 2)
+
+template <bool GATEUP, int NG>
+__device__ __forceinline__ void stream_tile_q4(const uint16_t* __restrict__ A,
+                                               const uint8_t* __restrict__ W0,
+                                               const uint8_t* __restrict__ W1,
+                                               const uint32_t* __restrict__ P0,
+                                               const uint32_t* __restrict__ P1, int K, int N,
+                                               int k, int e, const int* lr, int m0, int rows,
+                                               int hbase, uint16_t* __restrict__ h_out,
+                                               const DownArgs& down) {
+  const int lane = lane_id();
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int f = blockIdx.x * kStFeat + l16;  // weight row (N % 16 == 0)
+  const long long row0 = static_cast<long long>(e) * N + f;
+  const uint8_t* pg = W0 + row0 * (K / 2) + 16 * grp;
+  const uint8_t* pu = GATEUP ? W1 + row0 * (K / 2) + 16 * grp : nullptr;
+  const uint32_t* qg = P0 + row0 * (K / 64);
+  const uint32_t* qu = GATEUP ? P1 + row0 * (K / 64) : nullptr;
+  const uint16_t* pa[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int gr = rows - 16 * g;
+    const int li_a = m0 + (gr > 0 ? 16 * g + (l16 < gr ? l16 : 0) : 0);
+    const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
+    pa[g] = A + arow * K + 8 * grp;
+  }
+  const int nb = K / 128;
+  const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
+
+  // codes and (scale, bias) words kQ4Ahead blocks ahead, token rows two blocks ahead (measured:
+  // four or eight blocks of codes ahead cost more in occupancy than they gain in latency)
+  u32x4 a[2][NG][4], cg[kQ4Ahead], cu[kQ4Ahead];
+  uint2 sg[kQ4Ahead], su[kQ4Ahead];           // (scale, bias) words of the block's two groups
+  auto blk = [&](int sq) { return (min(sq, nb - 1) + rot) % nb; };  // past the end: the last block
+  auto load_w = [&](int j, int sq) {
+    const int b = blk(sq);
+    cg[j] = load16(pg + 64 * b);
+    sg[j] = *reinterpret_cast<const uint2*>(qg + 2 * b);
+    if constexpr (GATEUP) {
+      cu[j] = load16(pu + 64 * b);
+      su[j] = *reinterpret_cast<const uint2*>(qu + 2 * b);
+    }
+  };
+  auto load_a = [&](int j, int sq) {
+    const int b = blk(sq);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) a[j][g][c] = load16(pa[g] + 128 * b + 32 * c);
+  };
+  f32x4 accg[NG], accu[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4 ones{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  auto fold = [](f32x4& acc, const f32x4& r, const f32x4& xs, uint32_t pair) {
+    const float sc = __uint_as_float(pair << 16);
+    const float bs = __uint_as_float(pair & 0xffff0000u);
+    const float b2 = fmaf(-128.f, sc, bs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, r[i], fmaf(b2, xs[i], acc[i]));
+  };
+  auto compute = [&](int ja, int jw) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {             // the block's two groups of 64
+      f32x4 rg[NG], ru[NG], xs[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        rg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ru[g] = rg[g];
+        xs[g] = rg[g];
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = 2 * h + cc;
+        const u32x4 wg = q4x8_to_bf16x8(cg[jw][c]);
+        u32x4 wu = wg;
+        if constexpr (GATEUP) wu = q4x8_to_bf16x8(cu[jw][c]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          rg[g] = mfma16x16x32(a[ja][g][c], wg, rg[g]);
+          if constexpr (GATEUP) ru[g] = mfma16x16x32(a[ja][g][c], wu, ru[g]);
+          xs[g] = mfma16x16x32(a[ja][g][c], ones, xs[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        fold(accg[g], rg[g], xs[g], h ? sg[jw].y : sg[jw].x);
+        if constexpr (GATEUP) fold(accu[g], ru[g], xs[g], h ? su[jw].y : su[jw].x);
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kQ4Ahead; ++j) load_w(j, j);
+  load_a(0, 0);
+  load_a(1, 1);
+  for (int b0 = 0; b0 < nb; b0 += kQ4Ahead) {
+#pragma unroll
+    for (int j = 0; j < kQ4Ahead; ++j) {      // block b0 + j: codes in slot j, rows in slot j % 2
+      if (b0 + j < nb) compute(j % 2, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(j, b0 + j + kQ4Ahead);
+      load_a(j % 2, b0 + j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * g + (lane >> 4) * 4 + r;
+      if (i >= rows) continue;
+      const int li = m0 + i;
+      const int hrow = hbase >= 0 ? hbase + li : lr[li];
+      if constexpr (GATEUP) {
+        const float hv = silu(accg[g][r]) * accu[g][r];
+        h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
+      } else {
+        const DownRow dr = down_row(down, lr[li], hrow, N);
+        down_put(down, dr, f, accg[g][r]);
+      }
+    }
+  }
+}
+
 // Grid (N / 16, E), one wave per block: block (x, e) computes features [16 x, 16 x + 16) of
 // expert e for all of the expert's rows, up to 16 MAXG rows per pass over the weights (a further
 // pass mostly hits the caches). MAXG = 2 lets an expert with 17..32 rows, common under a
 // selection bias, read its weights once, at the cost of registers (fewer resident waves).
-// W8: int8 weight codes with fp32 row scales S0 (gate or down) and S1 (up).
-template <bool GATEUP, int MAXG, bool W8>
+// WF (WeightFormat): bf16 weights; int8 codes with fp32 row scales S0 (gate or down) and S1
+// (up); or packed 4-bit codes with (scale, bias) pairs S0 and S1.
+template <bool GATEUP, int MAXG, int WF>
 __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ W0, const void* __restrict__ W1,
-    const float* __restrict__ S0, const float* __restrict__ S1, int K, int N, int k,
+    const void* __restrict__ S0, const void* __restrict__ S1, int K, int N, int k,
     RowSource rs, uint16_t* __restrict__ h_out, DownArgs down) {
   __shared__ int lr[kMaxScanRows];
   const int e = blockIdx.y;
@@ -465,19 +612,36 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
   // passes of up to 16 MAXG rows: the 16-row groups of a pass share each weight load
   for (int m0 = 0; m0 < count; m0 += 16 * MAXG) {
     const int rows = min(16 * MAXG, count - m0);
-    if (MAXG > 1 && rows > 16)
-      stream_tile<GATEUP, MAXG, W8>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase, h_out,
-                                    down);
-    else
-      stream_tile<GATEUP, 1, W8>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
+    if constexpr (WF == kWQ4) {
+      const uint8_t* c0 = static_cast<const uint8_t*>(W0);
+      const uint8_t* c1 = static_cast<const uint8_t*>(W1);
+      const uint32_t* p0 = static_cast<const uint32_t*>(S0);
+      const uint32_t* p1 = static_cast<const uint32_t*>(S1);
+      if (MAXG > 1 && rows > 16)
+        stream_tile_q4<GATEUP, MAXG>(A, c0, c1, p0, p1, K, N, k, e, lr, m0, rows, hbase, h_out,
+                                     down);
+      else
+        stream_tile_q4<GATEUP, 1>(A, c0, c1, p0, p1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
+    } else {
+      constexpr bool W8 = WF == kWI8;
+      const float* s0 = static_cast<const float*>(S0);
+      const float* s1 = static_cast<const float*>(S1);
+      if (MAXG > 1 && rows > 16)
+        stream_tile<GATEUP, MAXG, W8>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase, h_out,
+                                      down);
+      else
+        stream_tile<GATEUP, 1, W8>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase, h_out,
+                                   down);
+    }
   }
 }
 
 }  // namespace
 
-// Prefill tiles: 256 x 128, eight waves of 64 x 64, a 3-slot ring (72 KB, two blocks per CU). Measured on the skewed prefill against 128 x 128 / 256 x 256 tiles, waves
-// of 128 x 64 and deeper rings at one block per CU: all slower, the two co-resident blocks
-// covering each other's barrier and LDS waits matter more than the LDS bytes per product.
+// Prefill tiles: 256 x 128, eight waves of 64 x 64, a 3-slot ring (72 KB, two blocks per CU).
+// Measured on the skewed prefill against 128 x 128 / 256 x 256 tiles, waves of 128 x 64 or
+// 32 x 64, 64-wide K steps and deeper rings at one block per CU: none faster, the two co-resident
+// blocks covering each other's barrier and LDS waits matter more than the LDS bytes per product.
 constexpr int kTileM = 256;
 constexpr int kTileN = 128;
 constexpr int kTileRing = 3;
@@ -488,43 +652,56 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
   return rows <= kMaxScanRows && d % 256 == 0 && H % 256 == 0 && rows <= 32ll * E;
 }
 
+namespace {
+
+// Gate/up and down weight-streaming launches for one weight format. Two-group passes where every
+// block of the grid stays resident at their lower occupancy (gate/up: at most 2048 blocks;
+// down: at most 4096).
+template <int WF>
+hipError_t launch_streaming(const uint16_t* x, const void* wg, const void* wu, const void* wd,
+                            int d, int E, int H, int k, const RowSource& rs, uint16_t* h,
+                            const DownArgs& down, hipStream_t s, const StageMarks& gu,
+                            const QuantWeights& qw) {
+  const DownArgs none{};
+  const dim3 g_gu(H / kStFeat, E), g_dn(d / kStFeat, E);
+  const bool g2 = (H / kStFeat) * E <= 2048;
+  const hipError_t err =
+      g2 ? launch_marked(ffn_stream_kernel<true, 2, WF>, g_gu, dim3(kWave), s, gu, x, wg, wu,
+                         qw.gate, qw.up, d, H, k, rs, h, none)
+         : launch_marked(ffn_stream_kernel<true, 1, WF>, g_gu, dim3(kWave), s, gu, x, wg, wu,
+                         qw.gate, qw.up, d, H, k, rs, h, none);
+  if (err != hipSuccess) return err;
+  RowSource rs2 = rs;
+  rs2.counts_out = nullptr;
+  if ((d / kStFeat) * E <= 4096)
+    ffn_stream_kernel<false, 2, WF><<<g_dn, kWave, 0, s>>>(h, wd, nullptr, qw.down, nullptr, H, d,
+                                                           k, rs2, nullptr, down);
+  else
+    ffn_stream_kernel<false, 1, WF><<<g_dn, kWave, 0, s>>>(h, wd, nullptr, qw.down, nullptr, H, d,
+                                                           k, rs2, nullptr, down);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, const void* wd,
                            int T, int d, int E, int H, int k, const RowSource& rs, uint16_t* h,
                            const DownArgs& down, hipStream_t s, const StageMarks& gu,
-                           const WeightScales& q8) {
+                           const QuantWeights& qw) {
   const int rows = T * k;
   if (rows <= 0) return hipSuccess;
   DownArgs none{};
   hipError_t err;
-  const bool w8 = q8.gate != nullptr;
   if (ffn_bf16_streaming(T, d, E, H, k)) {
-    // two-group passes where every block of the grid stays resident at their lower occupancy
-    // (gate/up: ~154 VGPRs, 12 waves per CU; down: ~120 VGPRs, 16 waves per CU)
-    const bool g2 = (H / kStFeat) * E <= 2048;
-    const dim3 g_gu(H / kStFeat, E), g_dn(d / kStFeat, E);
-#define MOE_GU(MG, W)                                                                    \
-  launch_marked(ffn_stream_kernel<true, MG, W>, g_gu, dim3(kWave), s, gu, x, wg, wu, q8.gate, \
-                q8.up, d, H, k, rs, h, none)
-    err = w8 ? (g2 ? MOE_GU(2, true) : MOE_GU(1, true)) : (g2 ? MOE_GU(2, false) : MOE_GU(1, false));
-#undef MOE_GU
-    if (err != hipSuccess) return err;
-    RowSource rs2 = rs;
-    rs2.counts_out = nullptr;
-    const bool g2d = (d / kStFeat) * E <= 4096;
-#define MOE_DN(MG, W)                                                                        \
-  ffn_stream_kernel<false, MG, W><<<g_dn, kWave, 0, s>>>(h, wd, nullptr, q8.down, nullptr, H, d, k, \
-                                                         rs2, nullptr, down)
-    if (w8) {
-      if (g2d) MOE_DN(2, true);
-      else MOE_DN(1, true);
-    } else {
-      if (g2d) MOE_DN(2, false);
-      else MOE_DN(1, false);
+    switch (qw.fmt) {
+      case kWBf16: return launch_streaming<kWBf16>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
+      case kWI8: return launch_streaming<kWI8>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
+      case kWQ4: return launch_streaming<kWQ4>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
+      default: return hipErrorInvalidValue;
     }
-#undef MOE_DN
-    return hipGetLastError();
   }
-  if (w8) return hipErrorInvalidValue;  // int8 weights: weight-streaming shapes only (checked above)
+  // quantised weights: weight-streaming shapes only (checked by the callers)
+  if (qw.fmt != kWBf16) return hipErrorInvalidValue;
   // grouped GEMM over the dispatch order; 1-D grid sized for the worst-case tile count
   constexpr int NT = kTileM / kTileWaveRows * (kTileN / 64) * kWave;
   const long long mt = max_tiles(rows, E, kTileM);

@@ -118,28 +118,39 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k);
 // Largest T*k the by-ids row scan supports.
 constexpr int kMaxScanRows = 2048;
 
-// Row scales of int8 expert weights ([E,H], [E,H], [E,d]); all NULL for bf16 weights.
-struct WeightScales {
-  const float* gate;
-  const float* up;
-  const float* down;
+// Storage of the expert weights on the bf16 path.
+enum WeightFormat {
+  kWBf16 = 0,  // bf16 bits
+  kWI8 = 1,    // int8 codes, fp32 row scales `gate`, `up`, `down` ([E,H], [E,H], [E,d])
+  kWQ4 = 2     // packed 4-bit codes, uint32 (scale, bias) pairs per group of 64 along K
+};
+struct QuantWeights {
+  int fmt;           // WeightFormat
+  const void* gate;  // quantisation arrays of the three stacks (NULL for bf16)
+  const void* up;
+  const void* down;
 };
 
 // h is the [T*k, H] intermediate (bf16 bits or fp32). `gu` marks the gate/up launch (timing).
-// wg, wu, wd are bf16 bits, or int8 codes when `q8.gate` is set (weight-streaming shapes only).
+// wg, wu, wd are in the storage `qw.fmt` names; quantised formats on weight-streaming shapes
+// only (hipErrorInvalidValue otherwise).
 hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, const void* wd,
                            int T, int d, int E, int H, int k, const RowSource& rs, uint16_t* h,
                            const DownArgs& down, hipStream_t s, const StageMarks& gu,
-                           const WeightScales& q8);
+                           const QuantWeights& qw);
 hipError_t launch_ffn_f32(const float* x, const float* wg, const float* wu, const float* wd,
                           int T, int d, int E, int H, int k, const int32_t* offsets,
                           const int32_t* sorted_rows, float* h, const DownArgs& down,
                           hipStream_t s, const StageMarks& gu);
 
-// ---------------------------------------------------------------- int8 weights (quant.hip)
+// ---------------------------------------------------------- quantised weights (quant.hip)
 // Per-row symmetric int8 codes of a [rows, K] matrix (bf16 bits or fp32), K % 16 == 0.
 hipError_t launch_quantize_rows_i8(const void* w, long long rows, int K, bool bf16, int8_t* q,
                                    float* scales, hipStream_t s);
+// 4-bit affine codes in groups of 64 (packed order and pairs as in moe_quantize_groups_q4),
+// K % 128 == 0.
+hipError_t launch_quantize_groups_q4(const void* w, long long rows, int K, bool bf16, uint8_t* q,
+                                     uint32_t* qpar, hipStream_t s);
 
 // ---------------------------------------------------------------- combine (combine.hip)
 // row_pos == NULL: expert_out is indexed by the assignment row itself.

@@ -202,7 +202,7 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
     const RowSource rs{nullptr, T * k, expert_offsets, sorted_rows, nullptr};
     return hip_status(moe::launch_ffn_bf16(static_cast<const uint16_t*>(x), w_gate, w_up, w_down, T,
                                            d, E, H, k, rs, at<uint16_t>(ws, lay.h), down, s,
-                                           moe::StageMarks{}, moe::WeightScales{}));
+                                           moe::StageMarks{}, moe::QuantWeights{}));
   }
   return hip_status(moe::launch_ffn_f32(
       static_cast<const float*>(x), static_cast<const float*>(w_gate),
@@ -220,6 +220,18 @@ int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* 
   clear_stale_error();
   return hip_status(moe::launch_quantize_rows_i8(w, rows, K, dtype == MOE_BF16, q, scales,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_t* q,
+                           uint32_t* qpar, void* stream) {
+  if (rows < 0 || K < 128 || K % 128 != 0) return MOE_ERR_SHAPE;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !qpar) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(qpar)) return MOE_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(moe::launch_quantize_groups_q4(w, rows, K, dtype == MOE_BF16, q, qpar,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
@@ -246,14 +258,16 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   // dtype
   const bool abi2 = a->struct_size >= sizeof(moe_layer_args);
   const int w_dtype = (abi2 && a->w_dtype != 0) ? a->w_dtype : dtype;
-  moe::WeightScales q8{};
+  moe::QuantWeights qw{};
   if (w_dtype != dtype) {
-    if (w_dtype != MOE_I8 || dtype != MOE_BF16 || !moe::ffn_bf16_streaming(T, d, E, H, k))
+    if ((w_dtype != MOE_I8 && w_dtype != MOE_Q4) || dtype != MOE_BF16 ||
+        !moe::ffn_bf16_streaming(T, d, E, H, k))
       return MOE_ERR_UNSUPPORTED;
     if (!a->w_gate_scale || !a->w_up_scale || !a->w_down_scale) return MOE_ERR_NULL;
     if (!aligned16(a->w_gate_scale) || !aligned16(a->w_up_scale) || !aligned16(a->w_down_scale))
       return MOE_ERR_SHAPE;
-    q8 = moe::WeightScales{a->w_gate_scale, a->w_up_scale, a->w_down_scale};
+    qw = moe::QuantWeights{w_dtype == MOE_I8 ? moe::kWI8 : moe::kWQ4, a->w_gate_scale,
+                           a->w_up_scale, a->w_down_scale};
   }
   if (T == 0) return MOE_OK;
   if (!a->x || !a->w_router || !a->w_gate || !a->w_up || !a->w_down || !a->y) return MOE_ERR_NULL;
@@ -327,7 +341,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
                                    : RowSource{nullptr, T * k, offsets, sorted_rows, nullptr};
     MOE_TRY(moe::launch_ffn_bf16(static_cast<const uint16_t*>(a->x), a->w_gate, a->w_up,
                                  a->w_down, T, d, E, H, k, rs, at<uint16_t>(ws, lay.h), down, s,
-                                 gu, q8));
+                                 gu, qw));
   } else {
     MOE_TRY(moe::launch_ffn_f32(
         static_cast<const float*>(a->x), static_cast<const float*>(a->w_gate),

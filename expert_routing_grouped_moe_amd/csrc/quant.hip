@@ -1,4 +1,5 @@
-// Symmetric per-row int8 codes of expert weights, for the quantised decode path (moe_quantize_rows_i8).
+// Quantised expert weights for the decode path: 4-bit affine group codes
+// (moe_quantize_groups_q4, below) and symmetric per-row int8 codes (moe_quantize_rows_i8):
 //   s = fp32(max_i |w_i| / 127),   q_i = clamp(rint(fp32(w_i / s)), -127, 127)   (ties to even)
 // both divisions IEEE round-to-nearest-even (__fdiv_rn), so the codes are defined exactly; an
 // all-zero row gets s = 0 and q = 0. The pages run quantised expert stacks for decode
@@ -64,7 +65,74 @@ __global__ __launch_bounds__(kWave * kQRowsPerBlock) void quantize_rows_i8_kerne
   }
 }
 
+// 4-bit affine codes, groups of 64 along K (moe_quantize_groups_q4): one thread per group.
+//   lo, hi = min, max;  s = bf16(fp32(fp32(hi - lo) / 15));  b = bf16(lo)
+//   q_i = clamp(rint(fp32(fp32(w_i - b) / s)), 0, 15)      (s == 0: q_i = 0)
+// with IEEE round-to-nearest-even subtractions and divisions (__fsub_rn, __fdiv_rn) and bf16()
+// rounding to nearest even, so codes, scale and bias are defined exactly. The ZONOS2-4bit card
+// quantises the experts affinely at 4 bits in groups of 64 ("Quantization recipe"); this
+// arithmetic is the library's reading of that scheme.
+// Group G of a row covers k = 64 G .. 64 G + 63, i.e. MFMA steps c = 2 (G % 2) and 2 (G % 2) + 1
+// of block G / 2 for all four lane groups: eight packed words, written separately.
+constexpr int kQ4Group = 64;
+
+__device__ __forceinline__ float bf16_round(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return __uint_as_float(((u + 0x7fffu + ((u >> 16) & 1u)) >> 16) << 16);
+}
+
+__global__ __launch_bounds__(256) void quantize_groups_q4_kernel(
+    const void* __restrict__ w, long long groups, int K, bool bf16, uint8_t* __restrict__ q,
+    uint32_t* __restrict__ qpar) {
+  const long long gi = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gi >= groups) return;
+  const int gpr = K / kQ4Group;                 // groups per row
+  const long long row = gi / gpr;
+  const int G = static_cast<int>(gi - row * gpr);
+  const long long base = row * K + static_cast<long long>(G) * kQ4Group;
+  float v[kQ4Group];
+#pragma unroll
+  for (int i = 0; i < kQ4Group; i += 4) load4(w, bf16, base + i, v + i);
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < kQ4Group; ++i) {
+    lo = fminf(lo, v[i]);
+    hi = fmaxf(hi, v[i]);
+  }
+  const float sc = bf16_round(__fdiv_rn(__fsub_rn(hi, lo), 15.f));
+  const float bs = bf16_round(lo);
+  qpar[gi] = (__float_as_uint(sc) >> 16) | (__float_as_uint(bs) & 0xffff0000u);
+  uint32_t* out = reinterpret_cast<uint32_t*>(q + row * (K / 2) + 64 * (G / 2));
+  const int c0 = 2 * (G % 2);
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = v[32 * cc + 8 * g + i];  // k = 64 G + 32 cc + 8 g + i
+        uint32_t code = 0;
+        if (sc > 0.f)
+          code = static_cast<uint32_t>(fminf(15.f, fmaxf(0.f, rintf(__fdiv_rn(__fsub_rn(x, bs), sc)))));
+        word |= code << ((i & 1) ? 16 + 4 * (i >> 1) : 4 * (i >> 1));
+      }
+      out[4 * g + c0 + cc] = word;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_groups_q4(const void* w, long long rows, int K, bool bf16, uint8_t* q,
+                                     uint32_t* qpar, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const long long groups = rows * (K / kQ4Group);
+  const long long blocks = (groups + 255) / 256;
+  quantize_groups_q4_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(w, groups, K, bf16, q,
+                                                                          qpar);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows_i8(const void* w, long long rows, int K, bool bf16, int8_t* q,
                                    float* scales, hipStream_t s) {

@@ -15,7 +15,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
-MOE_ABI_VERSION = 2  # include/moe.h; the library must report the same value
+MOE_ABI_VERSION = 3  # include/moe.h; the library must report the same value
 
 MOE_OK = 0
 MOE_ERR_NULL = -1
@@ -27,6 +27,7 @@ MOE_ERR_HIP = -5
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_I8 = 2
+MOE_Q4 = 3
 
 MOE_SCORING_SOFTMAX = 0
 MOE_SCORING_SELECTED_SOFTMAX = 1
@@ -37,7 +38,7 @@ SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELEC
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_quantize_rows_i8")
+           "moe_quantize_rows_i8", "moe_quantize_groups_q4")
 
 
 class MoeError(RuntimeError):
@@ -96,6 +97,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_rows_i8.restype = c_int
     lib.moe_quantize_rows_i8.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
                                          c_void_p, c_void_p]
+    lib.moe_quantize_groups_q4.restype = c_int
+    lib.moe_quantize_groups_q4.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
+                                           c_void_p, c_void_p]
     if lib.moe_abi_version() != MOE_ABI_VERSION:
         raise ImportError(f"{_LIB_PATH} reports ABI {lib.moe_abi_version()}, the binding expects "
                           f"{MOE_ABI_VERSION}; rebuild the library")
@@ -257,22 +261,29 @@ def moe_combine(expert_out, row_pos, topk_w, y=None, stream=None):
 def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias=None,
                     sel_bias=None, logits=None, topk_ids=None, topk_w=None, expert_counts=None,
                     w_scales=None):
-    """``w_scales`` = (gate, up, down) fp32 row scales when the expert weights are int8 codes
-    (moe_quantize_rows_i8)."""
+    """Quantised expert weights: int8 codes (moe_quantize_rows_i8) with ``w_scales`` = their
+    (gate, up, down) fp32 row scales, or uint8 packed 4-bit codes (moe_quantize_groups_q4) with
+    ``w_scales`` = their int32 (scale, bias) pair arrays."""
     T, d = x.shape
     E, H, _ = w_gate.shape
-    wt = torch.int8 if w_gate.dtype == torch.int8 else x.dtype
+    wt = w_gate.dtype if w_gate.dtype in (torch.int8, torch.uint8) else x.dtype
+    q4 = wt == torch.uint8
     _need(x, "x", (T, d))
     _need(w_router, "w_router", (E, d), x.dtype)
-    _need(w_gate, "w_gate", (E, H, d), wt)
-    _need(w_up, "w_up", (E, H, d), wt)
-    _need(w_down, "w_down", (E, d, H), wt)
-    if wt == torch.int8:
+    _need(w_gate, "w_gate", (E, H, d // 2 if q4 else d), wt)
+    _need(w_up, "w_up", (E, H, d // 2 if q4 else d), wt)
+    _need(w_down, "w_down", (E, d, H // 2 if q4 else H), wt)
+    if wt in (torch.int8, torch.uint8):
         if w_scales is None:
-            raise ValueError("int8 expert weights need w_scales = (gate, up, down)")
-        _need(w_scales[0], "w_gate_scale", (E, H), torch.float32)
-        _need(w_scales[1], "w_up_scale", (E, H), torch.float32)
-        _need(w_scales[2], "w_down_scale", (E, d), torch.float32)
+            raise ValueError("quantised expert weights need w_scales = (gate, up, down)")
+        if q4:
+            _need(w_scales[0], "w_gate_scale", (E, H, d // 64), torch.int32)
+            _need(w_scales[1], "w_up_scale", (E, H, d // 64), torch.int32)
+            _need(w_scales[2], "w_down_scale", (E, d, H // 64), torch.int32)
+        else:
+            _need(w_scales[0], "w_gate_scale", (E, H), torch.float32)
+            _need(w_scales[1], "w_up_scale", (E, H), torch.float32)
+            _need(w_scales[2], "w_down_scale", (E, d), torch.float32)
     _need(router_bias, "router_bias", (E,), torch.float32)
     _need(sel_bias, "sel_bias", (E,), torch.float32)
     _need(y, "y", (T, d), torch.float32)
@@ -284,8 +295,8 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
     a.struct_size = ctypes.sizeof(MoeLayerArgs)
     a.T, a.d, a.E, a.H, a.k = T, d, E, H, k
     a.dtype = _dtype_code(x)
-    a.w_dtype = MOE_I8 if wt == torch.int8 else a.dtype
-    if wt == torch.int8:
+    a.w_dtype = {torch.int8: MOE_I8, torch.uint8: MOE_Q4}.get(wt, a.dtype)
+    if wt in (torch.int8, torch.uint8):
         a.w_gate_scale, a.w_up_scale, a.w_down_scale = (t.data_ptr() for t in w_scales)
     a.scoring = _scoring_code(scoring)
     for name, t in (("x", x), ("w_router", w_router), ("router_bias", router_bias),
@@ -300,7 +311,8 @@ def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias
                       sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
                       expert_counts=None, workspace=None, stream=None, args=None, w_scales=None):
     """The fused layer. Returns y [T, d] fp32. Optional outputs are written when passed. With
-    int8 expert weights (codes from moe_quantize_rows_i8) pass their row scales as w_scales."""
+    quantised expert weights (moe_quantize_rows_i8 or moe_quantize_groups_q4 codes) pass their
+    scale arrays as w_scales."""
     T, d = x.shape
     E, H, _ = w_gate.shape
     y = _empty((T, d), torch.float32, x) if y is None else y
@@ -329,3 +341,20 @@ def moe_quantize_rows_i8(w, q=None, scales=None, stream=None):
     _check(LIB.moe_quantize_rows_i8(_ptr(w), rows, K, _dtype_code(w), _ptr(q), _ptr(scales),
                                     _stream(stream)), "moe_quantize_rows_i8")
     return q, scales
+
+
+def moe_quantize_groups_q4(w, q=None, qpar=None, stream=None):
+    """4-bit affine codes of w [..., K] (bf16 or fp32, K % 128 == 0) in groups of 64: returns
+    (q uint8 [..., K / 2] packed codes, qpar int32 [..., K / 64] (scale, bias) bf16 pairs)."""
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    q = torch.empty(tuple(w.shape[:-1]) + (K // 2,), dtype=torch.uint8, device=w.device) if q is None else q
+    qpar = (torch.empty(tuple(w.shape[:-1]) + (K // 64,), dtype=torch.int32, device=w.device)
+            if qpar is None else qpar)
+    _need(q, "q", tuple(w.shape[:-1]) + (K // 2,), torch.uint8)
+    _need(qpar, "qpar", tuple(w.shape[:-1]) + (K // 64,), torch.int32)
+    _check(LIB.moe_quantize_groups_q4(_ptr(w), rows, K, _dtype_code(w), _ptr(q), _ptr(qpar),
+                                      _stream(stream)), "moe_quantize_groups_q4")
+    return q, qpar

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
   MOE_OK = 0,
@@ -69,7 +69,11 @@ enum moe_dtype {
   MOE_BF16 = 1,
   /* int8 expert weights with one fp32 scale per weight row (moe_quantize_rows_i8). Only as
      moe_layer_args.w_dtype, with bf16 activations, on the decode path. Added in ABI 2. */
-  MOE_I8 = 2
+  MOE_I8 = 2,
+  /* 4-bit affine expert weights, one bf16 (scale, bias) pair per group of 64 along the reduction
+     index, codes in the packed order of moe_quantize_groups_q4. Only as moe_layer_args.w_dtype,
+     with bf16 activations, on the decode path. Added in ABI 3. */
+  MOE_Q4 = 3
 };
 
 enum moe_scoring {
@@ -208,17 +212,22 @@ typedef struct moe_layer_args {
   /* ABI 2. w_dtype = 0, or a struct_size that ends before w_dtype (MOE_LAYER_ARGS_V1_SIZE),
      means the expert weights have the activation dtype (as does w_dtype = dtype).
      w_dtype = MOE_I8: w_gate, w_up and w_down hold int8 codes in the same [E,H,d] / [E,d,H]
-     layouts, and the scale arrays hold their fp32 row scales ([E,H], [E,H], [E,d]) as written
-     by moe_quantize_rows_i8; the layer computes with the weights scale * code. This quantised
-     decode path (bytes per weight halved: the pages run quantised expert stacks for decode,
-     ZONOS2-4bit MLX card, "Performance notes"; zonos2.cpp INTERNALS, "Recommended: F16 spine +
-     K-quant experts") needs dtype = MOE_BF16 and the weight-streaming regime (T*k <= 2048,
-     T*k <= 32*E, d and H multiples of 256): anything else returns MOE_ERR_UNSUPPORTED. Missing
-     scales: MOE_ERR_NULL. Scales must be 16-byte aligned. */
+     layouts, and the quantisation arrays hold their fp32 row scales ([E,H], [E,H], [E,d]) as
+     written by moe_quantize_rows_i8; the layer computes with the weights scale * code.
+     w_dtype = MOE_Q4 (ABI 3): w_gate, w_up and w_down hold packed 4-bit codes ([E,H,d/2],
+     [E,H,d/2], [E,d,H/2] bytes) and the quantisation arrays their uint32 (scale, bias) pairs
+     ([E,H,d/64], [E,H,d/64], [E,d,H/64]), both as written by moe_quantize_groups_q4; the layer
+     computes with the weights scale * code + bias of each group.
+     These quantised decode paths (fewer bytes per weight: the pages run quantised expert stacks
+     for decode, ZONOS2-4bit MLX card, "Performance notes" and "Quantization recipe"; zonos2.cpp
+     INTERNALS, "Recommended: F16 spine + K-quant experts") need dtype = MOE_BF16 and the
+     weight-streaming regime (T*k <= 2048, T*k <= 32*E, d and H multiples of 256): anything else
+     returns MOE_ERR_UNSUPPORTED. Missing quantisation arrays: MOE_ERR_NULL. They must be 16-byte
+     aligned. */
   int32_t w_dtype;
-  const float* w_gate_scale;  /* [E, H] */
-  const float* w_up_scale;    /* [E, H] */
-  const float* w_down_scale;  /* [E, d] */
+  const void* w_gate_scale;   /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
+  const void* w_up_scale;     /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
+  const void* w_down_scale;   /* MOE_I8: float [E, d];  MOE_Q4: uint32 [E, d, H / 64] */
 } moe_layer_args;
 
 #define MOE_LAYER_ARGS_V1_SIZE offsetof(moe_layer_args, w_dtype)
@@ -248,6 +257,28 @@ int moe_layer_forward(const moe_layer_args* args, void* ws, size_t ws_bytes, voi
  */
 int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* q, float* scales,
                          void* stream);
+
+/*
+ * 4-bit affine codes of a row-major [rows, K] weight matrix in groups of 64 along K (the
+ * ZONOS2-4bit card quantises the experts affinely at 4 bits with group size 64, "Quantization
+ * recipe"; the arithmetic below is this library's reading). For each group of 64 values w_i:
+ *   lo, hi = min, max;   s = bf16(fp32(fp32(hi - lo) / 15));   b = bf16(lo)
+ *   q_i    = clamp(rint(fp32(fp32(w_i - b) / s)), 0, 15)   (ties to even; s == 0 gives q_i = 0)
+ * where fp32() is one IEEE round-to-nearest-even operation and bf16() rounds to nearest even.
+ * The weight the layer uses is s * q_i + b.
+ * Outputs (device): qpar uint32 [rows, K / 64], bf16 bits of s in the low half and of b in the
+ * high half; q uint8 [rows, K / 2] in this packed order: the 64 bytes of block j (k = 128 j ..
+ * 128 j + 127) are 16 little-endian uint32 words, word 4 g + c holding the codes of k = 128 j +
+ * 32 c + 8 g + i, i = 0..7, with i = 2 m in bits 4 m .. 4 m + 3 and i = 2 m + 1 in bits
+ * 16 + 4 m .. 19 + 4 m (g, c, m = 0..3). Each 16-byte quarter of a block is then the eight-code
+ * runs one lane group of the matrix cores needs, and a shift and a mask turn two codes into
+ * a pair of bf16 values.
+ * w: device, dtype MOE_BF16 or MOE_F32. 128 <= K, K % 128 == 0 (MOE_ERR_SHAPE otherwise); rows >= 0
+ * (0 is a no-op); pointers 16-byte aligned. Non-finite weights are outside the contract.
+ * Asynchronous on `stream`, capturable, allocates nothing. Added in ABI 3.
+ */
+int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_t* q,
+                           uint32_t* qpar, void* stream);
 
 #ifdef __cplusplus
 }

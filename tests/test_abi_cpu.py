@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.moe_abi_version() == 2 == moe.MOE_ABI_VERSION
+    assert moe.moe_abi_version() == 3 == moe.MOE_ABI_VERSION
     hdr = re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read())
     assert hdr and int(hdr.group(1)) == moe.MOE_ABI_VERSION
     for st in (0, -1, -2, -3, -4, -5):
@@ -157,6 +157,36 @@ def test_layer_int8_weight_validation():
     assert run(_args(**{**q8, "struct_size": moe.MoeLayerArgs.w_dtype.offset}), n=0) == \
         moe.MOE_ERR_WORKSPACE
     assert run(_args(struct_size=moe.MoeLayerArgs.w_dtype.offset - 4)) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_layer_q4_weight_validation():
+    L = moe.LIB
+    T, d, E, H = 16, 256, 8, 256
+    ws = L.moe_workspace_size(T, d, E, H, 1, 1)
+    run = lambda a, n=ws: L.moe_layer_forward(ctypes.byref(a), FAKE, n, None)
+    q4 = dict(T=T, d=d, E=E, H=H, w_dtype=moe.MOE_Q4, w_gate_scale=FAKE.value,
+              w_up_scale=FAKE.value, w_down_scale=FAKE.value)
+    assert run(_args(**{**q4, "T": 0})) == moe.MOE_OK
+    assert run(_args(**{**q4, "w_gate_scale": None})) == moe.MOE_ERR_NULL
+    assert run(_args(**{**q4, "w_up_scale": MISALIGNED.value})) == moe.MOE_ERR_SHAPE
+    assert run(_args(**{**q4, "dtype": 0})) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(**{**q4, "d": 128, "H": 128})) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(**{**q4, "T": 2048, "k": 2}), n=1 << 40) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(**q4), n=ws - 256) == moe.MOE_ERR_WORKSPACE
+
+
+def test_quantize_q4_validation():
+    L = moe.LIB
+    q = lambda w=FAKE, rows=4, K=256, dt=1, qq=FAKE, p=FAKE: L.moe_quantize_groups_q4(
+        w, rows, K, dt, qq, p, None)
+    assert q(rows=0) == moe.MOE_OK
+    assert q(rows=-1) == moe.MOE_ERR_SHAPE
+    assert q(K=64) == moe.MOE_ERR_SHAPE           # groups of 64, blocks of 128
+    assert q(K=192) == moe.MOE_ERR_SHAPE
+    assert q(dt=2) == moe.MOE_ERR_UNSUPPORTED
+    assert q(w=None) == moe.MOE_ERR_NULL
+    assert q(p=None) == moe.MOE_ERR_NULL
+    assert q(qq=MISALIGNED) == moe.MOE_ERR_SHAPE
 
 
 def test_quantize_validation():
