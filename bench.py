@@ -110,6 +110,60 @@ def algorithmic(inp, counts, weights="native"):
                 gu_flops=gu_flops)
 
 
+def ladder_timing(moe, inp, x, wr, copies, rb, sb, steps, quant=False):
+    """Serving-side decode with a changing batch width: `steps` steps whose token counts are drawn
+    uniformly from 1..T (seeded), run as direct moe_layer_forward calls, as replays of a graph
+    ladder with one bucket per batch width, and as replays of a ladder with power-of-two buckets
+    (padding rows are extra tokens: more experts touched). One ladder per weight copy, as the
+    steps rotate through the copies. Reports microseconds per step and tokens per second."""
+    import numpy as np
+    import torch
+    T, k = inp.T, inp.k
+    rng = np.random.default_rng(1234)
+    ts = rng.integers(1, T + 1, size=steps)
+    pow2 = sorted({min(T, 1 << i) for i in range(T.bit_length() + 1)})
+    exact = list(range(1, T + 1))
+    stream = torch.cuda.Stream()
+    qs = lambda c: ((c["w_gate_scale"], c["w_up_scale"], c["w_down_scale"]) if quant else None)
+    mk = lambda buckets: [moe.MoeGraphLadder(x, wr, c["w_gate"], c["w_up"], c["w_down"], k,
+                                             inp.scoring, buckets, router_bias=rb, sel_bias=sb,
+                                             w_scales=qs(c), stream=stream) for c in copies]
+    ladders = {"ladder": mk(exact), "ladder_pow2": mk(pow2)}
+    ys = [torch.empty((T, inp.d), dtype=torch.float32, device=x.device) for _ in copies]
+    wss = [torch.empty(max(1, moe.moe_workspace_size(T, inp.d, inp.E, inp.H, k, moe.MOE_BF16
+                                                      if inp.dtype == "bf16" else moe.MOE_F32)),
+                       dtype=torch.uint8, device=x.device) for _ in copies]
+
+    def direct(i, t):
+        c = copies[i % len(copies)]
+        moe.moe_layer_forward(x[:t], wr, c["w_gate"], c["w_up"], c["w_down"], k, inp.scoring,
+                              router_bias=rb, sel_bias=sb, y=ys[i % len(copies)][:t],
+                              workspace=wss[i % len(copies)], stream=stream, w_scales=qs(c))
+
+    def replay(name):
+        return lambda i, t: ladders[name][i % len(copies)].run(int(t), stream)
+
+    out = {"steps": steps, "batch_widths": "uniform 1..%d, seed 1234" % T,
+           "ladder_buckets": "1..%d" % T, "ladder_pow2_buckets": pow2}
+    with torch.cuda.stream(stream):
+        for name, fn in (("direct", direct), ("ladder", replay("ladder")),
+                         ("ladder_pow2", replay("ladder_pow2"))):
+            for i in range(min(steps, 20)):
+                fn(i, int(ts[i]))
+            stream.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                fn(i, int(ts[i]))
+            stream.synchronize()
+            el = time.perf_counter() - t0
+            out[name + "_us_per_step"] = el / steps * 1e6
+            out[name + "_tokens_per_s"] = float(ts.sum()) / el
+    for lads in ladders.values():
+        for lad in lads:
+            lad.close()
+    return out
+
+
 def cpu_baseline(inp, budget_s: float):
     """The fp64 oracle as it stands, timed on this host on the same workload."""
     import numpy as np
@@ -155,6 +209,9 @@ def main():
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB ten times (counter calibration)")
+    ap.add_argument("--ladder", type=int, default=0, metavar="STEPS",
+                    help="also time STEPS decode steps of seeded random batch widths 1..T, launched "
+                         "directly and replayed from a graph ladder (buckets 1, 2, 4, ..., T)")
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -387,6 +444,9 @@ def main():
         "event_step_median_us": statistics.median(step_ms_ev) * 1e3,
         "roofline": roof,
     }
+    if args.ladder:
+        result["ladder"] = ladder_timing(moe, inp, x, wr, copies, rb, sb, args.ladder,
+                                         quant=quant)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(result))

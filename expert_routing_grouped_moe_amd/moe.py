@@ -38,7 +38,10 @@ SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELEC
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_quantize_rows_i8", "moe_quantize_groups_q4")
+           "moe_quantize_rows_i8", "moe_quantize_groups_q4", "moe_ladder_create", "moe_ladder_run",
+           "moe_ladder_destroy")
+
+MOE_LADDER_MAX_BUCKETS = 256
 
 
 class MoeError(RuntimeError):
@@ -100,6 +103,13 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_groups_q4.restype = c_int
     lib.moe_quantize_groups_q4.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
                                            c_void_p, c_void_p]
+    lib.moe_ladder_create.restype = c_int
+    lib.moe_ladder_create.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_int, c_void_p, c_size_t,
+                                      c_void_p, POINTER(c_void_p)]
+    lib.moe_ladder_run.restype = c_int
+    lib.moe_ladder_run.argtypes = [c_void_p, c_int, c_void_p, c_void_p]
+    lib.moe_ladder_destroy.restype = None
+    lib.moe_ladder_destroy.argtypes = [c_void_p]
     if lib.moe_abi_version() != MOE_ABI_VERSION:
         raise ImportError(f"{_LIB_PATH} reports ABI {lib.moe_abi_version()}, the binding expects "
                           f"{MOE_ABI_VERSION}; rebuild the library")
@@ -358,3 +368,48 @@ def moe_quantize_groups_q4(w, q=None, qpar=None, stream=None):
     _check(LIB.moe_quantize_groups_q4(_ptr(w), rows, K, _dtype_code(w), _ptr(q), _ptr(qpar),
                                       _stream(stream)), "moe_quantize_groups_q4")
     return q, qpar
+
+
+class MoeGraphLadder:
+    """moe_ladder_create / moe_ladder_run / moe_ladder_destroy over torch tensors: the layer is
+    captured once per bucket of batch sizes on the buffers given here (every token-indexed tensor
+    holds x.shape[0] rows), and run(T) replays the smallest bucket >= T. The object keeps every
+    captured tensor referenced until close(). `stream` must be a torch.cuda.Stream other than the
+    default stream (capture needs a stream of its own)."""
+
+    def __init__(self, x, w_router, w_gate, w_up, w_down, k, scoring, buckets, y=None,
+                 router_bias=None, sel_bias=None, logits=None, topk_ids=None, topk_w=None,
+                 expert_counts=None, w_scales=None, stream=None):
+        T, d = x.shape
+        E, H, _ = w_gate.shape
+        self.y = _empty((T, d), torch.float32, x) if y is None else y
+        self.args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, self.y,
+                                    router_bias, sel_bias, logits, topk_ids, topk_w,
+                                    expert_counts, w_scales)
+        ws_bytes = moe_workspace_size(T, d, E, H, k, self.args.dtype)
+        self.workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        self._keep = (x, w_router, w_gate, w_up, w_down, router_bias, sel_bias, logits, topk_ids,
+                      topk_w, expert_counts, w_scales)
+        b = (ctypes.c_int32 * len(buckets))(*buckets)
+        self.buckets = list(buckets)
+        self._h = c_void_p()
+        _check(LIB.moe_ladder_create(ctypes.byref(self.args), b, len(buckets), _ptr(self.workspace),
+                                     self.workspace.numel(), _stream(stream), ctypes.byref(self._h)),
+               "moe_ladder_create")
+
+    def run(self, T, stream=None):
+        """Replays the bucket for T tokens; returns the bucket size used."""
+        used = ctypes.c_int32()
+        _check(LIB.moe_ladder_run(self._h, T, _stream(stream), ctypes.byref(used)), "moe_ladder_run")
+        return used.value
+
+    def close(self):
+        if self._h:
+            LIB.moe_ladder_destroy(self._h)
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover (interpreter shutdown)
+            pass

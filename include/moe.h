@@ -280,6 +280,41 @@ int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* 
 int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_t* q,
                            uint32_t* qpar, void* stream);
 
+/*
+ * Graph ladder (serving-side decode). zonos2.cpp INTERNALS, "Performance": the decode graph is
+ * captured once and replayed. A serving loop's batch width changes from step to step, so the
+ * ladder captures moe_layer_forward once per bucket of batch sizes and replays the smallest bucket
+ * that holds the step's tokens. Added in ABI 3.
+ *
+ * moe_ladder_create: `a` describes the layer at its largest batch: every token-indexed buffer (x,
+ *   y, and the optional logits, topk_ids, topk_w) holds a->T rows. For bucket b the captured graph
+ *   runs moe_layer_forward on the first b rows of those buffers, with every other argument of `a`
+ *   (weights, biases, expert_counts, ws) unchanged; prof_events is ignored. buckets: n_buckets
+ *   (1..MOE_LADDER_MAX_BUCKETS) strictly ascending sizes in 1..a->T. ws must hold
+ *   moe_workspace_size(a->T, ...) bytes. Every buffer must stay alive and in place until
+ *   moe_ladder_destroy. `stream` must be a real stream (not NULL) that is not being captured; the
+ *   call captures on it and enqueues no work. Unlike every other entry point it allocates: host
+ *   memory and the graphs' resources; it is not itself capturable. Errors: MOE_ERR_NULL,
+ *   MOE_ERR_SHAPE (buckets), MOE_ERR_UNSUPPORTED (stream), any error moe_layer_forward returns for
+ *   a bucket (nothing is kept), MOE_ERR_HIP (capture or instantiation failed).
+ * moe_ladder_run: replays, on `stream`, the graph of the smallest bucket b >= T (1 <= T <= the
+ *   largest bucket, else MOE_ERR_SHAPE). Rows T..b-1 are computed as extra tokens from whatever x
+ *   holds there (their outputs go to rows T..b-1 of y and of the optional outputs, and they count
+ *   in expert_counts); rows below T are exactly what moe_layer_forward on the first T rows gives
+ *   whenever both calls take the same kernel path. *bucket_out (if not NULL) receives b.
+ *   Capturable (a graph launch).
+ * moe_ladder_destroy: releases the ladder (NULL is a no-op); the caller's stream work using it must
+ *   have completed.
+ */
+#define MOE_LADDER_MAX_BUCKETS 256
+
+typedef struct moe_graph_ladder moe_graph_ladder;
+
+int moe_ladder_create(const moe_layer_args* a, const int32_t* buckets, int n_buckets, void* ws,
+                      size_t ws_bytes, void* stream, moe_graph_ladder** out);
+int moe_ladder_run(const moe_graph_ladder* ladder, int T, void* stream, int32_t* bucket_out);
+void moe_ladder_destroy(moe_graph_ladder* ladder);
+
 #ifdef __cplusplus
 }
 #endif

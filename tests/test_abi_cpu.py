@@ -189,6 +189,26 @@ def test_quantize_q4_validation():
     assert q(qq=MISALIGNED) == moe.MOE_ERR_SHAPE
 
 
+def test_ladder_validation():
+    L = moe.LIB
+    out = ctypes.c_void_p()
+    b = (ctypes.c_int32 * 3)(1, 8, 16)
+    mk = lambda a, bb=b, n=3, s=FAKE, o=ctypes.byref(out): L.moe_ladder_create(
+        ctypes.byref(a), bb, n, FAKE, 1 << 30, s, o)
+    assert L.moe_ladder_create(None, b, 3, FAKE, 1 << 30, FAKE, ctypes.byref(out)) == moe.MOE_ERR_NULL
+    assert mk(_args(), bb=None) == moe.MOE_ERR_NULL
+    assert mk(_args(), o=None) == moe.MOE_ERR_NULL
+    assert mk(_args(), n=0) == moe.MOE_ERR_SHAPE
+    assert mk(_args(), n=moe.MOE_LADDER_MAX_BUCKETS + 1) == moe.MOE_ERR_SHAPE
+    assert mk(_args(), bb=(ctypes.c_int32 * 3)(1, 8, 8)) == moe.MOE_ERR_SHAPE        # not ascending
+    assert mk(_args(), bb=(ctypes.c_int32 * 3)(0, 8, 16)) == moe.MOE_ERR_SHAPE       # empty bucket
+    assert mk(_args(), bb=(ctypes.c_int32 * 3)(1, 8, 17)) == moe.MOE_ERR_SHAPE       # > T = 16
+    assert mk(_args(struct_size=8)) == moe.MOE_ERR_UNSUPPORTED
+    assert mk(_args(), s=None) == moe.MOE_ERR_UNSUPPORTED                            # no null stream
+    assert L.moe_ladder_run(None, 4, None, None) == moe.MOE_ERR_NULL
+    L.moe_ladder_destroy(None)
+
+
 def test_quantize_validation():
     L = moe.LIB
     q = lambda w=FAKE, rows=4, K=64, dt=1, qq=FAKE, s=FAKE: L.moe_quantize_rows_i8(w, rows, K, dt, qq, s, None)
