@@ -17,6 +17,8 @@
 //  * prefill (many rows per expert): a grouped GEMM over the dispatch order with 256 x 128 block
 //    tiles, operands copied from global memory straight into a 3-slot LDS ring (no register
 //    staging), 8 waves of 64 x 64 each, two blocks per CU, tiles ordered per XCD for L2 reuse.
+#include <type_traits>
+
 #include "common.hpp"
 #include "down_epilogue.hpp"
 #include "kernels.hpp"
@@ -329,7 +331,7 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 //  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
 //    that concurrent waves spread over the HBM channels instead of reading the same offset of
 //    their rows. The sum order is fixed per wave, so results repeat exactly.
-template <bool GATEUP, int NG, bool W8>
+template <bool GATEUP, int NG, bool W8, int NB>
 __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
                                             const void* __restrict__ W0,
                                             const void* __restrict__ W1,
@@ -362,22 +364,22 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
     pa[g] = A + arow * K + kq;
   }
-  const int nb = K / 128;                     // even: K % 256 == 0 on this path
+  const int nb = NB > 0 ? NB : K / 128;       // even: K % 256 == 0 on this path
   const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
 
-  u32x4 a0[NG][4], bg0[WR], bu0[WR], a1[NG][4], bg1[WR], bu1[WR];
-  auto load = [&](u32x4 (*a)[4], u32x4* bg, u32x4* bu, int sq) {
+  u32x4 a[2][NG][4], bg[2][WR], bu[2][WR];     // two blocks in flight, slot = block % 2
+  auto load = [&](int j, int sq) {
     const int kb = ((min(sq, nb - 1) + rot) % nb) * 128;  // past the end: re-read the last block
 #pragma unroll
     for (int c = 0; c < WR; ++c) {
       const int off = W8 ? kb + 16 * c : 2 * (kb + 32 * c);  // bytes
-      bg[c] = load16(pg + off);
-      if constexpr (GATEUP) bu[c] = load16(pu + off);
+      bg[j][c] = load16(pg + off);
+      if constexpr (GATEUP) bu[j][c] = load16(pu + off);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int g = 0; g < NG; ++g) a[g][c] = load16(pa[g] + kb + (W8 ? 8 * c : 32 * c));
+      for (int g = 0; g < NG; ++g) a[j][g][c] = load16(pa[g] + kb + (W8 ? 8 * c : 32 * c));
   };
   auto wop = [&](const u32x4* b, int c) -> u32x4 {
     if constexpr (W8) {
@@ -393,31 +395,33 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  auto compute = [&](u32x4 (*a)[4], const u32x4* bg, const u32x4* bu) {
+  auto compute = [&](int j) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 wg = wop(bg, c);
+      const u32x4 wg = wop(bg[j], c);
       u32x4 wu = wg;
-      if constexpr (GATEUP) wu = wop(bu, c);
+      if constexpr (GATEUP) wu = wop(bu[j], c);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        accg[g] = mfma16x16x32(a[g][c], wg, accg[g]);
-        if constexpr (GATEUP) accu[g] = mfma16x16x32(a[g][c], wu, accu[g]);
+        accg[g] = mfma16x16x32(a[j][g][c], wg, accg[g]);
+        if constexpr (GATEUP) accu[g] = mfma16x16x32(a[j][g][c], wu, accu[g]);
       }
     }
   };
-  load(a0, bg0, bu0, 0);
-  load(a1, bg1, bu1, 1);
+  load(0, 0);
+  load(1, 1);
+  // unrolled completely when NB is known: in straight-line code the compiler's wait counts leave
+  // the next block in flight, while a loop back edge makes it wait for every outstanding load
+#pragma unroll (NB > 0 ? NB / 2 : 1)
   for (int sq = 0; sq < nb; sq += 2) {
-    // sched_barrier keeps the scheduler from sinking the prefetches below the next compute
-    compute(a0, bg0, bu0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(a0, bg0, bu0, sq + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(a1, bg1, bu1);
-    __builtin_amdgcn_sched_barrier(0);
-    load(a1, bg1, bu1, sq + 3);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // sched_barrier keeps the scheduler from sinking the prefetch below the next compute
+      compute(j);
+      __builtin_amdgcn_sched_barrier(0);
+      load(j, sq + j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
 #pragma unroll
@@ -623,15 +627,28 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
       else
         stream_tile_q4<GATEUP, 1>(A, c0, c1, p0, p1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
     } else {
+      // the reduction loop fully unrolled for the expert widths of the two models (nb blocks of
+      // 128); the 4-bit loop stays rolled: unrolled, the scheduler hoists the small code loads of
+      // every block to the front and the kernel spills
       constexpr bool W8 = WF == kWI8;
       const float* s0 = static_cast<const float*>(S0);
       const float* s1 = static_cast<const float*>(S1);
-      if (MAXG > 1 && rows > 16)
-        stream_tile<GATEUP, MAXG, W8>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase, h_out,
-                                      down);
-      else
-        stream_tile<GATEUP, 1, W8>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase, h_out,
-                                   down);
+      auto tile = [&](auto nb_const) {
+        constexpr int NB = decltype(nb_const)::value;
+        if (MAXG > 1 && rows > 16)
+          stream_tile<GATEUP, MAXG, W8, NB>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
+                                            h_out, down);
+        else
+          stream_tile<GATEUP, 1, W8, NB>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
+                                         h_out, down);
+      };
+      switch (K) {
+        case 512: tile(std::integral_constant<int, 4>{}); break;
+        case 1024: tile(std::integral_constant<int, 8>{}); break;
+        case 2048: tile(std::integral_constant<int, 16>{}); break;
+        case 2816: tile(std::integral_constant<int, 22>{}); break;
+        default: tile(std::integral_constant<int, 0>{}); break;
+      }
     }
   }
 }
