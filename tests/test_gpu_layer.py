@@ -57,6 +57,11 @@ EDGE = [
     ("E256-k8", 64, 128, 256, 8, 64, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
     ("all-one-expert", 500, 128, 16, 1, 256, orc.SOFTMAX, "bf16", None, "hot5"),
     ("prefill-ragged", 1111, 192, 8, 2, 320, orc.SOFTMAX, "bf16", None, None),
+    # prefill with about one row tile per expert: ragged, one hot expert over several tiles
+    # with the others empty, and the ZONOS2 widths (K = 2048, 2816)
+    ("prefill-few-rows-ragged", 777, 512, 16, 2, 512, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("prefill-few-rows-hot-expert", 600, 1024, 8, 1, 512, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("prefill-zonos2-widths", 1200, 2048, 16, 1, 2816, orc.SOFTMAX, "bf16", None, None),
     # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
     ("prefill-xcd-hot-expert", 2000, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
