@@ -64,6 +64,10 @@ EDGE = [
     ("prefill-zonos2-widths", 1200, 2048, 16, 1, 2816, orc.SOFTMAX, "bf16", None, None),
     # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
     ("prefill-xcd-hot-expert", 2000, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
+    # k = 1 with H >= 1024: the down GEMM splits its reduction in two halves added into y; here
+    # with XCD-ordered tiles, one hot expert and a ragged last tile
+    ("prefill-split-down-hot", 2100, 256, 8, 1, 1024, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("prefill-split-down-ragged", 333, 128, 4, 1, 1088, orc.SOFTMAX, "bf16", None, None),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
     # few rows per expert with d, H multiples of 128: the weight-streaming expert kernels
     ("stream-k3", 40, 128, 16, 3, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
@@ -108,7 +112,8 @@ def test_layer_T0_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill"])
+@pytest.mark.parametrize("name", ["zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill",
+                                  "zonos2-skewed-prefill"])
 def test_layer_deterministic(name):
     inp = gen.make_inputs(name)
     dev = upload(inp)
