@@ -396,16 +396,11 @@ def main():
     streaming = inp.dtype == "bf16" and T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and \
         T * k <= 32 * E
     # the gate/up kernel instantiation the library picks for this shape (two-group passes where
-    # the whole grid stays resident: (H / 16) * E <= 2048 blocks; the reduction split over 4 or 2
-    # waves per block when it is at most 8 blocks of 128 long, each wave keeping an even number)
+    # the whole grid stays resident: (H / 16) * E <= 2048 blocks)
     if streaming:
-        blocks = (H // 16) * E
-        maxg = 2 if blocks <= 2048 else 1
-        nb, kw = d // 128, 1
-        if args.weights != "q4" and nb <= 8:
-            kw = next((w for w in (4, 2) if nb % (2 * w) == 0 and blocks * w <= 8192), 1)
-        roof["kernel"] = "ffn_stream_kernel<true, %d, %d, %d>" % (
-            maxg, {"native": 0, "int8": 1, "q4": 2}[args.weights], kw)
+        maxg = 2 if (H // 16) * E <= 2048 else 1
+        roof["kernel"] = "ffn_stream_kernel<true, %d, %d>" % (
+            maxg, {"native": 0, "int8": 1, "q4": 2}[args.weights])
     else:
         roof["kernel"] = ("gemm_dma_kernel<true, 256, 128, 3, 64>" if inp.dtype == "bf16"
                           else "ffn_f32_kernel<true>")

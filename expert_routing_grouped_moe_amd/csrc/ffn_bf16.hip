@@ -288,26 +288,22 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
 
 // ------------------------------------------------------------------------------ streaming
 
-constexpr int kStFeat = 16;  // output features per block
+constexpr int kStFeat = 16;  // output features per block (one wave)
 
-// Rows r (ascending) of expert e, from the expert ids, by the block's first wave: a ballot per
-// 64 ids. The count reaches the other waves through LDS (`total_out`).
-__device__ int scan_rows(const int32_t* __restrict__ ids, int n, int e, int* lr, int* total_out) {
-  if (threadIdx.x < kWave) {
-    const int lane = lane_id();
-    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    int total = 0;
-    for (int base = 0; base < n; base += kWave) {
-      const int r = base + lane;
-      const bool m = r < n && ids[r] == e;
-      const unsigned long long mask = __ballot(m);
-      if (m) lr[total + __popcll(mask & lt)] = r;
-      total += __popcll(mask);
-    }
-    if (lane == 0) *total_out = total;
+// Rows r (ascending) of expert e, from the expert ids, by one wave: a ballot per 64 ids.
+__device__ int scan_rows(const int32_t* __restrict__ ids, int n, int e, int* lr) {
+  const int lane = lane_id();
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int total = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int r = base + lane;
+    const bool m = r < n && ids[r] == e;
+    const unsigned long long mask = __ballot(m);
+    if (m) lr[total + __popcll(mask & lt)] = r;
+    total += __popcll(mask);
   }
   __syncthreads();
-  return *total_out;
+  return total;
 }
 
 // 8 int8 codes (two dwords, lowest k first) as 8 bf16 values (exact: |code| <= 127 needs 7
@@ -334,20 +330,15 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 //  * two blocks are in flight ahead of use;
 //  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
 //    that concurrent waves spread over the HBM channels instead of reading the same offset of
-//    their rows. The sum order is fixed per wave, so results repeat exactly;
-//  * with KW > 1 waves per block, wave w takes the w-th of KW equal slices of the reduction
-//    (NB blocks of 128 from block kblk0) and the partial sums meet in LDS (`red`), where wave 0
-//    adds them in slice order and runs the epilogue. Short reductions then wait for one or two
-//    memory round trips per wave instead of one per pair of blocks.
-template <bool GATEUP, int NG, bool W8, int NB, int KW>
+//    their rows. The sum order is fixed per wave, so results repeat exactly.
+template <bool GATEUP, int NG, bool W8, int NB>
 __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
                                             const void* __restrict__ W0,
                                             const void* __restrict__ W1,
                                             const float* __restrict__ S0,
                                             const float* __restrict__ S1, int K, int N, int k,
                                             int e, const int* lr, int m0, int rows, int hbase,
-                                            uint16_t* __restrict__ h_out, const DownArgs& down,
-                                            int kblk0, float* red) {
+                                            uint16_t* __restrict__ h_out, const DownArgs& down) {
   constexpr int WR = W8 ? 2 : 4;              // weight registers (u32x4) per matrix per block
   const int lane = lane_id();
   const int l16 = lane & 15;
@@ -373,12 +364,12 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
     pa[g] = A + arow * K + kq;
   }
-  const int nb = NB > 0 ? NB : K / 128 / KW;  // even (checked by the launcher)
+  const int nb = NB > 0 ? NB : K / 128;       // even: K % 256 == 0 on this path
   const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
 
   u32x4 a[2][NG][4], bg[2][WR], bu[2][WR];     // two blocks in flight, slot = block % 2
   auto load = [&](int j, int sq) {
-    const int kb = ((sq + rot) % nb + kblk0) * 128;
+    const int kb = ((min(sq, nb - 1) + rot) % nb) * 128;  // past the end: re-read the last block
 #pragma unroll
     for (int c = 0; c < WR; ++c) {
       const int off = W8 ? kb + 16 * c : 2 * (kb + 32 * c);  // bytes
@@ -428,37 +419,8 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
       // sched_barrier keeps the scheduler from sinking the prefetch below the next compute
       compute(j);
       __builtin_amdgcn_sched_barrier(0);
-      if (sq + j + 2 < nb) load(j, sq + j + 2);
+      load(j, sq + j + 2);
       __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  if constexpr (KW > 1) {
-    constexpr int NV = NG * (GATEUP ? 8 : 4);  // partial sums per lane
-    const int wave = threadIdx.x / kWave;
-    __syncthreads();                           // wave 0 is done with the previous pass's sums
-    if (wave > 0) {
-      float* dst = red + (wave - 1) * NV * kWave + lane;
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dst[(4 * g + r) * kWave] = accg[g][r];
-          if constexpr (GATEUP) dst[(4 * NG + 4 * g + r) * kWave] = accu[g][r];
-        }
-    }
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 0; w < KW - 1; ++w) {
-      const float* src = red + w * NV * kWave + lane;
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          accg[g][r] += src[(4 * g + r) * kWave];
-          if constexpr (GATEUP) accu[g][r] += src[(4 * NG + 4 * g + r) * kWave];
-        }
     }
   }
 
@@ -633,20 +595,16 @@ __device__ __forceinline__ void stream_tile_q4(const uint16_t* __restrict__ A,
 // selection bias, read its weights once, at the cost of registers (fewer resident waves).
 // WF (WeightFormat): bf16 weights; int8 codes with fp32 row scales S0 (gate or down) and S1
 // (up); or packed 4-bit codes with (scale, bias) pairs S0 and S1.
-// KW waves per block split the reduction into equal slices (bf16 and int8 weights).
-template <bool GATEUP, int MAXG, int WF, int KW>
-__global__ __launch_bounds__(kWave * KW) void ffn_stream_kernel(
+template <bool GATEUP, int MAXG, int WF>
+__global__ __launch_bounds__(kWave) void ffn_stream_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ W0, const void* __restrict__ W1,
     const void* __restrict__ S0, const void* __restrict__ S1, int K, int N, int k,
     RowSource rs, uint16_t* __restrict__ h_out, DownArgs down) {
-  static_assert(KW == 1 || WF != kWQ4, "4-bit weights: one wave per block");
   __shared__ int lr[kMaxScanRows];
-  __shared__ int sh_count;
-  __shared__ float red[KW > 1 ? (KW - 1) * MAXG * 8 * kWave : 1];
   const int e = blockIdx.y;
   int count, hbase;
   if (rs.ids) {
-    count = scan_rows(rs.ids, rs.n_rows, e, lr, &sh_count);
+    count = scan_rows(rs.ids, rs.n_rows, e, lr);
     hbase = -1;
     if (rs.counts_out && blockIdx.x == 0 && threadIdx.x == 0) rs.counts_out[e] = count;
   } else {
@@ -675,18 +633,16 @@ __global__ __launch_bounds__(kWave * KW) void ffn_stream_kernel(
       constexpr bool W8 = WF == kWI8;
       const float* s0 = static_cast<const float*>(S0);
       const float* s1 = static_cast<const float*>(S1);
-      const int kblk0 = static_cast<int>(threadIdx.x / kWave) * (K / 128 / KW);
       auto tile = [&](auto nb_const) {
         constexpr int NB = decltype(nb_const)::value;
         if (MAXG > 1 && rows > 16)
-          stream_tile<GATEUP, MAXG, W8, NB, KW>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows,
-                                                hbase, h_out, down, kblk0, red);
+          stream_tile<GATEUP, MAXG, W8, NB>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
+                                            h_out, down);
         else
-          stream_tile<GATEUP, 1, W8, NB, KW>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
-                                             h_out, down, kblk0, red);
+          stream_tile<GATEUP, 1, W8, NB>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
+                                         h_out, down);
       };
-      switch (K / KW) {                        // blocks of 128 per wave
-        case 256: tile(std::integral_constant<int, 2>{}); break;
+      switch (K) {
         case 512: tile(std::integral_constant<int, 4>{}); break;
         case 1024: tile(std::integral_constant<int, 8>{}); break;
         case 2048: tile(std::integral_constant<int, 16>{}); break;
@@ -715,42 +671,6 @@ bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
 
 namespace {
 
-// Waves per streaming block (the reduction split into that many slices): the largest of 4 and 2
-// that leaves every wave an even number of 128-k blocks, for reductions of at most
-// kStreamSliceNb blocks and grids of at most kStreamMaxWaves waves; otherwise 1, as for 4-bit
-// weights. Short reductions are latency-bound (a few round trips per wave, with few experts
-// touched): zonos3mini decode (K = 1024 and 512) gained ~5 % per layer call. Long ones are
-// bandwidth-bound: on zonos2 decode (K = 2048) two slices were ~1 % slower with bf16 weights and
-// ~4 % with int8.
-constexpr int kStreamSliceNb = 8;
-constexpr long long kStreamMaxWaves = 8192;
-
-inline int stream_waves(int K, long long blocks, int wf) {
-  const int nb = K / 128;
-  if (wf == kWQ4 || nb > kStreamSliceNb) return 1;
-  for (int kw = 4; kw >= 2; kw /= 2)
-    if (nb % (2 * kw) == 0 && blocks * kw <= kStreamMaxWaves) return kw;
-  return 1;
-}
-
-template <bool GATEUP, int MAXG, int WF>
-hipError_t launch_stream_kernel(int kw, dim3 grid, hipStream_t s, const StageMarks& m,
-                                const uint16_t* A, const void* W0, const void* W1, const void* S0,
-                                const void* S1, int K, int N, int k, const RowSource& rs,
-                                uint16_t* h, const DownArgs& down) {
-  if constexpr (WF != kWQ4) {
-    if (kw == 4)
-      return launch_marked(ffn_stream_kernel<GATEUP, MAXG, WF, 4>, grid, dim3(4 * kWave), s, m,
-                           A, W0, W1, S0, S1, K, N, k, rs, h, down);
-    if (kw == 2)
-      return launch_marked(ffn_stream_kernel<GATEUP, MAXG, WF, 2>, grid, dim3(2 * kWave), s, m,
-                           A, W0, W1, S0, S1, K, N, k, rs, h, down);
-  }
-  if (kw != 1) return hipErrorInvalidValue;
-  return launch_marked(ffn_stream_kernel<GATEUP, MAXG, WF, 1>, grid, dim3(kWave), s, m, A, W0,
-                       W1, S0, S1, K, N, k, rs, h, down);
-}
-
 // Gate/up and down weight-streaming launches for one weight format. Two-group passes where every
 // block of the grid stays resident at their lower occupancy (gate/up: at most 2048 blocks;
 // down: at most 4096).
@@ -760,25 +680,23 @@ hipError_t launch_streaming(const uint16_t* x, const void* wg, const void* wu, c
                             const DownArgs& down, hipStream_t s, const StageMarks& gu,
                             const QuantWeights& qw) {
   const DownArgs none{};
-  const long long b_gu = static_cast<long long>(H / kStFeat) * E;
-  const long long b_dn = static_cast<long long>(d / kStFeat) * E;
   const dim3 g_gu(H / kStFeat, E), g_dn(d / kStFeat, E);
-  const int kw_gu = stream_waves(d, b_gu, WF), kw_dn = stream_waves(H, b_dn, WF);
+  const bool g2 = (H / kStFeat) * E <= 2048;
   const hipError_t err =
-      b_gu <= 2048
-          ? launch_stream_kernel<true, 2, WF>(kw_gu, g_gu, s, gu, x, wg, wu, qw.gate, qw.up, d, H,
-                                              k, rs, h, none)
-          : launch_stream_kernel<true, 1, WF>(kw_gu, g_gu, s, gu, x, wg, wu, qw.gate, qw.up, d, H,
-                                              k, rs, h, none);
+      g2 ? launch_marked(ffn_stream_kernel<true, 2, WF>, g_gu, dim3(kWave), s, gu, x, wg, wu,
+                         qw.gate, qw.up, d, H, k, rs, h, none)
+         : launch_marked(ffn_stream_kernel<true, 1, WF>, g_gu, dim3(kWave), s, gu, x, wg, wu,
+                         qw.gate, qw.up, d, H, k, rs, h, none);
   if (err != hipSuccess) return err;
   RowSource rs2 = rs;
   rs2.counts_out = nullptr;
-  const StageMarks no_marks{};
-  return b_dn <= 4096
-             ? launch_stream_kernel<false, 2, WF>(kw_dn, g_dn, s, no_marks, h, wd, nullptr,
-                                                  qw.down, nullptr, H, d, k, rs2, nullptr, down)
-             : launch_stream_kernel<false, 1, WF>(kw_dn, g_dn, s, no_marks, h, wd, nullptr,
-                                                  qw.down, nullptr, H, d, k, rs2, nullptr, down);
+  if ((d / kStFeat) * E <= 4096)
+    ffn_stream_kernel<false, 2, WF><<<g_dn, kWave, 0, s>>>(h, wd, nullptr, qw.down, nullptr, H, d,
+                                                           k, rs2, nullptr, down);
+  else
+    ffn_stream_kernel<false, 1, WF><<<g_dn, kWave, 0, s>>>(h, wd, nullptr, qw.down, nullptr, H, d,
+                                                           k, rs2, nullptr, down);
+  return hipGetLastError();
 }
 
 }  // namespace
