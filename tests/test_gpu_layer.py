@@ -62,6 +62,8 @@ EDGE = [
     ("prefill-few-rows-ragged", 777, 512, 16, 2, 512, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
     ("prefill-few-rows-hot-expert", 600, 1024, 8, 1, 512, orc.SOFTMAX, "bf16", None, "hot5"),
     ("prefill-zonos2-widths", 1200, 2048, 16, 1, 2816, orc.SOFTMAX, "bf16", None, None),
+    # many experts: 29 empty, 20 with 1..32 rows, 15 larger (one with 1212 rows)
+    ("prefill-small-experts", 1500, 256, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 2.0, None),
     # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
     ("prefill-xcd-hot-expert", 2000, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
     # k = 1 with H >= 1024: the down GEMM splits its reduction in two halves added into y; here

@@ -100,3 +100,35 @@ def test_expert_ffn_and_combine(case):
     assert eo_err <= tol * np.sqrt(np.mean(eo_ref ** 2)), eo_err
     y_err = np.abs(y.cpu().numpy() - y_ref).max()
     assert y_err <= tol * np.sqrt(np.mean(y_ref ** 2)), y_err
+
+
+def test_expert_ffn_small_and_large_experts():
+    """Prefill grouping (grouped GEMM) with expert counts of 0, 1, 31, 32, 33 rows and on both
+    sides of the 256-row tile (255, 256, 257), checked expert by expert."""
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    counts = np.array([0, 1, 31, 32, 33, 64, 100, 255, 256, 257, 300, 5, 17, 2, 0, 40])
+    E, k, d, H = len(counts), 1, 256, 512
+    T = int(counts.sum())
+    inp = gen.make_inputs_custom(T, d, E, k, H, orc.SOFTMAX, "bf16", seed=77)
+    dev = upload(inp)
+    rng = np.random.default_rng(5)
+    ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, k).astype(np.int64)
+    w = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    off, rows, pos = orc.permute_ref(ids, E)
+    eo = moe.moe_expert_ffn(dev["x"], dev["w_gate"], dev["w_up"], dev["w_down"], k,
+                            _t(off.astype(np.int32)), _t(rows.astype(np.int32)))
+    y = moe.moe_combine(eo, _t(pos.astype(np.int32)), _t(w))
+    torch.cuda.synchronize()
+    eo_ref = orc.expert_ffn_ref(inp.x, inp.w_gate, inp.w_up, inp.w_down, off, rows, k)
+    y_ref = orc.combine_ref(eo_ref, pos, w, k)
+    tol = TOL["bf16"]
+    eo_g = eo.cpu().numpy()
+    # every expert group on its own (a tile that misses an expert leaves its rows unset)
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        if b > a:
+            err = np.abs(eo_g[a:b] - eo_ref[a:b]).max()
+            assert err <= tol * np.sqrt(np.mean(eo_ref[a:b] ** 2)), (e, counts[e], err)
+    y_err = np.abs(y.cpu().numpy() - y_ref).max()
+    assert y_err <= tol * np.sqrt(np.mean(y_ref ** 2)), y_err
