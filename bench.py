@@ -401,9 +401,12 @@ def main():
         maxg = 2 if (H // 16) * E <= 2048 else 1
         roof["kernel"] = "ffn_stream_kernel<true, %d, %d>" % (
             maxg, {"native": 0, "int8": 1, "q4": 2}[args.weights])
+    elif inp.dtype == "bf16":
+        # 256 x 256 tiles with 64-wide K steps once the experts average a full 256-row tile
+        roof["kernel"] = ("gemm_dma_kernel<true, 256, 256, 2, 64, 64>" if T * k >= 256 * E
+                          else "gemm_dma_kernel<true, 256, 128, 3, 64, 32>")
     else:
-        roof["kernel"] = ("gemm_dma_kernel<true, 256, 128, 3, 64>" if inp.dtype == "bf16"
-                          else "ffn_f32_kernel<true>")
+        roof["kernel"] = "ffn_f32_kernel<true>"
     traffic = measured_traffic(roof["kernel"], args.workload + ("/" + args.weights if quant else ""))
     roof["traffic"] = traffic
     roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"

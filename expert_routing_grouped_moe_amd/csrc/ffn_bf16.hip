@@ -90,9 +90,14 @@ inline bool prefill_xcd_order(int rows, int E, int bm) {
 // Three slots of a 256 x 128 tile take 72 KB, so two blocks (16 waves, <= 128 VGPRs each) share
 // a CU and one block's barrier wait is covered by the other's products; measured faster than
 // 256 x 256 tiles at one block per CU despite the larger L2 traffic.
-constexpr int kDBK = 32;
+// BK = 64 (128-byte rows, eight pieces): piece p of row r sits at position p ^ ((r >> 1) & 7).
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(BK == 32 || BK == 64, "K step");
+  if constexpr (BK == 32) return ((r >> 1) ^ (r >> 2)) & 3;
+  else return (r >> 1) & 7;
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -129,7 +134,7 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool GATEUP, int BM, int BN, int RING, int WROWS>
+template <bool GATEUP, int BM, int BN, int RING, int WROWS, int BK>
 __global__ __launch_bounds__(BM / WROWS * (BN / 64) * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
@@ -142,11 +147,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
   constexpr int WN = BN / WNW;              // columns per wave
   constexpr int MB = WROWS / 16;            // 16-row blocks per wave
   constexpr int NBK = WN / 16;              // 16-column blocks per wave
-  constexpr int CHA = BM / 16, CHB = BN / 16;     // 1 KB chunks per K step
+  constexpr int RPC = 1024 / (2 * BK);            // rows per 1 KB chunk
+  constexpr int PCS = BK / 8;                     // 16-byte pieces per row
+  constexpr int CHA = BM / RPC, CHB = BN / RPC;   // 1 KB chunks per K step
   constexpr int CPW = (CHA + CHB) / NW;           // chunks per wave per K step
   static_assert((CHA + CHB) % NW == 0, "chunks split over the waves");
   static_assert(RING >= 2 && (RING - 2) * CPW < 64, "ring depth within the wait counter");
-  constexpr int STAGE = (BM + BN) * kDBK;         // bf16 elements per ring slot
+  constexpr int STAGE = (BM + BN) * BK;           // bf16 elements per ring slot
   constexpr int FEAT = GATEUP ? BN / 2 : BN;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
   static_assert(2 * (kMaxE + 1) * 4 <= STAGE * 2, "tile table fits one slot");
@@ -167,32 +174,32 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
   const int n0 = nt * FEAT;
   const long long wstride = static_cast<long long>(N) * K;
 
-  // this lane's source rows: chunk j = wave + NW c covers LDS rows 16 j .. 16 j + 15 of the
-  // step (A rows first, then B rows); lane i fills row 16 j + i / 4, position i % 4
+  // this lane's source rows: chunk j = wave + NW c covers LDS rows RPC j .. RPC j + RPC - 1 of
+  // the step (A rows first, then B rows); lane i fills row RPC j + i / PCS, position i % PCS
   const uint16_t* src[CPW];
   int ldsoff[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int j = wave + NW * c;
-    const int r = 16 * j + lane / 4;        // row of the step tile (A: < BM)
-    const int pos = lane & 3;
+    const int r = RPC * j + lane / PCS;     // row of the step tile (A: < BM)
+    const int pos = lane % PCS;
     if (j < CHA) {
       const int pr = ti.row0 + (r < ti.rows ? r : 0);
       const long long arow = GATEUP ? static_cast<long long>(sorted_rows[pr] / k) : pr;
-      src[c] = A + arow * K + ((pos ^ swz(r)) * 8);
+      src[c] = A + arow * K + ((pos ^ swz<BK>(r)) * 8);
     } else {
       const int rb = r - BM;
       const int f = min(n0 + (GATEUP ? (rb % FEAT) : rb), N - 1);
       const uint16_t* wsrc = (GATEUP && rb >= FEAT) ? W1 : W0;
-      src[c] = wsrc + ti.e * wstride + static_cast<long long>(f) * K + ((pos ^ swz(rb)) * 8);
+      src[c] = wsrc + ti.e * wstride + static_cast<long long>(f) * K + ((pos ^ swz<BK>(rb)) * 8);
     }
-    ldsoff[c] = 16 * j * kDBK;              // element offset of the chunk inside a slot
+    ldsoff[c] = RPC * j * BK;               // element offset of the chunk inside a slot
   }
-  const int nk = K / kDBK;
+  const int nk = K / BK;
   const uint32_t ring0 = lds_addr(ring);
   auto issue = [&](int kt) {
     const int slot = kt % RING;
-    const int k0 = min(kt, nk - 1) * kDBK;  // prologue past the end: re-read the last step
+    const int k0 = min(kt, nk - 1) * BK;    // prologue past the end: re-read the last step
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
       dma16(src[c] + k0, ring0 + 2u * static_cast<uint32_t>(slot * STAGE + ldsoff[c]));
@@ -208,16 +215,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
   const bool wave_live = live_mb > 0;
   const int l16 = lane & 15;
   const int q = lane >> 4;                  // 16-byte piece (k 8q .. 8q+7) of the MFMA step
+  // fragment offsets of the first 32-wide MFMA step of a slot; with BK = 64 the second step's
+  // pieces 4 + q sit at offset ^ 32 (the piece index's bit 2)
   int aoff[MB], boff[NBK];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int r = wm * WROWS + mb * 16 + l16;
-    aoff[mb] = r * kDBK + ((q ^ swz(r)) * 8);
+    aoff[mb] = r * BK + ((q ^ swz<BK>(r)) * 8);
   }
 #pragma unroll
   for (int cb = 0; cb < NBK; ++cb) {
     const int r = brow[cb] + l16;
-    boff[cb] = BM * kDBK + r * kDBK + ((q ^ swz(r)) * 8);
+    boff[cb] = BM * BK + r * BK + ((q ^ swz<BK>(r)) * 8);
   }
 
   f32x4 acc[MB][NBK];
@@ -228,15 +237,20 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
 
   auto compute = [&](int slot) {
     const uint16_t* st = &ring[slot * STAGE];
-    u32x4 bf[NBK], af[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) af[mb] = load16(st + aoff[mb]);
+    for (int sub = 0; sub < BK / 32; ++sub) {
+      const int x = 32 * sub;               // XOR on the element offset
+      u32x4 bf[NBK], af[MB];
 #pragma unroll
-    for (int cb = 0; cb < NBK; ++cb) bf[cb] = load16(st + boff[cb]);
+      for (int mb = 0; mb < MB; ++mb) af[mb] = load16(st + (aoff[mb] ^ x));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int cb = 0; cb < NBK; ++cb) bf[cb] = load16(st + (boff[cb] ^ x));
 #pragma unroll
-      for (int cb = 0; cb < NBK; ++cb) acc[mb][cb] = mfma16x16x32(af[mb], bf[cb], acc[mb][cb]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < NBK; ++cb)
+          acc[mb][cb] = mfma16x16x32(af[mb], bf[cb], acc[mb][cb]);
+    }
   };
 
   // issue order = step order; step kt is complete once at most (issued after it) * CPW of this
@@ -655,14 +669,24 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
 
 }  // namespace
 
-// Prefill tiles: 256 x 128, eight waves of 64 x 64, a 3-slot ring (72 KB, two blocks per CU).
-// Measured on the skewed prefill against 128 x 128 / 256 x 256 tiles, waves of 128 x 64 or
-// 32 x 64, 64-wide K steps and deeper rings at one block per CU: none faster, the two co-resident
-// blocks covering each other's barrier and LDS waits matter more than the LDS bytes per product.
+// Prefill tiles: 256 x 128, eight waves of 64 x 64, 32-wide K steps in a 3-slot ring (72 KB, two
+// blocks per CU). Measured on the skewed prefill against 128 x 128 / 256 x 256 tiles, waves of
+// 128 x 64 or 32 x 64, 64-wide K steps and deeper rings at one block per CU: none faster, the two
+// co-resident blocks covering each other's barrier and LDS waits.
 constexpr int kTileM = 256;
 constexpr int kTileN = 128;
 constexpr int kTileRing = 3;
 constexpr int kTileWaveRows = 64;
+constexpr int kTileK = 32;
+// The gate/up exception, once the experts average a full row tile (XCD-ordered tiles): 256 x 256
+// tiles with 64-wide K steps in a 2-slot ring (128 KB, one block of kWideWaveRows-row waves per
+// CU). The 128-byte row segments double the copy rate from L2 and the wider tile copies a third
+// less per product (skewed prefill gate/up: 215 against 233 us). The down projection keeps the
+// 256 x 128 tiles: its few wide tiles would fill the one-block slots badly.
+constexpr int kWideN = 256;
+constexpr int kWideRing = 2;
+constexpr int kWideK = 64;
+constexpr int kWideWaveRows = 64;
 
 bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
   const long long rows = static_cast<long long>(T) * k;
@@ -724,12 +748,21 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, co
   const long long mt = max_tiles(rows, E, kTileM);
   const bool xcd = prefill_xcd_order(rows, E, kTileM);
   const int ntn_gu = (H + kTileN / 2 - 1) / (kTileN / 2), ntn_dn = (d + kTileN - 1) / kTileN;
-  err = launch_marked(gemm_dma_kernel<true, kTileM, kTileN, kTileRing, kTileWaveRows>,
-                      dim3(static_cast<unsigned>(prefill_grid(mt, ntn_gu, xcd))), dim3(NT), s, gu,
-                      x, static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu), d, H,
-                      E, k, rs.offsets, rs.sorted_rows, h, none, xcd);
+  if (xcd) {
+    constexpr int NTW = kTileM / kWideWaveRows * (kWideN / 64) * kWave;
+    const int ntn_w = (H + kWideN / 2 - 1) / (kWideN / 2);
+    err = launch_marked(gemm_dma_kernel<true, kTileM, kWideN, kWideRing, kWideWaveRows, kWideK>,
+                        dim3(static_cast<unsigned>(prefill_grid(mt, ntn_w, xcd))), dim3(NTW), s,
+                        gu, x, static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
+                        d, H, E, k, rs.offsets, rs.sorted_rows, h, none, xcd);
+  } else {
+    err = launch_marked(gemm_dma_kernel<true, kTileM, kTileN, kTileRing, kTileWaveRows, kTileK>,
+                        dim3(static_cast<unsigned>(prefill_grid(mt, ntn_gu, xcd))), dim3(NT), s,
+                        gu, x, static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
+                        d, H, E, k, rs.offsets, rs.sorted_rows, h, none, xcd);
+  }
   if (err != hipSuccess) return err;
-  gemm_dma_kernel<false, kTileM, kTileN, kTileRing, kTileWaveRows>
+  gemm_dma_kernel<false, kTileM, kTileN, kTileRing, kTileWaveRows, kTileK>
       <<<static_cast<unsigned>(prefill_grid(mt, ntn_dn, xcd)), NT, 0, s>>>(
           h, static_cast<const uint16_t*>(wd), nullptr, H, d, E, k, rs.offsets, rs.sorted_rows,
           nullptr, down, xcd);
