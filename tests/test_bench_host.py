@@ -96,3 +96,9 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"] and msg["n_gpus"] == 2
+
+
+def test_spread(bench):
+    s = bench._spread([0.5, 0.1, 0.4, 0.2, 0.3])      # ms, unordered
+    assert s["median"] == pytest.approx(300.0) and s["n"] == 5
+    assert s["p10"] == pytest.approx(100.0) and s["p90"] == pytest.approx(500.0)
