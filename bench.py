@@ -51,12 +51,21 @@ KERNEL_SOURCES = ("expert_routing_grouped_moe_amd/csrc/ffn_bf16.hip",
                   "expert_routing_grouped_moe_amd/csrc/kernels.hpp")
 
 
+def _code_only(text: str) -> str:
+    """Source text without // and /* */ comments, whitespace runs collapsed: an edit of comments
+    or layout leaves the hash (and the counters it keys) valid."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,8 +15,10 @@
 //    rows itself (from the dispatch order, or by scanning the expert ids), so the decode layer
 //    needs no dispatch kernel.
 //  * prefill (many rows per expert): a grouped GEMM over the dispatch order with 256 x 128 block
-//    tiles, operands copied from global memory straight into a 3-slot LDS ring (no register
-//    staging), 8 waves of 64 x 64 each, two blocks per CU, tiles ordered per XCD for L2 reuse.
+//    tiles, operands copied from global memory straight into a 3-slot LDS ring of 32-wide K steps
+//    (no register staging), 8 waves of 64 x 64 each, two blocks per CU; once the experts average
+//    a full row tile the gate/up product switches to 256 x 256 tiles with 64-wide K steps (one
+//    block of 16 waves per CU) and the tiles are ordered per XCD for L2 reuse.
 #include <type_traits>
 
 #include "common.hpp"

@@ -102,3 +102,11 @@ def test_spread(bench):
     s = bench._spread([0.5, 0.1, 0.4, 0.2, 0.3])      # ms, unordered
     assert s["median"] == pytest.approx(300.0) and s["n"] == 5
     assert s["p10"] == pytest.approx(100.0) and s["p90"] == pytest.approx(500.0)
+
+
+def test_kernel_hash_ignores_comments_only(bench):
+    a = "int f(int x) { // doubles\n  return 2 * x; /* fast */ }\n"
+    b = "int f(int x) {\n  /* twice x */\n  return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
