@@ -112,7 +112,7 @@ def algorithmic(inp, counts, weights="native"):
     step_bytes = (touched * (3 * d * H * wb + (2 * H + d) * sb) + T * d * ab + E * d * ab +
                   T * d * 4 + rows * 8)
     step_flops = 6 * d * H * rows + 2 * T * d * E
-    # the gate/up kernel alone: its weights (and scales), the gathered x rows, the bf16 h it writes
+    # the gate/up kernel alone: its weights (and scales), the gathered x rows, the fp16 h it writes
     gu_bytes = touched * (2 * d * H * wb + 2 * H * sb) + rows * d * ab + rows * H * ab
     gu_flops = 4 * d * H * rows
     return dict(touched=touched, step_bytes=step_bytes, step_flops=step_flops, gu_bytes=gu_bytes,

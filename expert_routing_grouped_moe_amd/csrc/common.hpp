@@ -39,12 +39,42 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// fp32 -> fp16 bits, round to nearest even, saturated to +-65504 (no infinities from finite h);
+// NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_f16_bits_sat(float f) {
+  if (f != f) return 0x7e00;
+  const float c = fminf(fmaxf(f, -65504.0f), 65504.0f);
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(c));
+}
+
+// Eight bf16 values (four dwords, lowest first) as eight fp16 values. Exact for every bf16
+// value of magnitude >= 2^-17 and <= 65504 (fp16 holds bf16's 8 significant bits there); the
+// pack rounds toward zero, which only affects smaller, fp16-subnormal magnitudes.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xffff0000u);
+    out[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return out;
+}
+
 // D = A(16x32) * B(32x16) + C on the CDNA4 matrix cores, fp32 accumulate.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, eight consecutive k each
 // (k = 8 * (l / 16) + 0..7); it receives C rows 4 * (l / 16) + 0..3 of column (l % 16).
 // Any fixed lane->k assignment used identically for A and B gives the same sum over k.
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// The same product on fp16 operands (same lane layout).
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -1,7 +1,10 @@
 // bf16 expert FFN (steps 5-6) on the CDNA4 matrix cores, fp32 accumulation.
 //   gate/up:  h[p, n] = silu(x[t] . Wg[e, n]) * (x[t] . Wu[e, n])      (SwiGLU; audio.cpp PR #1271,
-//             "Summary"), t = sorted_rows[p] / k, h rounded to bf16
-//   down:     o[p, n] = h[p] . Wd[e, n]  -> expert_out, or weighted into y
+//             "Summary"), t = sorted_rows[p] / k, h rounded to fp16 (saturated at +-65504)
+//   down:     o[p, n] = h[p] . Wd[e, n]  -> expert_out, or weighted into y; fp16 operands (the
+//             bf16, int8 or 4-bit weights are converted exactly), fp32 accumulation. fp16's 11
+//             significant bits keep the rounding of h from dominating the error: rounded to bf16,
+//             h alone put the skewed prefill's largest output error at 0.0203 x output RMS.
 // Both are "NT" products: every operand row (token row, weight row) is contiguous along the
 // reduction index, as the 3-D expert stacks of zonos2.cpp INTERNALS ("Recommended: F16 spine +
 // K-quant experts") are stored.
@@ -247,11 +250,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
       for (int mb = 0; mb < MB; ++mb) af[mb] = load16(st + (aoff[mb] ^ x));
 #pragma unroll
       for (int cb = 0; cb < NBK; ++cb) bf[cb] = load16(st + (boff[cb] ^ x));
+      if constexpr (!GATEUP) {              // h is fp16: the bf16 weights go to fp16 (exact)
+#pragma unroll
+        for (int cb = 0; cb < NBK; ++cb) bf[cb] = bf16x8_to_f16x8(bf[cb]);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int cb = 0; cb < NBK; ++cb)
-          acc[mb][cb] = mfma16x16x32(af[mb], bf[cb], acc[mb][cb]);
+          acc[mb][cb] = GATEUP ? mfma16x16x32(af[mb], bf[cb], acc[mb][cb])
+                               : mfma16x16x32_f16(af[mb], bf[cb], acc[mb][cb]);
     }
   };
 
@@ -287,7 +295,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
           const int f = n0 + wn * (WN / 2) + cb * 16 + l16;
           if (f < N) {
             const float hv = silu(acc[mb][cb][r]) * acc[mb][cb + NBK / 2][r];
-            h_out[static_cast<long long>(p) * N + f] = f32_to_bf16_bits(hv);
+            h_out[static_cast<long long>(p) * N + f] = f32_to_f16_bits_sat(hv);
           }
         }
       } else {
@@ -332,6 +340,16 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t v, int sh) {
 __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 16), i8pair_to_bf16x2(w1, 0),
                i8pair_to_bf16x2(w1, 16)};
+}
+// The same codes as 8 fp16 values (exact), for products against the fp16 h.
+__device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t v, int sh) {
+  const float lo = static_cast<float>(static_cast<int8_t>(v >> sh));
+  const float hi = static_cast<float>(static_cast<int8_t>(v >> (sh + 8)));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+__device__ __forceinline__ u32x4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{i8pair_to_f16x2(w0, 0), i8pair_to_f16x2(w0, 16), i8pair_to_f16x2(w1, 0),
+               i8pair_to_f16x2(w1, 16)};
 }
 
 // Up to NG groups of 16 rows (entries m0 .. of the expert's row list) against this wave's 16
@@ -400,7 +418,8 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   auto wop = [&](const u32x4* b, int c) -> u32x4 {
     if constexpr (W8) {
       const u32x4 v = b[c >> 1];
-      return (c & 1) ? i8x8_to_bf16x8(v[2], v[3]) : i8x8_to_bf16x8(v[0], v[1]);
+      const uint32_t w0 = (c & 1) ? v[2] : v[0], w1 = (c & 1) ? v[3] : v[1];
+      return GATEUP ? i8x8_to_bf16x8(w0, w1) : i8x8_to_f16x8(w0, w1);
     } else {
       return b[c];
     }
@@ -411,16 +430,24 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // h is fp16, so the down product runs on fp16 operands, its weights converted exactly (bf16
+  // weights here, int8 codes in wop)
+  constexpr bool kF16Down = !GATEUP;
   auto compute = [&](int j) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 wg = wop(bg[j], c);
+      u32x4 wg = wop(bg[j], c);
       u32x4 wu = wg;
       if constexpr (GATEUP) wu = wop(bu[j], c);
+      if constexpr (kF16Down && !W8) wg = bf16x8_to_f16x8(wg);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        accg[g] = mfma16x16x32(a[j][g][c], wg, accg[g]);
-        if constexpr (GATEUP) accu[g] = mfma16x16x32(a[j][g][c], wu, accu[g]);
+        if constexpr (kF16Down) {
+          accg[g] = mfma16x16x32_f16(a[j][g][c], wg, accg[g]);
+        } else {
+          accg[g] = mfma16x16x32(a[j][g][c], wg, accg[g]);
+          if constexpr (GATEUP) accu[g] = mfma16x16x32(a[j][g][c], wu, accu[g]);
+        }
       }
     }
   };
@@ -450,7 +477,7 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
       const int hrow = hbase >= 0 ? hbase + li : lr[li];
       if constexpr (GATEUP) {
         const float hv = silu(sg * accg[g][r]) * (su * accu[g][r]);
-        h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
+        h_out[static_cast<long long>(hrow) * N + f] = f32_to_f16_bits_sat(hv);
       } else {
         const DownRow dr = down_row(down, lr[li], hrow, N);
         down_put(down, dr, f, sg * accg[g][r]);
@@ -460,10 +487,13 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
 }
 
 // Two 4-bit codes per 16-bit half: bits 4 m and 16 + 4 m of a packed word (see
-// moe_quantize_groups_q4) become the bf16 values 128 + code, exact (8 significant bits), with one
-// shift, one mask and one OR per pair.
-__device__ __forceinline__ u32x4 q4x8_to_bf16x8(uint32_t v) {
-  constexpr uint32_t kMask = 0x000F000Fu, kBase = 0x43004300u;  // bf16 128.0 in both halves
+// moe_quantize_groups_q4) become the bf16 values 128 + code (F16 = false), exact (8 significant
+// bits), or the fp16 values 1024 + code (F16 = true, for products against the fp16 h), exact
+// (11 significant bits), with one shift, one mask and one OR per pair.
+template <bool F16>
+__device__ __forceinline__ u32x4 q4x8_to_16x8(uint32_t v) {
+  constexpr uint32_t kMask = 0x000F000Fu;
+  constexpr uint32_t kBase = F16 ? 0x64006400u : 0x43004300u;  // 1024.0 / 128.0 in both halves
   return u32x4{(v & kMask) | kBase, ((v >> 4) & kMask) | kBase, ((v >> 8) & kMask) | kBase,
                ((v >> 12) & kMask) | kBase};
 }
@@ -471,9 +501,10 @@ __device__ __forceinline__ u32x4 q4x8_to_bf16x8(uint32_t v) {
 // stream_tile for 4-bit affine weights (groups of 64 along K, one bf16 (scale, bias) pair per
 // group, codes packed so that a lane's 16 bytes of a 128-k block are its four 8-k runs at
 // k = 32 c + 8 g: the bf16 k layout, so each MFMA step lies inside one group).
-// The MFMA sums x * (128 + q) over a group (R) and, against a B operand of ones, x alone (X);
-// with scale s and bias b the group's contribution is s * R + (b - 128 s) * X, folded into the
-// fp32 accumulator in the group's order. Codes are requested kQ4Ahead blocks ahead of use, token
+// The MFMA sums x * (c0 + q) over a group (R) and, against a B operand of ones, x alone (X),
+// with c0 = 128 (bf16 token rows, gate/up) or 1024 (fp16 h, down); with scale s and bias b the
+// group's contribution is s * R + (b - c0 s) * X, folded into the fp32 accumulator in the
+// group's order. Codes are requested kQ4Ahead blocks ahead of use, token
 // rows two blocks ahead; passes, rotation and the epilogue are as in stream_tile.
 constexpr int kQ4Ahead = 2;  // even: a block's token rows sit in slot (block % 2)
 
@@ -533,11 +564,18 @@ __device__ __forceinline__ void stream_tile_q4(const uint16_t* __restrict__ A,
     accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const u32x4 ones{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  // gate/up: bf16 x against bf16 128 + q; down: fp16 h against fp16 1024 + q
+  constexpr bool F16 = !GATEUP;
+  constexpr float kCodeBase = F16 ? 1024.f : 128.f;
+  constexpr uint32_t kOne = F16 ? 0x3C003C00u : 0x3F803F80u;  // 1.0 in both halves
+  const u32x4 ones{kOne, kOne, kOne, kOne};
+  auto mfma = [](u32x4 a, u32x4 b, f32x4 c) {
+    return F16 ? mfma16x16x32_f16(a, b, c) : mfma16x16x32(a, b, c);
+  };
   auto fold = [](f32x4& acc, const f32x4& r, const f32x4& xs, uint32_t pair) {
     const float sc = __uint_as_float(pair << 16);
     const float bs = __uint_as_float(pair & 0xffff0000u);
-    const float b2 = fmaf(-128.f, sc, bs);
+    const float b2 = fmaf(-kCodeBase, sc, bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, r[i], fmaf(b2, xs[i], acc[i]));
   };
@@ -554,14 +592,14 @@ __device__ __forceinline__ void stream_tile_q4(const uint16_t* __restrict__ A,
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int c = 2 * h + cc;
-        const u32x4 wg = q4x8_to_bf16x8(cg[jw][c]);
+        const u32x4 wg = q4x8_to_16x8<F16>(cg[jw][c]);
         u32x4 wu = wg;
-        if constexpr (GATEUP) wu = q4x8_to_bf16x8(cu[jw][c]);
+        if constexpr (GATEUP) wu = q4x8_to_16x8<F16>(cu[jw][c]);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          rg[g] = mfma16x16x32(a[ja][g][c], wg, rg[g]);
-          if constexpr (GATEUP) ru[g] = mfma16x16x32(a[ja][g][c], wu, ru[g]);
-          xs[g] = mfma16x16x32(a[ja][g][c], ones, xs[g]);
+          rg[g] = mfma(a[ja][g][c], wg, rg[g]);
+          if constexpr (GATEUP) ru[g] = mfma(a[ja][g][c], wu, ru[g]);
+          xs[g] = mfma(a[ja][g][c], ones, xs[g]);
         }
       }
 #pragma unroll
@@ -596,7 +634,7 @@ __device__ __forceinline__ void stream_tile_q4(const uint16_t* __restrict__ A,
       const int hrow = hbase >= 0 ? hbase + li : lr[li];
       if constexpr (GATEUP) {
         const float hv = silu(accg[g][r]) * accu[g][r];
-        h_out[static_cast<long long>(hrow) * N + f] = f32_to_bf16_bits(hv);
+        h_out[static_cast<long long>(hrow) * N + f] = f32_to_f16_bits_sat(hv);
       } else {
         const DownRow dr = down_row(down, lr[li], hrow, N);
         down_put(down, dr, f, accg[g][r]);

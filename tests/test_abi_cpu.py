@@ -48,7 +48,7 @@ def test_workspace_size():
     a = L.moe_workspace_size(64, 2048, 16, 2816, 1, 1)
     b = L.moe_workspace_size(128, 2048, 16, 2816, 1, 1)
     assert 0 < a < b
-    # h (bf16) alone is T*k*H*2 bytes
+    # h (2-byte fp16 on this path) alone is T*k*H*2 bytes
     assert a >= 64 * 2816 * 2
     # k >= 2 outside the weight-streaming path stages fp32 expert outputs: T*k*d*4 more bytes
     assert L.moe_workspace_size(64, 128, 8, 256, 2, 0) - L.moe_workspace_size(64, 128, 8, 256, 1, 0) \
