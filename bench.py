@@ -433,9 +433,10 @@ def main():
         roof["kernel"] = "ffn_stream_kernel<true, %d, %d>" % (
             maxg, {"native": 0, "int8": 1, "q4": 2}[args.weights])
     elif inp.dtype == "bf16":
-        # 256 x 256 tiles with 64-wide K steps once the experts average a full 256-row tile
+        # 256 x 256 tiles with 64-wide K steps once the experts average a full 256-row tile,
+        # 128 x 256 tiles with 32-wide K steps below that
         roof["kernel"] = ("gemm_dma_kernel<true, 256, 256, 2, 64, 64>" if T * k >= 256 * E
-                          else "gemm_dma_kernel<true, 256, 128, 3, 64, 32>")
+                          else "gemm_dma_kernel<true, 128, 256, 3, 64, 32>")
     else:
         roof["kernel"] = "ffn_f32_kernel<true>"
     traffic = measured_traffic(roof["kernel"], args.workload + ("/" + args.weights if quant else ""))

@@ -17,11 +17,11 @@
 //    flight, with the expert's token rows read alongside from L2. The block finds its expert's
 //    rows itself (from the dispatch order, or by scanning the expert ids), so the decode layer
 //    needs no dispatch kernel.
-//  * prefill (many rows per expert): a grouped GEMM over the dispatch order with 256 x 128 block
-//    tiles, operands copied from global memory straight into a 3-slot LDS ring of 32-wide K steps
-//    (no register staging), 8 waves of 64 x 64 each, two blocks per CU; once the experts average
-//    a full row tile the gate/up product switches to 256 x 256 tiles with 64-wide K steps (one
-//    block of 16 waves per CU) and the tiles are ordered per XCD for L2 reuse.
+//  * prefill (many rows per expert): a grouped GEMM over the dispatch order, operands copied
+//    from global memory straight into an LDS ring (no register staging), waves of 64 x 64: 128 x
+//    256 tiles with 32-wide K steps at two blocks per CU while the experts average less than a
+//    256-row tile; beyond that the tiles are ordered per XCD for L2 reuse, gate/up on 256 x 256
+//    tiles with 64-wide K steps (one block of 16 waves per CU) and down on 256 x 128 tiles.
 #include <type_traits>
 
 #include "common.hpp"
@@ -709,24 +709,22 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
 
 }  // namespace
 
-// Prefill tiles: 256 x 128, eight waves of 64 x 64, 32-wide K steps in a 3-slot ring (72 KB, two
-// blocks per CU). Measured on the skewed prefill against 128 x 128 / 256 x 256 tiles, waves of
-// 128 x 64 or 32 x 64, 64-wide K steps and deeper rings at one block per CU: none faster, the two
-// co-resident blocks covering each other's barrier and LDS waits.
+// Prefill tile configurations, chosen from the shape (eight or sixteen waves of 64 x 64, 3-slot
+// rings of 32-wide K steps at two blocks per CU unless stated otherwise):
+//  * fewer rows than a full 256-row tile per expert on average (plain tile order, zonos3mini
+//    prefill): 128 x 256 tiles for both products (gate/up: 128 gate + 128 up features). Against
+//    256 x 128 tiles the grid shrinks from 632 to ~440 blocks (one round of the block slots),
+//    small experts pad half as many rows, and each weight fragment of the down product is
+//    converted to fp16 by two waves instead of four: gate/up 55 -> 48 us, down 55 -> 47 us.
+//  * a full row tile per expert or more (XCD-ordered tiles, zonos2 skewed prefill): gate/up on
+//    256 x 256 tiles with 64-wide K steps in a 2-slot ring (128 KB, one block per CU): 128-byte row
+//    segments copy from L2 at twice the rate of 64-byte ones and the wider tile copies a third
+//    less per product (gate/up 215 against 233 us). The down product keeps 256 x 128 tiles
+//    (128 x 256: 185 against 166 us; 256 x 256 with one block per CU: 159 against 152 us).
+// Also measured slower on the skewed prefill: waves of 128 x 64 or 32 x 64, deeper rings, and
+// 64-wide K steps at 256 x 128 (one block per CU).
 constexpr int kTileM = 256;
-constexpr int kTileN = 128;
-constexpr int kTileRing = 3;
 constexpr int kTileWaveRows = 64;
-constexpr int kTileK = 32;
-// The gate/up exception, once the experts average a full row tile (XCD-ordered tiles): 256 x 256
-// tiles with 64-wide K steps in a 2-slot ring (128 KB, one block of kWideWaveRows-row waves per
-// CU). The 128-byte row segments double the copy rate from L2 and the wider tile copies a third
-// less per product (skewed prefill gate/up: 215 against 233 us). The down projection keeps the
-// 256 x 128 tiles: its few wide tiles would fill the one-block slots badly.
-constexpr int kWideN = 256;
-constexpr int kWideRing = 2;
-constexpr int kWideK = 64;
-constexpr int kWideWaveRows = 64;
 
 bool ffn_bf16_streaming(int T, int d, int E, int H, int k) {
   const long long rows = static_cast<long long>(T) * k;
@@ -763,6 +761,22 @@ hipError_t launch_streaming(const uint16_t* x, const void* wg, const void* wu, c
   return hipGetLastError();
 }
 
+// One grouped-GEMM launch: BM x BN tiles (gate/up: BN / 2 gate and BN / 2 up features) with
+// BK-wide K steps in a RING-slot ring, 64 x 64 waves.
+template <bool GATEUP, int BM, int BN, int RING, int BK>
+hipError_t launch_gemm(int rows, int E, bool xcd, hipStream_t s, const StageMarks& marks,
+                       const uint16_t* A, const void* W0, const void* W1, int K, int N, int k,
+                       const RowSource& rs, uint16_t* h, const DownArgs& down) {
+  constexpr int NT = BM / kTileWaveRows * (BN / 64) * kWave;
+  constexpr int FEAT = GATEUP ? BN / 2 : BN;
+  const int ntn = (N + FEAT - 1) / FEAT;
+  const long long grid = prefill_grid(max_tiles(rows, E, BM), ntn, xcd);
+  return launch_marked(gemm_dma_kernel<GATEUP, BM, BN, RING, kTileWaveRows, BK>,
+                       dim3(static_cast<unsigned>(grid)), dim3(NT), s, marks, A,
+                       static_cast<const uint16_t*>(W0), static_cast<const uint16_t*>(W1), K, N,
+                       E, k, rs.offsets, rs.sorted_rows, h, down, xcd);
+}
+
 }  // namespace
 
 hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, const void* wd,
@@ -783,30 +797,20 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, co
   }
   // quantised weights: weight-streaming shapes only (checked by the callers)
   if (qw.fmt != kWBf16) return hipErrorInvalidValue;
-  // grouped GEMM over the dispatch order; 1-D grid sized for the worst-case tile count
-  constexpr int NT = kTileM / kTileWaveRows * (kTileN / 64) * kWave;
-  const long long mt = max_tiles(rows, E, kTileM);
-  const bool xcd = prefill_xcd_order(rows, E, kTileM);
-  const int ntn_gu = (H + kTileN / 2 - 1) / (kTileN / 2), ntn_dn = (d + kTileN - 1) / kTileN;
-  if (xcd) {
-    constexpr int NTW = kTileM / kWideWaveRows * (kWideN / 64) * kWave;
-    const int ntn_w = (H + kWideN / 2 - 1) / (kWideN / 2);
-    err = launch_marked(gemm_dma_kernel<true, kTileM, kWideN, kWideRing, kWideWaveRows, kWideK>,
-                        dim3(static_cast<unsigned>(prefill_grid(mt, ntn_w, xcd))), dim3(NTW), s,
-                        gu, x, static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
-                        d, H, E, k, rs.offsets, rs.sorted_rows, h, none, xcd);
-  } else {
-    err = launch_marked(gemm_dma_kernel<true, kTileM, kTileN, kTileRing, kTileWaveRows, kTileK>,
-                        dim3(static_cast<unsigned>(prefill_grid(mt, ntn_gu, xcd))), dim3(NT), s,
-                        gu, x, static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
-                        d, H, E, k, rs.offsets, rs.sorted_rows, h, none, xcd);
+  // grouped GEMM over the dispatch order; 1-D grids sized for the worst-case tile count
+  const StageMarks no_marks{};
+  if (prefill_xcd_order(rows, E, kTileM)) {
+    err = launch_gemm<true, 256, 256, 2, 64>(rows, E, true, s, gu, x, wg, wu, d, H, k, rs, h,
+                                             none);
+    if (err != hipSuccess) return err;
+    return launch_gemm<false, 256, 128, 3, 32>(rows, E, true, s, no_marks, h, wd, nullptr, H, d,
+                                               k, rs, nullptr, down);
   }
+  err = launch_gemm<true, 128, 256, 3, 32>(rows, E, false, s, gu, x, wg, wu, d, H, k, rs, h,
+                                           none);
   if (err != hipSuccess) return err;
-  gemm_dma_kernel<false, kTileM, kTileN, kTileRing, kTileWaveRows, kTileK>
-      <<<static_cast<unsigned>(prefill_grid(mt, ntn_dn, xcd)), NT, 0, s>>>(
-          h, static_cast<const uint16_t*>(wd), nullptr, H, d, E, k, rs.offsets, rs.sorted_rows,
-          nullptr, down, xcd);
-  return hipGetLastError();
+  return launch_gemm<false, 128, 256, 3, 32>(rows, E, false, s, no_marks, h, wd, nullptr, H, d, k,
+                                             rs, nullptr, down);
 }
 
 }  // namespace moe
