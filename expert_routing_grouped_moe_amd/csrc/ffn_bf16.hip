@@ -84,18 +84,18 @@ inline bool prefill_xcd_order(int rows, int E, int bm) {
 }
 
 // Grouped GEMM with loads straight from global memory into LDS (global_load_lds_dwordx4: each
-// lane's 16 bytes land at base + 16 * lane, so one wave instruction fills 1 KB = 16 rows of a
-// 32-wide K step). A ring of RING K steps lives in LDS; the loads of step kt + RING - 1 are
-// issued right after the barrier that retires step kt - 1, so RING - 1 steps are in flight
-// behind the products. One barrier per K step. Waves of 64 x 64 outputs, (BM / 64) x (BN / 64)
-// of them per block.
-// LDS rows are 64 bytes (32 bf16); the four 16-byte pieces of row r sit at position
-// piece ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3, so a fragment read (16 consecutive rows, one
+// lane's 16 bytes land at base + 16 * lane, so one wave instruction fills 1 KB: 16 rows of a
+// 32-wide K step or 8 rows of a 64-wide one). A ring of RING K steps lives in LDS; the loads of
+// step kt + RING - 1 are issued right after the barrier that retires step kt - 1, so RING - 1
+// steps are in flight behind the products. One barrier per K step. Waves of WROWS x 64 outputs,
+// (BM / WROWS) x (BN / 64) of them per block.
+// An LDS row holds one K step of one operand row: 64 bytes for BK = 32, whose four 16-byte pieces
+// sit at position piece ^ (((r >> 1) ^ (r >> 2)) & 3), or 128 bytes for BK = 64, whose eight
+// pieces sit at piece ^ ((r >> 1) & 7); either way a fragment read (16 consecutive rows, one
 // piece) touches 16 distinct 16-byte bank groups.
-// Three slots of a 256 x 128 tile take 72 KB, so two blocks (16 waves, <= 128 VGPRs each) share
-// a CU and one block's barrier wait is covered by the other's products; measured faster than
-// 256 x 256 tiles at one block per CU despite the larger L2 traffic.
-// BK = 64 (128-byte rows, eight pieces): piece p of row r sits at position p ^ ((r >> 1) & 7).
+// Three slots of 32-wide steps of a 256 x 128 or 128 x 256 tile take 72 KB, so two blocks
+// (16 waves, <= 128 VGPRs each) share a CU and one block's barrier wait is covered by the other's
+// products; the 256 x 256 tile with 64-wide steps (two slots, 128 KB) runs one block per CU.
 
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
