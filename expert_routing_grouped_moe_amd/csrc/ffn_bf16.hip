@@ -1,8 +1,9 @@
 // bf16 expert FFN (steps 5-6) on the CDNA4 matrix cores, fp32 accumulation.
 //   gate/up:  h[p, n] = silu(x[t] . Wg[e, n]) * (x[t] . Wu[e, n])      (SwiGLU; audio.cpp PR #1271,
 //             "Summary"), t = sorted_rows[p] / k, h rounded to fp16 (saturated at +-65504)
-//   down:     o[p, n] = h[p] . Wd[e, n]  -> expert_out, or weighted into y; fp16 operands (the
-//             bf16, int8 or 4-bit weights are converted exactly), fp32 accumulation. fp16's 11
+//   down:     o[p, n] = h[p] . Wd[e, n]  -> expert_out, or weighted into y; fp16 operands (int8
+//             and 4-bit codes convert exactly, bf16 weights exactly for magnitudes 2^-17..65504,
+//             smaller ones toward zero), fp32 accumulation. fp16's 11
 //             significant bits keep the rounding of h from dominating the error: rounded to bf16,
 //             h alone put the skewed prefill's largest output error at 0.0203 x output RMS.
 // Both are "NT" products: every operand row (token row, weight row) is contiguous along the
@@ -250,7 +251,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
       for (int mb = 0; mb < MB; ++mb) af[mb] = load16(st + (aoff[mb] ^ x));
 #pragma unroll
       for (int cb = 0; cb < NBK; ++cb) bf[cb] = load16(st + (boff[cb] ^ x));
-      if constexpr (!GATEUP) {              // h is fp16: the bf16 weights go to fp16 (exact)
+      if constexpr (!GATEUP) {              // h is fp16: the bf16 weights go to fp16
 #pragma unroll
         for (int cb = 0; cb < NBK; ++cb) bf[cb] = bf16x8_to_f16x8(bf[cb]);
       }
@@ -430,7 +431,7 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // h is fp16, so the down product runs on fp16 operands, its weights converted exactly (bf16
+  // h is fp16, so the down product runs on fp16 operands, its weights converted to fp16 (bf16
   // weights here, int8 codes in wop)
   constexpr bool kF16Down = !GATEUP;
   auto compute = [&](int j) {

@@ -166,7 +166,8 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_counts, int T, in
  *   expert_out [T*k, d]   fp32 output, in grouped (sorted) order
  *   ws, ws_bytes          device workspace of at least moe_workspace_size(T, d, E, H, k, dtype)
  * bf16: products on MFMA with fp32 accumulation; h is rounded to fp16 (saturated at +-65504)
- * before the down matmul, which runs on fp16 operands (the bf16 weights convert exactly).
+ * before the down matmul, which runs on fp16 operands (bf16 weights convert exactly for
+ * magnitudes 2^-17..65504; smaller ones are rounded toward zero, an error below 2^-24).
  * fp32: fp32 FMA throughout.
  */
 int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* w_up,
