@@ -66,10 +66,10 @@ EDGE = [
     ("prefill-small-experts", 1500, 256, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 2.0, None),
     # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
     ("prefill-xcd-hot-expert", 2000, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
-    # k = 1 with H >= 1024: the down GEMM splits its reduction in two halves added into y; here
-    # with XCD-ordered tiles, one hot expert and a ragged last tile
-    ("prefill-split-down-hot", 2100, 256, 8, 1, 1024, orc.SOFTMAX, "bf16", None, "hot5"),
-    ("prefill-split-down-ragged", 333, 128, 4, 1, 1088, orc.SOFTMAX, "bf16", None, None),
+    # k = 1 with long down reductions (H >= 1024, 32 or 34 K steps; the weighted output is stored
+    # straight into y): XCD-ordered tiles with one hot expert, and a ragged last tile
+    ("prefill-long-down-hot", 2100, 256, 8, 1, 1024, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("prefill-long-down-ragged", 333, 128, 4, 1, 1088, orc.SOFTMAX, "bf16", None, None),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
     # few rows per expert with d, H multiples of 128: the weight-streaming expert kernels
     ("stream-k3", 40, 128, 16, 3, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
