@@ -2,8 +2,9 @@
 //   gate/up:  h[p, n] = silu(x[t] . Wg[e, n]) * (x[t] . Wu[e, n])      (SwiGLU; audio.cpp PR #1271,
 //             "Summary"), t = sorted_rows[p] / k, h rounded to fp16 (saturated at +-65504)
 //   down:     o[p, n] = h[p] . Wd[e, n]  -> expert_out, or weighted into y; fp16 operands (int8
-//             and 4-bit codes convert exactly, bf16 weights exactly for magnitudes 2^-17..65504,
-//             smaller ones toward zero), fp32 accumulation. fp16's 11
+//             codes convert exactly, bf16 weights exactly for magnitudes 2^-17..65504, smaller
+//             ones toward zero; 4-bit weights s * q + b are formed in fp32 and rounded to
+//             nearest fp16), fp32 accumulation. fp16's 11
 //             significant bits keep the rounding of h from dominating the error: rounded to bf16,
 //             h alone put the skewed prefill's largest output error at 0.0203 x output RMS.
 // Both are "NT" products: every operand row (token row, weight row) is contiguous along the
@@ -353,6 +354,34 @@ __device__ __forceinline__ u32x4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
                i8pair_to_f16x2(w1, 16)};
 }
 
+// 8 packed 4-bit codes (see moe_quantize_groups_q4: element 2 j is the nibble at bits 4 j, element
+// 2 j + 1 the one at bits 16 + 4 j) of one group, dequantised in fp32 as w = s * q + b (one
+// rounding) with the group's bf16 scale s (low half of `pair`) and bias b (high half), then
+// rounded to nearest fp16 (11 significant bits: rounded to bf16 instead, the weights' rounding
+// put zonos2 decode's largest output error at 0.0175 x output RMS, near the 2e-2 bound).
+__device__ __forceinline__ u32x4 q4x8_dequant(uint32_t v, uint32_t pair) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const float sc = __uint_as_float(pair << 16);
+  const float bs = __uint_as_float(pair & 0xffff0000u);
+  // even nibbles to the bytes of t[0], odd ones to t[1]: byte m of t[i] is nibble 2 m + i, so
+  // element pair j = (nibble j, nibble 4 + j) sits in bytes (j / 2, j / 2 + 2) of t[j % 2]
+  // (the masks are opaque to the compiler, which would otherwise fold each byte read back into a
+  // bit-field extract of v and spend an extra instruction per code instead of v_cvt_f32_ubyteN)
+  uint32_t t[2];
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t[0]) : "v"(v));
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t[1]) : "v"(v >> 4));
+  auto byte = [](uint32_t w, int m) { return static_cast<float>((w >> (8 * m)) & 0xffu); };
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = fmaf(sc, byte(t[j & 1], j >> 1), bs);
+    const float hi = fmaf(sc, byte(t[j & 1], (j >> 1) + 2), bs);
+    out[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+  }
+  return out;
+}
+
 // Up to NG groups of 16 rows (entries m0 .. of the expert's row list) against this wave's 16
 // features over the whole reduction length K, with no barrier and no LDS staging; the groups
 // share every weight load, so an expert with up to 16 NG rows reads its weights once:
@@ -360,35 +389,45 @@ __device__ __forceinline__ u32x4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
 //    bf16 weights: k = 32 c + 8 g, so each load instruction reads 64 contiguous bytes of each of
 //    16 rows; int8 weights (W8): k = 32 g + 8 c, so a lane's 32 code bytes of the block are
 //    contiguous (two 16-byte loads), converted to bf16 right before the MFMA and scaled per row
-//    in the epilogue. The A rows (a token row of x or a row of h, both L2-resident) are read
-//    with the same k layout, one piece per step, for every group;
+//    in the epilogue; 4-bit weights (W4): the bf16 k layout, a lane's 16 code bytes of the block
+//    in one load plus the (scale, bias) pairs of the block's two groups of 64, each weight formed
+//    as s * q + b in fp32 and rounded to fp16 right before the MFMA (q4x8_dequant), the gate/up's
+//    bf16 token rows converted to fp16 for these products. The A rows (a token row of x or a row
+//    of h, both L2-resident) are read with the same k layout, one piece per step, for every
+//    group;
 //  * two blocks are in flight ahead of use;
 //  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
 //    that concurrent waves spread over the HBM channels instead of reading the same offset of
 //    their rows. The sum order is fixed per wave, so results repeat exactly.
-template <bool GATEUP, int NG, bool W8, int NB>
+template <bool GATEUP, int NG, int WF, int NB>
 __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
                                             const void* __restrict__ W0,
                                             const void* __restrict__ W1,
-                                            const float* __restrict__ S0,
-                                            const float* __restrict__ S1, int K, int N, int k,
+                                            const void* __restrict__ S0,
+                                            const void* __restrict__ S1, int K, int N, int k,
                                             int e, const int* lr, int m0, int rows, int hbase,
                                             uint16_t* __restrict__ h_out, const DownArgs& down) {
-  constexpr int WR = W8 ? 2 : 4;              // weight registers (u32x4) per matrix per block
+  constexpr bool W8 = WF == kWI8, W4 = WF == kWQ4;
+  constexpr int WR = W8 ? 2 : (W4 ? 1 : 4);   // weight registers (u32x4) per matrix per block
   const int lane = lane_id();
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int kq = W8 ? 32 * grp : 8 * grp;     // lane's first k inside a 128-k block
   const int f = blockIdx.x * kStFeat + l16;  // weight row (N % 16 == 0)
   const long long row0 = static_cast<long long>(e) * N + f;
-  const long long wofs = row0 * K + kq;      // elements (bf16) or bytes (int8)
-  const char* pg = static_cast<const char*>(W0) + (W8 ? wofs : 2 * wofs);
-  const char* pu = GATEUP ? static_cast<const char*>(W1) + (W8 ? wofs : 2 * wofs) : nullptr;
+  // bytes: bf16 2 per weight, int8 1, 4-bit one half (a lane's 16 bytes of a block hold the
+  // codes of its k = 32 c + 8 g runs, as packed by moe_quantize_groups_q4)
+  const long long wofs = W4 ? row0 * (K / 2) + 16 * grp : (W8 ? row0 * K + kq : 2 * (row0 * K + kq));
+  const char* pg = static_cast<const char*>(W0) + wofs;
+  const char* pu = GATEUP ? static_cast<const char*>(W1) + wofs : nullptr;
   float sg = 1.f, su = 1.f;
   if constexpr (W8) {
-    sg = S0[row0];
-    if constexpr (GATEUP) su = S1[row0];
+    sg = static_cast<const float*>(S0)[row0];
+    if constexpr (GATEUP) su = static_cast<const float*>(S1)[row0];
   }
+  // 4-bit: the (scale, bias) pairs of a block's two groups of 64, per row
+  const uint32_t* qg = W4 ? static_cast<const uint32_t*>(S0) + row0 * (K / 64) : nullptr;
+  const uint32_t* qu = (W4 && GATEUP) ? static_cast<const uint32_t*>(S1) + row0 * (K / 64) : nullptr;
   // lanes past a group's rows read row 0 of that group (never stored: row i of the product
   // depends only on A row i; the duplicate reads coalesce); a group past all rows repeats group 0
   const uint16_t* pa[NG];
@@ -403,21 +442,29 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
 
   u32x4 a[2][NG][4], bg[2][WR], bu[2][WR];     // two blocks in flight, slot = block % 2
+  uint2 pgs[2], pus[2];                        // 4-bit: the block's (scale, bias) pairs
   auto load = [&](int j, int sq) {
-    const int kb = ((min(sq, nb - 1) + rot) % nb) * 128;  // past the end: re-read the last block
+    const int blk = (min(sq, nb - 1) + rot) % nb;  // past the end: re-read the last block
+    const int kb = blk * 128;
 #pragma unroll
     for (int c = 0; c < WR; ++c) {
-      const int off = W8 ? kb + 16 * c : 2 * (kb + 32 * c);  // bytes
+      const int off = W4 ? 64 * blk : (W8 ? kb + 16 * c : 2 * (kb + 32 * c));  // bytes
       bg[j][c] = load16(pg + off);
       if constexpr (GATEUP) bu[j][c] = load16(pu + off);
+    }
+    if constexpr (W4) {
+      pgs[j] = *reinterpret_cast<const uint2*>(qg + 2 * blk);
+      if constexpr (GATEUP) pus[j] = *reinterpret_cast<const uint2*>(qu + 2 * blk);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int g = 0; g < NG; ++g) a[j][g][c] = load16(pa[g] + kb + (W8 ? 8 * c : 32 * c));
   };
-  auto wop = [&](const u32x4* b, int c) -> u32x4 {
-    if constexpr (W8) {
+  auto wop = [&](const u32x4* b, int c, uint2 pr) -> u32x4 {
+    if constexpr (W4) {
+      return q4x8_dequant(b[0][c], c < 2 ? pr.x : pr.y);
+    } else if constexpr (W8) {
       const u32x4 v = b[c >> 1];
       const uint32_t w0 = (c & 1) ? v[2] : v[0], w1 = (c & 1) ? v[3] : v[1];
       return GATEUP ? i8x8_to_bf16x8(w0, w1) : i8x8_to_f16x8(w0, w1);
@@ -437,14 +484,18 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   auto compute = [&](int j) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      u32x4 wg = wop(bg[j], c);
+      u32x4 wg = wop(bg[j], c, pgs[j]);
       u32x4 wu = wg;
-      if constexpr (GATEUP) wu = wop(bu[j], c);
-      if constexpr (kF16Down && !W8) wg = bf16x8_to_f16x8(wg);
+      if constexpr (GATEUP) wu = wop(bu[j], c, pus[j]);
+      if constexpr (kF16Down && WF == kWBf16) wg = bf16x8_to_f16x8(wg);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if constexpr (kF16Down) {
           accg[g] = mfma16x16x32_f16(a[j][g][c], wg, accg[g]);
+        } else if constexpr (W4) {          // fp16 weights: the bf16 token rows go to fp16
+          const u32x4 av = bf16x8_to_f16x8(a[j][g][c]);
+          accg[g] = mfma16x16x32_f16(av, wg, accg[g]);
+          accu[g] = mfma16x16x32_f16(av, wu, accu[g]);
         } else {
           accg[g] = mfma16x16x32(a[j][g][c], wg, accg[g]);
           if constexpr (GATEUP) accu[g] = mfma16x16x32(a[j][g][c], wu, accu[g]);
@@ -487,163 +538,6 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   }
 }
 
-// Two 4-bit codes per 16-bit half: bits 4 m and 16 + 4 m of a packed word (see
-// moe_quantize_groups_q4) become the bf16 values 128 + code (F16 = false), exact (8 significant
-// bits), or the fp16 values 1024 + code (F16 = true, for products against the fp16 h), exact
-// (11 significant bits), with one shift, one mask and one OR per pair.
-template <bool F16>
-__device__ __forceinline__ u32x4 q4x8_to_16x8(uint32_t v) {
-  constexpr uint32_t kMask = 0x000F000Fu;
-  constexpr uint32_t kBase = F16 ? 0x64006400u : 0x43004300u;  // 1024.0 / 128.0 in both halves
-  return u32x4{(v & kMask) | kBase, ((v >> 4) & kMask) | kBase, ((v >> 8) & kMask) | kBase,
-               ((v >> 12) & kMask) | kBase};
-}
-
-// stream_tile for 4-bit affine weights (groups of 64 along K, one bf16 (scale, bias) pair per
-// group, codes packed so that a lane's 16 bytes of a 128-k block are its four 8-k runs at
-// k = 32 c + 8 g: the bf16 k layout, so each MFMA step lies inside one group).
-// The MFMA sums x * (c0 + q) over a group (R) and, against a B operand of ones, x alone (X),
-// with c0 = 128 (bf16 token rows, gate/up) or 1024 (fp16 h, down); with scale s and bias b the
-// group's contribution is s * R + (b - c0 s) * X, folded into the fp32 accumulator in the
-// group's order. Codes are requested kQ4Ahead blocks ahead of use, token
-// rows two blocks ahead; passes, rotation and the epilogue are as in stream_tile.
-constexpr int kQ4Ahead = 2;  // even: a block's token rows sit in slot (block % 2)
-
-template <bool GATEUP, int NG>
-__device__ __forceinline__ void stream_tile_q4(const uint16_t* __restrict__ A,
-                                               const uint8_t* __restrict__ W0,
-                                               const uint8_t* __restrict__ W1,
-                                               const uint32_t* __restrict__ P0,
-                                               const uint32_t* __restrict__ P1, int K, int N,
-                                               int k, int e, const int* lr, int m0, int rows,
-                                               int hbase, uint16_t* __restrict__ h_out,
-                                               const DownArgs& down) {
-  const int lane = lane_id();
-  const int l16 = lane & 15;
-  const int grp = lane >> 4;
-  const int f = blockIdx.x * kStFeat + l16;  // weight row (N % 16 == 0)
-  const long long row0 = static_cast<long long>(e) * N + f;
-  const uint8_t* pg = W0 + row0 * (K / 2) + 16 * grp;
-  const uint8_t* pu = GATEUP ? W1 + row0 * (K / 2) + 16 * grp : nullptr;
-  const uint32_t* qg = P0 + row0 * (K / 64);
-  const uint32_t* qu = GATEUP ? P1 + row0 * (K / 64) : nullptr;
-  const uint16_t* pa[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int gr = rows - 16 * g;
-    const int li_a = m0 + (gr > 0 ? 16 * g + (l16 < gr ? l16 : 0) : 0);
-    const long long arow = GATEUP ? lr[li_a] / k : (hbase >= 0 ? hbase + li_a : lr[li_a]);
-    pa[g] = A + arow * K + 8 * grp;
-  }
-  const int nb = K / 128;
-  const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
-
-  // codes and (scale, bias) words kQ4Ahead blocks ahead, token rows two blocks ahead (measured:
-  // four or eight blocks of codes ahead cost more in occupancy than they gain in latency)
-  u32x4 a[2][NG][4], cg[kQ4Ahead], cu[kQ4Ahead];
-  uint2 sg[kQ4Ahead], su[kQ4Ahead];           // (scale, bias) words of the block's two groups
-  auto blk = [&](int sq) { return (min(sq, nb - 1) + rot) % nb; };  // past the end: the last block
-  auto load_w = [&](int j, int sq) {
-    const int b = blk(sq);
-    cg[j] = load16(pg + 64 * b);
-    sg[j] = *reinterpret_cast<const uint2*>(qg + 2 * b);
-    if constexpr (GATEUP) {
-      cu[j] = load16(pu + 64 * b);
-      su[j] = *reinterpret_cast<const uint2*>(qu + 2 * b);
-    }
-  };
-  auto load_a = [&](int j, int sq) {
-    const int b = blk(sq);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int g = 0; g < NG; ++g) a[j][g][c] = load16(pa[g] + 128 * b + 32 * c);
-  };
-  f32x4 accg[NG], accu[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    accg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // gate/up: bf16 x against bf16 128 + q; down: fp16 h against fp16 1024 + q
-  constexpr bool F16 = !GATEUP;
-  constexpr float kCodeBase = F16 ? 1024.f : 128.f;
-  constexpr uint32_t kOne = F16 ? 0x3C003C00u : 0x3F803F80u;  // 1.0 in both halves
-  const u32x4 ones{kOne, kOne, kOne, kOne};
-  auto mfma = [](u32x4 a, u32x4 b, f32x4 c) {
-    return F16 ? mfma16x16x32_f16(a, b, c) : mfma16x16x32(a, b, c);
-  };
-  auto fold = [](f32x4& acc, const f32x4& r, const f32x4& xs, uint32_t pair) {
-    const float sc = __uint_as_float(pair << 16);
-    const float bs = __uint_as_float(pair & 0xffff0000u);
-    const float b2 = fmaf(-kCodeBase, sc, bs);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, r[i], fmaf(b2, xs[i], acc[i]));
-  };
-  auto compute = [&](int ja, int jw) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {             // the block's two groups of 64
-      f32x4 rg[NG], ru[NG], xs[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        rg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ru[g] = rg[g];
-        xs[g] = rg[g];
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int c = 2 * h + cc;
-        const u32x4 wg = q4x8_to_16x8<F16>(cg[jw][c]);
-        u32x4 wu = wg;
-        if constexpr (GATEUP) wu = q4x8_to_16x8<F16>(cu[jw][c]);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          rg[g] = mfma(a[ja][g][c], wg, rg[g]);
-          if constexpr (GATEUP) ru[g] = mfma(a[ja][g][c], wu, ru[g]);
-          xs[g] = mfma(a[ja][g][c], ones, xs[g]);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        fold(accg[g], rg[g], xs[g], h ? sg[jw].y : sg[jw].x);
-        if constexpr (GATEUP) fold(accu[g], ru[g], xs[g], h ? su[jw].y : su[jw].x);
-      }
-    }
-  };
-#pragma unroll
-  for (int j = 0; j < kQ4Ahead; ++j) load_w(j, j);
-  load_a(0, 0);
-  load_a(1, 1);
-  for (int b0 = 0; b0 < nb; b0 += kQ4Ahead) {
-#pragma unroll
-    for (int j = 0; j < kQ4Ahead; ++j) {      // block b0 + j: codes in slot j, rows in slot j % 2
-      if (b0 + j < nb) compute(j % 2, j);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(j, b0 + j + kQ4Ahead);
-      load_a(j % 2, b0 + j + 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * g + (lane >> 4) * 4 + r;
-      if (i >= rows) continue;
-      const int li = m0 + i;
-      const int hrow = hbase >= 0 ? hbase + li : lr[li];
-      if constexpr (GATEUP) {
-        const float hv = silu(accg[g][r]) * accu[g][r];
-        h_out[static_cast<long long>(hrow) * N + f] = f32_to_f16_bits_sat(hv);
-      } else {
-        const DownRow dr = down_row(down, lr[li], hrow, N);
-        down_put(down, dr, f, accg[g][r]);
-      }
-    }
-  }
-}
-
 // Grid (N / 16, E), one wave per block: block (x, e) computes features [16 x, 16 x + 16) of
 // expert e for all of the expert's rows, up to 16 MAXG rows per pass over the weights (a further
 // pass mostly hits the caches). MAXG = 2 lets an expert with 17..32 rows, common under a
@@ -671,39 +565,23 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
   // passes of up to 16 MAXG rows: the 16-row groups of a pass share each weight load
   for (int m0 = 0; m0 < count; m0 += 16 * MAXG) {
     const int rows = min(16 * MAXG, count - m0);
-    if constexpr (WF == kWQ4) {
-      const uint8_t* c0 = static_cast<const uint8_t*>(W0);
-      const uint8_t* c1 = static_cast<const uint8_t*>(W1);
-      const uint32_t* p0 = static_cast<const uint32_t*>(S0);
-      const uint32_t* p1 = static_cast<const uint32_t*>(S1);
+    // the reduction loop fully unrolled for the expert widths of the two models (nb blocks of
+    // 128)
+    auto tile = [&](auto nb_const) {
+      constexpr int NB = decltype(nb_const)::value;
       if (MAXG > 1 && rows > 16)
-        stream_tile_q4<GATEUP, MAXG>(A, c0, c1, p0, p1, K, N, k, e, lr, m0, rows, hbase, h_out,
-                                     down);
+        stream_tile<GATEUP, MAXG, WF, NB>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase,
+                                          h_out, down);
       else
-        stream_tile_q4<GATEUP, 1>(A, c0, c1, p0, p1, K, N, k, e, lr, m0, rows, hbase, h_out, down);
-    } else {
-      // the reduction loop fully unrolled for the expert widths of the two models (nb blocks of
-      // 128); the 4-bit loop stays rolled: unrolled, the scheduler hoists the small code loads of
-      // every block to the front and the kernel spills
-      constexpr bool W8 = WF == kWI8;
-      const float* s0 = static_cast<const float*>(S0);
-      const float* s1 = static_cast<const float*>(S1);
-      auto tile = [&](auto nb_const) {
-        constexpr int NB = decltype(nb_const)::value;
-        if (MAXG > 1 && rows > 16)
-          stream_tile<GATEUP, MAXG, W8, NB>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
-                                            h_out, down);
-        else
-          stream_tile<GATEUP, 1, W8, NB>(A, W0, W1, s0, s1, K, N, k, e, lr, m0, rows, hbase,
-                                         h_out, down);
-      };
-      switch (K) {
-        case 512: tile(std::integral_constant<int, 4>{}); break;
-        case 1024: tile(std::integral_constant<int, 8>{}); break;
-        case 2048: tile(std::integral_constant<int, 16>{}); break;
-        case 2816: tile(std::integral_constant<int, 22>{}); break;
-        default: tile(std::integral_constant<int, 0>{}); break;
-      }
+        stream_tile<GATEUP, 1, WF, NB>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase,
+                                       h_out, down);
+    };
+    switch (K) {
+      case 512: tile(std::integral_constant<int, 4>{}); break;
+      case 1024: tile(std::integral_constant<int, 8>{}); break;
+      case 2048: tile(std::integral_constant<int, 16>{}); break;
+      case 2816: tile(std::integral_constant<int, 22>{}); break;
+      default: tile(std::integral_constant<int, 0>{}); break;
     }
   }
 }
