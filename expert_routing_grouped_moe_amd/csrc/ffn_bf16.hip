@@ -3,8 +3,8 @@
 //             "Summary"), t = sorted_rows[p] / k, h rounded to fp16 (saturated at +-65504)
 //   down:     o[p, n] = h[p] . Wd[e, n]  -> expert_out, or weighted into y; fp16 operands (int8
 //             codes convert exactly, bf16 weights exactly for magnitudes 2^-17..65504, smaller
-//             ones toward zero; 4-bit weights s * q + b are formed in fp32 and rounded to
-//             nearest fp16), fp32 accumulation. fp16's 11
+//             ones toward zero; 4-bit weights s * q + b are formed with one fp16 fused
+//             multiply-add), fp32 accumulation. fp16's 11
 //             significant bits keep the rounding of h from dominating the error: rounded to bf16,
 //             h alone put the skewed prefill's largest output error at 0.0203 x output RMS.
 // Both are "NT" products: every operand row (token row, weight row) is contiguous along the
@@ -355,29 +355,28 @@ __device__ __forceinline__ u32x4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
 }
 
 // 8 packed 4-bit codes (see moe_quantize_groups_q4: element 2 j is the nibble at bits 4 j, element
-// 2 j + 1 the one at bits 16 + 4 j) of one group, dequantised in fp32 as w = s * q + b (one
-// rounding) with the group's bf16 scale s (low half of `pair`) and bias b (high half), then
-// rounded to nearest fp16 (11 significant bits: rounded to bf16 instead, the weights' rounding
-// put zonos2 decode's largest output error at 0.0175 x output RMS, near the 2e-2 bound).
+// 2 j + 1 the one at bits 16 + 4 j, so both halves of a dword belong to one group) dequantised as
+// w = s * q + b with the group's bf16 scale s (low half of `pair`) and bias b (high half): one
+// packed fp16 fused multiply-add per pair, rounded once to nearest fp16 (s and b convert to fp16
+// exactly for magnitudes 2^-14..65504). 11 significant bits: rounded to bf16 instead, the
+// weights' rounding put zonos2 decode's largest output error at 0.0175 x output RMS, near the
+// 2e-2 bound.
 __device__ __forceinline__ u32x4 q4x8_dequant(uint32_t v, uint32_t pair) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   const float sc = __uint_as_float(pair << 16);
   const float bs = __uint_as_float(pair & 0xffff0000u);
-  // even nibbles to the bytes of t[0], odd ones to t[1]: byte m of t[i] is nibble 2 m + i, so
-  // element pair j = (nibble j, nibble 4 + j) sits in bytes (j / 2, j / 2 + 2) of t[j % 2]
-  // (the masks are opaque to the compiler, which would otherwise fold each byte read back into a
-  // bit-field extract of v and spend an extra instruction per code instead of v_cvt_f32_ubyteN)
-  uint32_t t[2];
-  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t[0]) : "v"(v));
-  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t[1]) : "v"(v >> 4));
-  auto byte = [](uint32_t w, int m) { return static_cast<float>((w >> (8 * m)) & 0xffu); };
+  const f16x2 s2 = __builtin_convertvector(f32x2{sc, sc}, f16x2);
+  const f16x2 b2 = __builtin_convertvector(f32x2{bs, bs}, f16x2);
+  const f16x2 base{static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lo = fmaf(sc, byte(t[j & 1], j >> 1), bs);
-    const float hi = fmaf(sc, byte(t[j & 1], (j >> 1) + 2), bs);
-    out[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+    // the pair's codes as the fp16 values 1024 + q (exact), less 1024 (exact), then s * q + b
+    // with one rounding
+    const uint32_t m = ((v >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+    const f16x2 q = __builtin_bit_cast(f16x2, m) - base;
+    out[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
   }
   return out;
 }
@@ -391,7 +390,7 @@ __device__ __forceinline__ u32x4 q4x8_dequant(uint32_t v, uint32_t pair) {
 //    contiguous (two 16-byte loads), converted to bf16 right before the MFMA and scaled per row
 //    in the epilogue; 4-bit weights (W4): the bf16 k layout, a lane's 16 code bytes of the block
 //    in one load plus the (scale, bias) pairs of the block's two groups of 64, each weight formed
-//    as s * q + b in fp32 and rounded to fp16 right before the MFMA (q4x8_dequant), the gate/up's
+//    as s * q + b in fp16 right before the MFMA (q4x8_dequant), the gate/up's
 //    bf16 token rows converted to fp16 for these products. The A rows (a token row of x or a row
 //    of h, both L2-resident) are read with the same k layout, one piece per step, for every
 //    group;

@@ -219,9 +219,9 @@ typedef struct moe_layer_args {
      w_dtype = MOE_Q4 (ABI 3): w_gate, w_up and w_down hold packed 4-bit codes ([E,H,d/2],
      [E,H,d/2], [E,d,H/2] bytes) and the quantisation arrays their uint32 (scale, bias) pairs
      ([E,H,d/64], [E,H,d/64], [E,d,H/64]), both as written by moe_quantize_groups_q4; the layer
-     computes with the weights scale * code + bias of each group, each formed in fp32 and rounded
-     to nearest fp16 for the matrix cores (the gate/up products convert the bf16 token rows to
-     fp16, exactly for magnitudes 2^-14..65504).
+     computes with the weights scale * code + bias of each group, each formed by one fp16 fused
+     multiply-add (rounded to nearest) for the matrix cores (scale, bias and the gate/up products'
+     bf16 token rows convert to fp16 exactly for magnitudes 2^-14..65504).
      These quantised decode paths (fewer bytes per weight: the pages run quantised expert stacks
      for decode, ZONOS2-4bit MLX card, "Performance notes" and "Quantization recipe"; zonos2.cpp
      INTERNALS, "Recommended: F16 spine + K-quant experts") need dtype = MOE_BF16 and the
