@@ -104,6 +104,9 @@ EDGE = [
     ("E256-k8", 64, 256, 256, 8, 256, orc.SELECTED_SOFTMAX, 0.5, None),
     ("hot-expert", 200, 256, 16, 1, 256, orc.SOFTMAX, None, "hot5"),     # many passes
     ("rows-17-32", 96, 256, 8, 2, 512, orc.SELECTED_SOFTMAX, 0.5, None),  # two-group passes
+    # d = H = 768: six 128-k blocks per row, outside the unrolled widths, so the reduction loop
+    # runs rolled over three trips with the prefetch carried across its back edge
+    ("generic-K768", 48, 768, 16, 2, 768, orc.SELECTED_SOFTMAX, 0.5, None),
 ]
 
 
