@@ -71,11 +71,13 @@ EDGE = [
     ("prefill-long-down-hot", 2100, 256, 8, 1, 1024, orc.SOFTMAX, "bf16", None, "hot5"),
     ("prefill-long-down-ragged", 333, 128, 4, 1, 1088, orc.SOFTMAX, "bf16", None, None),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
-    # few rows per expert with d, H multiples of 128: the weight-streaming expert kernels
-    ("stream-k3", 40, 128, 16, 3, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
-    ("stream-E256-k8", 64, 256, 256, 8, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
-    ("stream-hot-expert", 200, 128, 16, 1, 128, orc.SOFTMAX, "bf16", None, "hot5"),
-    ("stream-max-rows", 1024, 128, 64, 2, 128, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    # few rows per expert (T*k <= 2048 and <= 32 E) with d, H multiples of 256: the
+    # weight-streaming expert kernels (checked below); d = H = 768 runs their reduction loop rolled
+    ("stream-k3", 40, 256, 16, 3, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("stream-E256-k8", 64, 256, 256, 8, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("stream-hot-expert", 200, 256, 16, 1, 256, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("stream-max-rows", 1024, 256, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
+    ("stream-generic-K768", 48, 768, 16, 2, 768, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
     # the split router (few tokens, router matrix >= 64K elements): ragged T, and d wide enough
     # for slices wider than 256
     ("split-router-ragged", 37, 1024, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 0.5, None),
@@ -90,6 +92,8 @@ EDGE = [
 @pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
 def test_layer_edge_cases(case):
     name, T, d, E, k, H, scoring, dtype, sbv, rb = case
+    if name.startswith("stream-"):  # the shape rule of the weight-streaming path
+        assert T * k <= 2048 and T * k <= 32 * E and d % 256 == 0 and H % 256 == 0, name
     router_bias = None
     if rb == "hot5":
         router_bias = np.full(E, -30.0, np.float32)
