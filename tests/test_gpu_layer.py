@@ -65,7 +65,7 @@ EDGE = [
     # many experts: 29 empty, 20 with 1..32 rows, 15 larger (one with 1212 rows)
     ("prefill-small-experts", 1500, 256, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 2.0, None),
     # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
-    ("prefill-xcd-hot-expert", 2000, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
+    ("prefill-xcd-hot-expert", 2100, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
     # k = 1 with long down reductions (H >= 1024, 32 or 34 K steps; the weighted output is stored
     # straight into y): XCD-ordered tiles with one hot expert, and a ragged last tile
     ("prefill-long-down-hot", 2100, 256, 8, 1, 1024, orc.SOFTMAX, "bf16", None, "hot5"),
@@ -94,6 +94,8 @@ def test_layer_edge_cases(case):
     name, T, d, E, k, H, scoring, dtype, sbv, rb = case
     if name.startswith("stream-"):  # the shape rule of the weight-streaming path
         assert T * k <= 2048 and T * k <= 32 * E and d % 256 == 0 and H % 256 == 0, name
+    if "xcd" in name:               # XCD-ordered tiles: a full 256-row tile per expert or more
+        assert T * k >= 256 * E, name
     router_bias = None
     if rb == "hot5":
         router_bias = np.full(E, -30.0, np.float32)
