@@ -66,10 +66,11 @@ def test_permute_all_to_one_expert_and_empty():
 
 
 FFN_CASES = [
-    # name, T, d, E, k, H, dtype   (avg rows per expert decides decode vs prefill kernels)
+    # name, T, d, E, k, H, dtype: "decode" cases take the weight-streaming kernels (T*k <= 2048
+    # and <= 32 E, d and H multiples of 256), "prefill" ones the grouped GEMM (checked below)
     ("f32-tiny", 64, 128, 8, 1, 256, "f32"),
     ("f32-ragged", 37, 64, 5, 3, 96, "f32"),
-    ("bf16-decode-k1", 64, 512, 16, 1, 384, "bf16"),
+    ("bf16-decode-k1", 64, 512, 16, 1, 512, "bf16"),
     ("bf16-decode-k2", 64, 256, 64, 2, 256, "bf16"),
     ("bf16-decode-mt2", 300, 256, 16, 1, 256, "bf16"),
     ("bf16-prefill", 700, 256, 4, 2, 384, "bf16"),
@@ -81,7 +82,9 @@ FFN_CASES = [
 def test_expert_ffn_and_combine(case):
     import torch
     from expert_routing_grouped_moe_amd import moe
-    _, T, d, E, k, H, dtype = case
+    name, T, d, E, k, H, dtype = case
+    streaming = T * k <= 2048 and T * k <= 32 * E and d % 256 == 0 and H % 256 == 0
+    assert streaming == ("decode" in name) or dtype == "f32", name
     inp = gen.make_inputs_custom(T, d, E, k, H, orc.SOFTMAX, dtype, seed=T + d + E)
     dev = upload(inp)
     # routing from the oracle (fp64 logits), so the FFN sees exactly the oracle's grouping
