@@ -382,18 +382,26 @@ def decided_tokens(scores64, k, bound):
 
 
 def selection_admissible(scores64, k, bound, ids):
-    """For an undecided token, a selection is admissible when its k experts are distinct and each
-    scores within 2*bound of the k-th best fp64 score."""
+    """Whether a selection could come from an fp32 evaluation whose rank scores are each within
+    `bound` of the exact ones. Two such scores can swap order only when the exact ones lie within
+    2*bound of each other, so, with kth the k-th best exact score, a selection is admissible when
+    its k experts are distinct, every expert scoring above kth + 2*bound is among them (no k
+    others can overtake it), and none scores below kth - 2*bound (it cannot overtake the k
+    experts above it)."""
     s = np.asarray(scores64, dtype=f64)
     srt = -np.sort(-s, axis=1)
     kth = srt[:, k - 1]
     ok = np.ones(s.shape[0], dtype=bool)
     for t in range(s.shape[0]):
         sel = [int(v) for v in ids[t]]
+        band = 2.0 * float(bound[t])
         if len(set(sel)) != k:
             ok[t] = False
             continue
-        for e in sel:
-            if s[t, e] < kth[t] - 2.0 * bound[t]:
-                ok[t] = False
+        if any(s[t, e] < kth[t] - band for e in sel):
+            ok[t] = False
+            continue
+        sure = [e for e in range(s.shape[1]) if s[t, e] > kth[t] + band]
+        if any(e not in sel for e in sure):
+            ok[t] = False
     return ok

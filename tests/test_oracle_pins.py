@@ -109,6 +109,43 @@ def test_hand_q4_packing(hand):
     assert sorted(nib.tolist()) == sorted(q[0].tolist())
 
 
+def test_hand_q4_param_words(hand):
+    c = hand["q4_affine_groups"]
+    _, s, b = orc.quantize_groups_q4_ref(_q4_hand_row(c))
+    words = orc.pack_q4_params_ref(s, b)
+    assert words.dtype == np.uint32 and words.shape == (1, 4)
+    assert [int(v) for v in words[0]] == [int(w, 16) for w in c["param_words"]["group_words"]]
+    pair = c["param_words"]["pair"]
+    one = orc.pack_q4_params_ref(np.float32([_ev(pair["s"])]), np.float32([_ev(pair["b"])]))
+    assert int(one[0]) == int(pair["word"], 16)
+
+
+def test_hand_expert_counts():
+    # counts written out by hand: ids [[0],[2],[2],[1],[2]] over 4 experts -> 1, 1, 3, 0; a
+    # top-2 case [[3,0],[0,3],[4,3]] over 5 experts -> 2, 0, 0, 3, 1
+    c1 = orc.expert_counts_ref(np.array([[0], [2], [2], [1], [2]]), 4)
+    assert c1.tolist() == [1, 1, 3, 0]
+    c2 = orc.expert_counts_ref(np.array([[3, 0], [0, 3], [4, 3]]), 5)
+    assert c2.tolist() == [2, 0, 0, 3, 1]
+
+
+def test_selection_admissible_rules():
+    # one token, exact scores 5, 3, 2.95, 1; k = 2; bound 0.05 (band 2B = 0.1). The k-th score is
+    # 3: expert 0 is clear of the band (5 > 3.1) and must be chosen; experts 1 and 2 are within it
+    # and either may take the second slot; expert 3 (1 < 2.9) can never be chosen.
+    s = np.array([[5.0, 3.0, 2.95, 1.0]])
+    B = np.array([0.05])
+    cases = {(0, 1): True, (1, 0): True, (0, 2): True, (1, 2): False, (0, 3): False,
+             (0, 0): False, (2, 3): False}
+    for sel, want in cases.items():
+        got = bool(orc.selection_admissible(s, 2, B, np.array([sel]))[0])
+        assert got == want, (sel, got)
+    # a decided token (gap above the band) admits only the exact top-k set
+    s2 = np.array([[1.0, 4.0, 2.0]])
+    assert orc.selection_admissible(s2, 1, np.array([0.1]), np.array([[1]]))[0]
+    assert not orc.selection_admissible(s2, 1, np.array([0.1]), np.array([[2]]))[0]
+
+
 def test_hand_fp32_rank_add(hand):
     c = hand["fp32_rank_add"]
     L32 = _arr(c["logits"])[None, :].astype(np.float32)
@@ -361,6 +398,7 @@ def test_permute_invariants(T, E, k):
     ids, _, counts = orc.route_ref(L, None, k, orc.SOFTMAX)
     offsets, sorted_rows, row_pos = orc.permute_ref(ids, E)
     assert counts.sum() == T * k
+    np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
     np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(ids.ravel(), minlength=E))]))
     assert sorted(sorted_rows.tolist()) == list(range(T * k))
     np.testing.assert_array_equal(sorted_rows[row_pos], np.arange(T * k))
@@ -512,6 +550,9 @@ def _pins_pass():
         test_hand_q4_groups(hand)
         test_hand_q4_packing(hand)
         test_hand_fp32_rank_add(hand)
+        test_hand_q4_param_words(hand)
+        test_hand_expert_counts()
+        test_selection_admissible_rules()
         test_hand_swiglu_layer(hand, "swiglu_one_expert")
         test_hand_swiglu_layer(hand, "swiglu_two_experts_top1")
         test_select_matches_python_sort("ties", 16, 2)
@@ -591,6 +632,16 @@ MUTATIONS = {
     # packed nibbles of odd and even k swapped
     "q4_pack_swap": ("pack_q4_ref", lambda orig: (lambda q: (lambda p: ((p & 15) << 4 | (p >> 4)).astype(np.uint8))(
         orig(q)))),
+    # (scale, bias) halves of the 4-bit parameter word swapped
+    "q4_params_swap": ("pack_q4_params_ref", lambda orig: (lambda s, b: orig(b, s))),
+    # expert counts shifted by one index (the total stays right)
+    "counts_shift": ("expert_counts_ref", lambda orig: (lambda ids, E: np.roll(orig(ids, E), 1))),
+    # admissible selections checked only for closeness to the k-th score (a selection that
+    # leaves out an expert clearly above it passes)
+    "admissible_lax": ("selection_admissible", lambda orig: (lambda s, k, B, ids: np.array([
+        len(set(int(v) for v in ids[t])) == k and all(
+            np.asarray(s)[t, int(e)] >= -np.sort(-np.asarray(s)[t])[k - 1] - 2 * B[t] for e in ids[t])
+        for t in range(len(ids))]))),
     # rank on the fp64 sum instead of the binary32 add
     "rank_fp64": ("rank_scores_fp32", lambda orig: (lambda L, b=None: np.asarray(L, np.float64) + (
         0 if b is None else np.asarray(b, np.float64)[None, :]))),
