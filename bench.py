@@ -2,23 +2,28 @@
 
 A step is one moe_layer_forward over one batch: router logits, top-k + weights, dispatch,
 gate/up + SwiGLU, down projection and combine. Inputs are seeded synthetic tensors resident in
-HBM before timing. The default workload is the ZONOS2-shaped decode step (T=64 tokens, d=2048,
-16 experts, top-1, expert hidden 2816, bf16 weights, fp32 accumulation).
+HBM before timing.
 
-Cold weights: the layer's expert weights are kept in several identical copies and consecutive
-steps rotate through them, so that no step finds its weights in the 256 MB Infinity Cache left
-over from the step before (the copies together exceed 1.5 GB). The timed steps are replayed from
-a HIP graph (the decode loop of the pages replays a captured graph) holding one step per copy;
-`value` and `ms_per_step` come from the wall clock around them, bracketed by synchronizations.
+The headline (`value`, `ms_per_step`, `roofline`, `cpu_baseline`) is the ZONOS2-shaped skewed
+prefill (T=8192 tokens, d=2048, 16 experts, top-1, expert hidden 2816, bf16 weights, fp32
+accumulation; expert 0 takes ~40 % of the tokens and two experts none), the largest of the five
+workloads and the batched regime where the experts run as a grouped GEMM. The other four
+workloads (the fp32 correctness layer, the ZONOS2 and ZONOS3-Mini decode steps, the ZONOS3-Mini
+prefill) are timed in the same run and reported under `workloads`, each with its own roofline.
 
-Stage durations come from a second pass over the same steps, on the same stream, with the
-layer's profiling events (moe_layer_args.prof_events): a graph with event nodes when the runtime
-times those, else eager launches. In that pass the gate/up kernel, the roofline's dominant
-kernel, is launched with its own start/stop events (hipExtLaunchKernelGGL), so its duration is the
-kernel's alone; "dispatch" is the time from the end of routing to the start of that kernel (the
-dispatch kernel on the grouped-GEMM path, plus launch gaps).
+Cold weights: each workload's expert weights are kept in several identical copies and
+consecutive steps rotate through them, so that no step finds its weights in the 256 MB Infinity
+Cache left over from the step before (the copies together exceed 1.5 GB). One HIP graph per copy
+holds one captured step (the decode loop of the pages replays a captured graph); the timed region
+replays exactly `--steps` of them, after exactly `--warmup` untimed ones, bracketed by
+synchronizations. `value` = T / (wall time per step).
 
-Prints one JSON line (see the `result` dict at the end of main()).
+Kernel durations come from a second, host-launched pass over the same copies with the layer's
+profiling events (moe_layer_args.prof_events): the gate/up kernel, the roofline's dominant kernel,
+is launched with its own start/stop events (hipExtLaunchKernelGGL), so its duration is the
+kernel's alone.
+
+Prints one JSON line (see `result` in main()).
 """
 from __future__ import annotations
 
@@ -219,19 +224,234 @@ def cpu_baseline(inp, budget_s: float):
     return out
 
 
+HEADLINE = "zonos2-skewed-prefill"
+FIVE = ("tiny-fp32", "zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill",
+        "zonos2-skewed-prefill")
+
+
+def dominant_kernel(inp, weights="native"):
+    """The gate/up kernel instantiation the library picks for this shape (the dominant kernel of
+    every workload): the weight-streaming kernel for few rows per expert (two-group passes where
+    the whole grid stays resident: (H / 16) * E <= 2048 blocks), else the grouped GEMM."""
+    T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
+    if inp.dtype != "bf16":
+        return "ffn_f32_kernel<true>"
+    if T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and T * k <= 32 * E:
+        maxg = 2 if (H // 16) * E <= 2048 else 1
+        return "ffn_stream_kernel<true, %d, %d>" % (maxg, {"native": 0, "int8": 1, "q4": 2}[weights])
+    return gemm_kernel_name(T * k, E, True)
+
+
+def gemm_kernel_name(rows, E, gateup):
+    """Name of the grouped-GEMM instantiation for `rows` assignment rows over E experts."""
+    if rows >= 256 * E:     # experts average a full 256-row tile: XCD-ordered wide tiles
+        return ("gemm_dma_kernel<true, 256, 256, 2, 64, 64>" if gateup
+                else "gemm_dma_kernel<false, 256, 128, 3, 64, 32>")
+    return ("gemm_dma_kernel<true, 128, 256, 3, 64, 32>" if gateup
+            else "gemm_dma_kernel<false, 128, 256, 3, 64, 32>")
+
+
+def run_workload(name, steps, warmup, weights="native", warm=False, eager=False, ladder=0,
+                 cpu_budget=0.0, event_steps=200):
+    """Times `steps` layer steps of workload `name` (after `warmup` untimed ones) and returns its
+    summary: ms/step, tokens/s, the dominant kernel's roofline, the step's HBM and MFMA
+    fractions, per-stage medians from the event pass and, when cpu_budget > 0, the oracle's
+    timing on this host."""
+    import numpy as np
+    import torch
+    from expert_routing_grouped_moe_amd import inputs as gen
+    from expert_routing_grouped_moe_amd import moe
+
+    dev = "cuda:0"
+    inp = gen.make_inputs(name)
+    T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
+    dt_code = moe.MOE_BF16 if inp.dtype == "bf16" else moe.MOE_F32
+
+    def up(key):
+        if inp.dtype == "bf16":
+            return torch.from_numpy(inp.bits[key].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(getattr(inp, key)).to(dev)
+
+    x = up("x")
+    wr = up("w_router")
+    base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
+    quant = weights != "native"
+    if quant:
+        qfn = moe.moe_quantize_rows_i8 if weights == "int8" else moe.moe_quantize_groups_q4
+        qs = {key: qfn(t) for key, t in base.items()}
+        base = {key: v[0] for key, v in qs.items()}
+        base.update({key + "_scale": v[1] for key, v in qs.items()})
+        torch.cuda.synchronize()
+    wbytes = sum(t.numel() * t.element_size() for t in base.values())
+    ncopies = 1 if warm else max(2, min(16, math.ceil(1.6e9 / wbytes)))
+    copies = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(ncopies - 1)]
+    rb = None if inp.router_bias is None else torch.from_numpy(inp.router_bias).to(dev)
+    sb = None if inp.sel_bias is None else torch.from_numpy(inp.sel_bias).to(dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    counts = torch.zeros((E,), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, moe.moe_workspace_size(T, d, E, H, k, dt_code)), dtype=torch.uint8,
+                     device=dev)
+
+    hip = _hip()
+    nev = moe.MOE_PROF_EVENTS
+    events, ev_arrays, arg_list = [], [], []
+    for c in range(ncopies):
+        evs = []
+        for _ in range(nev):
+            h = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            evs.append(h)
+        events.append(evs)
+        ev_arrays.append((ctypes.c_void_p * nev)(*[e.value for e in evs]))
+        scales = ((copies[c]["w_gate_scale"], copies[c]["w_up_scale"], copies[c]["w_down_scale"])
+                  if quant else None)
+        arg_list.append(moe.make_layer_args(x, wr, copies[c]["w_gate"], copies[c]["w_up"],
+                                            copies[c]["w_down"], k, inp.scoring, y, rb, sb,
+                                            expert_counts=counts, w_scales=scales))
+
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def one_step(c, with_events):
+        a = arg_list[c]
+        a.prof_events = ctypes.cast(ev_arrays[c], ctypes.c_void_p).value if with_events else None
+        st = moe.LIB.moe_layer_forward(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                       ws.numel(), sptr)
+        if st != 0:
+            raise moe.MoeError(st, "moe_layer_forward")
+
+    # eager warm-up of every copy (validates the call), then one graph per copy, one step each
+    with torch.cuda.stream(stream):
+        for c in range(ncopies):
+            one_step(c, False)
+    torch.cuda.synchronize()
+    graphs = []
+    for c in range(ncopies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            one_step(c, False)
+        graphs.append(g)
+    y.fill_(float("nan"))
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item(), "graph replay did not run the layer"
+
+    def run_steps(n, first):
+        if eager:
+            with torch.cuda.stream(stream):
+                for i in range(first, first + n):
+                    one_step(i % ncopies, False)
+        else:
+            for i in range(first, first + n):
+                graphs[i % ncopies].replay()
+
+    run_steps(warmup, 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(steps, warmup)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / steps * 1e3
+
+    # event pass: host launches with a HIP event at every stage boundary, on the kernels' stream
+    stage_ms = {s_: [] for s_ in STAGES}
+    n_ev = max(ncopies, min(event_steps, 4 * steps))
+    for i0 in range(0, n_ev, ncopies):
+        with torch.cuda.stream(stream):
+            for c in range(ncopies):
+                one_step(c, True)
+        torch.cuda.synchronize()
+        for c in range(ncopies):
+            for i in range(nev - 1):
+                f = ctypes.c_float()
+                assert hip.hipEventElapsedTime(ctypes.byref(f), events[c][i], events[c][i + 1]) == 0
+                stage_ms[STAGES[i]].append(f.value)
+    step_ms_ev = [sum(stage_ms[s_][i] for s_ in STAGES) for i in range(len(stage_ms["route"]))]
+
+    cnt = counts.cpu().numpy()
+    alg = algorithmic(inp, cnt, weights)
+    gu_ms = statistics.mean(stage_ms["gate_up"])
+    prefill = gen.WORKLOADS[name].shape == "prefill"
+    if prefill:
+        ach = alg["gu_flops"] / (gu_ms * 1e-3) / 1e12
+        gbs = alg["gu_bytes"] / (gu_ms * 1e-3) / 1e9
+        # the HBM side as well: with cold weights and about one row tile per expert the gate/up
+        # product has fewer FLOPs per byte than the chip's ridge
+        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                "hbm_achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    else:
+        ach = alg["gu_bytes"] / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                "measured_read_ceiling": HBM_READ_CEILING_GBS,
+                "frac_of_measured_ceiling": ach / HBM_READ_CEILING_GBS}
+    roof["kernel"] = dominant_kernel(inp, weights)
+    traffic = measured_traffic(roof["kernel"], name + ("/" + weights if quant else ""))
+    roof["traffic"] = traffic
+    roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+                              if traffic is not None else "not measured for the current kernel")
+    roof["avg_launch_us"] = gu_ms * 1e3
+    roof["algorithmic_bytes_per_launch"] = alg["gu_bytes"]
+    roof["algorithmic_flops_per_launch"] = alg["gu_flops"]
+
+    step_s = ms_per_step * 1e-3
+    out = {
+        "tokens_per_s": T / step_s,
+        "ms_per_step": ms_per_step,
+        "steps": steps,
+        "warmup": warmup,
+        "dtype": inp.dtype,
+        "config": {"workload": name, "T": T, "d": d, "E": E, "k": k, "H": H,
+                   "scoring": inp.scoring, "seed": gen.WORKLOADS[name].seed,
+                   "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
+                   "expert_weights": {"int8": "int8, fp32 row scales",
+                                      "q4": "4-bit affine, groups of 64, bf16 scale and bias"
+                                      }.get(weights, inp.dtype),
+                   "timing": ("host launches" if eager else
+                              "HIP graph replay, one captured step per weight copy")},
+        "step_hbm_gbps": alg["step_bytes"] / step_s / 1e9,
+        "step_hbm_frac": alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
+        "step_tflops": alg["step_flops"] / step_s / 1e12,
+        "step_mfma_frac": alg["step_flops"] / step_s / 1e12 / (
+            BF16_PEAK_TFLOPS if inp.dtype == "bf16" else FP32_PEAK_TFLOPS),
+        "touched_experts": alg["touched"],
+        "stage_median_us": {s_: statistics.median(v) * 1e3 for s_, v in stage_ms.items()},
+        "event_step_us": _spread(step_ms_ev),
+        "roofline": roof,
+    }
+    if ladder:
+        out["ladder"] = ladder_timing(moe, inp, x, wr, copies, rb, sb, ladder, quant=quant)
+    if cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, cpu_budget)
+    for evs in events:
+        for e in evs:
+            hip.hipEventDestroy(e)
+    del graphs, copies, base, x, wr, y, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="zonos2-decode")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="the headline workload (default: the skewed prefill)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload alone (no `workloads` table)")
+    ap.add_argument("--other-steps", type=int, default=200,
+                    help="timed steps of each of the other workloads (warm-up: a tenth)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
     ap.add_argument("--weights", choices=("native", "int8", "q4"), default="native",
                     help="expert weights as given (bf16/fp32), int8 codes with per-row scales "
                          "(moe_quantize_rows_i8) or 4-bit affine codes in groups of 64 "
-                         "(moe_quantize_groups_q4); quantised weights on decode shapes only")
+                         "(moe_quantize_groups_q4); quantised weights on decode shapes only, "
+                         "headline workload only")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -256,235 +476,56 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
+        sys.exit(2)
 
-    import numpy as np
-    import torch
-    from expert_routing_grouped_moe_amd import inputs as gen
-    from expert_routing_grouped_moe_amd import moe
+    head = run_workload(args.workload, args.steps, args.warmup, weights=args.weights,
+                        warm=args.warm, eager=args.eager, ladder=args.ladder,
+                        cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_budget)
+    print(f"[bench] {args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
+    others = {}
+    if not args.only and args.weights == "native":
+        for name in FIVE:
+            if name == args.workload:
+                continue
+            others[name] = run_workload(name, args.other_steps, max(1, args.other_steps // 10),
+                                        warm=args.warm, eager=args.eager)
+            print(f"[bench] {name}: {others[name]['ms_per_step'] * 1e3:.1f} us/step",
+                  file=sys.stderr, flush=True)
 
-    dev = "cuda:0"
-    inp = gen.make_inputs(args.workload)
-    T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
-    dt_code = moe.MOE_BF16 if inp.dtype == "bf16" else moe.MOE_F32
-    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
-
-    def up(key):
-        if inp.dtype == "bf16":
-            return torch.from_numpy(inp.bits[key].view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(getattr(inp, key)).to(dev)
-
-    x = up("x")
-    wr = up("w_router")
-    base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
-    quant = args.weights != "native"
-    if quant:
-        qfn = moe.moe_quantize_rows_i8 if args.weights == "int8" else moe.moe_quantize_groups_q4
-        qs = {key: qfn(t) for key, t in base.items()}
-        base = {key: v[0] for key, v in qs.items()}
-        base.update({key + "_scale": v[1] for key, v in qs.items()})
-        torch.cuda.synchronize()
-    wbytes = sum(t.numel() * t.element_size() for t in base.values())
-    ncopies = 1 if args.warm else max(2, min(16, math.ceil(1.6e9 / wbytes)))
-    copies = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(ncopies - 1)]
-    rb = None if inp.router_bias is None else torch.from_numpy(inp.router_bias).to(dev)
-    sb = None if inp.sel_bias is None else torch.from_numpy(inp.sel_bias).to(dev)
-    y = torch.empty((T, d), dtype=torch.float32, device=dev)
-    counts = torch.zeros((E,), dtype=torch.int32, device=dev)
-    ws = torch.empty(max(1, moe.moe_workspace_size(T, d, E, H, k, dt_code)), dtype=torch.uint8,
-                     device=dev)
-
-    hip = _hip()
-    nev = moe.MOE_PROF_EVENTS
-    events = []
-    ev_arrays = []
-    arg_list = []
-    for c in range(ncopies):
-        evs = []
-        for _ in range(nev):
-            h = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(h)) == 0
-            evs.append(h)
-        arr = (ctypes.c_void_p * nev)(*[e.value for e in evs])
-        events.append(evs)
-        ev_arrays.append(arr)
-        scales = ((copies[c]["w_gate_scale"], copies[c]["w_up_scale"], copies[c]["w_down_scale"])
-                  if quant else None)
-        a = moe.make_layer_args(x, wr, copies[c]["w_gate"], copies[c]["w_up"],
-                                copies[c]["w_down"], k, inp.scoring, y, rb, sb,
-                                expert_counts=counts, w_scales=scales)
-        arg_list.append(a)
-
-    stream = torch.cuda.Stream()
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-
-    def one_step(c, with_events):
-        a = arg_list[c]
-        a.prof_events = ctypes.cast(ev_arrays[c], ctypes.c_void_p).value if with_events else None
-        st = moe.LIB.moe_layer_forward(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
-                                       ws.numel(), sptr)
-        if st != 0:
-            raise moe.MoeError(st, "moe_layer_forward")
-
-    def capture(with_events):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for c in range(ncopies):
-                one_step(c, with_events)
-        return g
-
-    # eager warm-up (also validates the call), then one graph holding one step per weight copy
-    with torch.cuda.stream(stream):
-        for i in range(max(ncopies, 3)):
-            one_step(i % ncopies, False)
-    torch.cuda.synchronize()
-    graph = capture(False)
-    y.fill_(float("nan"))
-    graph.replay()
-    torch.cuda.synchronize()
-    assert not torch.isnan(y).any().item(), "graph replay did not run the layer"
-    replays_w = max(1, math.ceil(args.warmup / ncopies))
-    replays = max(1, math.ceil(args.steps / ncopies))
-    steps = replays * ncopies
-    for _ in range(replays_w):
-        graph.replay()
-    torch.cuda.synchronize()
-
-    # timed region: `steps` layer steps replayed back to back
-    t0 = time.perf_counter()
-    if args.eager:
-        with torch.cuda.stream(stream):
-            for i in range(steps):
-                one_step(i % ncopies, False)
-    else:
-        for _ in range(replays):
-            graph.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / steps * 1e3
-
-    # stage timing: the same steps with a HIP event at every stage boundary, on the kernels'
-    # stream; replayed from a graph with event nodes when the runtime times those, else eager
-    def read_events():
-        out = []
-        for c in range(ncopies):
-            ms = []
-            for i in range(nev - 1):
-                f = ctypes.c_float()
-                if hip.hipEventElapsedTime(ctypes.byref(f), events[c][i], events[c][i + 1]) != 0:
-                    return None
-                ms.append(f.value)
-            out.append(ms)
-        return out
-
-    stage_ms = {s: [] for s in STAGES}
-    ev_mode = "graph"
-    try:
-        graph_ev = capture(True)
-        graph_ev.replay()
-        torch.cuda.synchronize()
-        if read_events() is None:
-            raise RuntimeError("event nodes carry no timestamps")
-    except Exception:
-        ev_mode = "eager"
-        graph_ev = None
-    ev_replays = max(1, min(replays, math.ceil(400 / ncopies)))
-    t_ev = time.perf_counter()
-    for _ in range(ev_replays):
-        if graph_ev is not None:
-            graph_ev.replay()
-        else:
-            with torch.cuda.stream(stream):
-                for c in range(ncopies):
-                    one_step(c, True)
-        torch.cuda.synchronize()
-        got = read_events()
-        assert got is not None, "stage events unreadable"
-        for ms in got:
-            for s_, v in zip(STAGES, ms):
-                stage_ms[s_].append(v)
-    ev_wall = time.perf_counter() - t_ev
-    step_ms_ev = [sum(stage_ms[s_][i] for s_ in STAGES) for i in range(len(stage_ms["route"]))]
-
-    cnt = counts.cpu().numpy()
-    alg = algorithmic(inp, cnt, args.weights)
-    med = {s: statistics.median(v) for s, v in stage_ms.items()}
-    gu_ms = statistics.mean(stage_ms["gate_up"])
-    prefill = gen.WORKLOADS[args.workload].shape == "prefill"
-    if prefill:
-        ach = alg["gu_flops"] / (gu_ms * 1e-3) / 1e12
-        gbs = alg["gu_bytes"] / (gu_ms * 1e-3) / 1e9
-        # the HBM side as well: with cold weights and about one row tile per expert the gate/up
-        # product has fewer FLOPs per byte than the chip's ridge
-        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
-                "hbm_achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
-    else:
-        ach = alg["gu_bytes"] / (gu_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                "measured_read_ceiling": HBM_READ_CEILING_GBS,
-                "frac_of_measured_ceiling": ach / HBM_READ_CEILING_GBS}
-    streaming = inp.dtype == "bf16" and T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and \
-        T * k <= 32 * E
-    # the gate/up kernel instantiation the library picks for this shape (two-group passes where
-    # the whole grid stays resident: (H / 16) * E <= 2048 blocks)
-    if streaming:
-        maxg = 2 if (H // 16) * E <= 2048 else 1
-        roof["kernel"] = "ffn_stream_kernel<true, %d, %d>" % (
-            maxg, {"native": 0, "int8": 1, "q4": 2}[args.weights])
-    elif inp.dtype == "bf16":
-        # 256 x 256 tiles with 64-wide K steps once the experts average a full 256-row tile,
-        # 128 x 256 tiles with 32-wide K steps below that
-        roof["kernel"] = ("gemm_dma_kernel<true, 256, 256, 2, 64, 64>" if T * k >= 256 * E
-                          else "gemm_dma_kernel<true, 128, 256, 3, 64, 32>")
-    else:
-        roof["kernel"] = "ffn_f32_kernel<true>"
-    traffic = measured_traffic(roof["kernel"], args.workload + ("/" + args.weights if quant else ""))
-    roof["traffic"] = traffic
-    roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-                              if traffic is not None else "not measured for the current kernel")
-    roof["avg_launch_us"] = gu_ms * 1e3
-    roof["algorithmic_bytes_per_launch"] = alg["gu_bytes"]
-    roof["algorithmic_flops_per_launch"] = alg["gu_flops"]
-
-    step_s = ms_per_step * 1e-3
     result = {
         "metric": METRIC,
-        "value": T / step_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": replays_w * ncopies,
-        "ms_per_step": ms_per_step,
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": inp.dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "d": d, "E": E, "k": k, "H": H,
-                   "scoring": inp.scoring, "seed": gen.WORKLOADS[args.workload].seed,
-                   "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
-                   "expert_weights": {"int8": "int8, fp32 row scales",
-                                      "q4": "4-bit affine, groups of 64, bf16 scale and bias"
-                                      }.get(args.weights, inp.dtype),
-                   "timing": ("host launches" if args.eager else
-                              "HIP graph replay, one step per weight copy"),
-                   "stage_events": ev_mode, "stage_event_steps": len(step_ms_ev)},
-        "step_hbm_gbps": alg["step_bytes"] / step_s / 1e9,
-        "step_hbm_frac": alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
-        "step_tflops": alg["step_flops"] / step_s / 1e12,
-        "step_mfma_frac": alg["step_flops"] / step_s / 1e12 / BF16_PEAK_TFLOPS,
-        "touched_experts": alg["touched"],
-        "stage_median_us": {s: v * 1e3 for s, v in med.items()},
-        "event_step_median_us": statistics.median(step_ms_ev) * 1e3,
-        "event_step_us": _spread(step_ms_ev),
-        "roofline": roof,
+        "config": head["config"],
+        "step_hbm_gbps": head["step_hbm_gbps"],
+        "step_hbm_frac": head["step_hbm_frac"],
+        "step_tflops": head["step_tflops"],
+        "step_mfma_frac": head["step_mfma_frac"],
+        "touched_experts": head["touched_experts"],
+        "stage_median_us": head["stage_median_us"],
+        "event_step_us": head["event_step_us"],
+        "roofline": head["roofline"],
     }
-    if args.ladder:
-        result["ladder"] = ladder_timing(moe, inp, x, wr, copies, rb, sb, args.ladder,
-                                         quant=quant)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    if "ladder" in head:
+        result["ladder"] = head["ladder"]
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+    if others:
+        table = {args.workload: {key: v for key, v in head.items() if key != "cpu_baseline"}}
+        table.update(others)
+        result["workloads"] = {name: table[name] for name in FIVE if name in table}
     print(json.dumps(result))
 
 

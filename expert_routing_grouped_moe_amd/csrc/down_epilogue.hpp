@@ -11,21 +11,24 @@ namespace moe {
 // Router row: the chosen experts' outputs are summed with their routing weights; "Notes": the
 // residual stream is F32):
 //   kDownExpertOut  expert_out[p, n] = o
-//   kDownStoreY     y[t, n] = w[t, j] * o           (k == 1)
+//   kDownStoreY     y[t, n] = w[t, j] * o           (k == 1; fp32, or bf16 rounded to nearest
+//                   even when y_bf16)
 //   kDownAtomicY    y[t, n] += w[t, j] * o          (k == 2, y cleared beforehand; two addends
 //                   onto 0 give fl(a + b) in either order, so the result is deterministic)
 struct DownRow {
-  float* dst;   // row pointer in expert_out or y
+  void* dst;    // row pointer in expert_out or y (fp32, or bf16 bits)
   float scale;  // routing weight (1 for expert_out)
 };
 
 __device__ __forceinline__ DownRow down_row(const DownArgs& a, int r, int p, int d) {
   DownRow out;
   if (a.mode == kDownExpertOut) {
-    out.dst = a.out + static_cast<long long>(p) * d;
+    out.dst = static_cast<float*>(a.out) + static_cast<long long>(p) * d;
     out.scale = 1.0f;
   } else {
-    out.dst = a.out + static_cast<long long>(r / a.k) * d;
+    const long long off = static_cast<long long>(r / a.k) * d;
+    out.dst = (a.mode == kDownStoreY && a.y_bf16) ? static_cast<void*>(static_cast<uint16_t*>(a.out) + off)
+                                                  : static_cast<void*>(static_cast<float*>(a.out) + off);
     out.scale = a.topk_w[r];
   }
   return out;
@@ -33,11 +36,14 @@ __device__ __forceinline__ DownRow down_row(const DownArgs& a, int r, int p, int
 
 __device__ __forceinline__ void down_put(const DownArgs& a, const DownRow& r, int n, float o) {
   if (a.mode == kDownAtomicY) {
-    unsafeAtomicAdd(r.dst + n, r.scale * o);
+    unsafeAtomicAdd(static_cast<float*>(r.dst) + n, r.scale * o);
   } else if (a.mode == kDownStoreY) {
-    r.dst[n] = r.scale * o;
+    if (a.y_bf16)
+      static_cast<uint16_t*>(r.dst)[n] = f32_to_bf16_bits(r.scale * o);
+    else
+      static_cast<float*>(r.dst)[n] = r.scale * o;
   } else {
-    r.dst[n] = o;
+    static_cast<float*>(r.dst)[n] = o;
   }
 }
 

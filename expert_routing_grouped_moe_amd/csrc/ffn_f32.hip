@@ -2,7 +2,8 @@
 // precision anywhere. SwiGLU as in audio.cpp PR #1271, "Summary", over the gate/up/down expert
 // stacks of zonos2.cpp INTERNALS, "Recommended: F16 spine + K-quant experts".
 //
-// Tiles: 16 grouped rows x 64 output features per block of 256 threads, K staged through LDS in
+// Tiles: 16 grouped rows x 64 output features per block of 256 threads (a 1-D grid, feature
+// tile fastest: block b covers row tile b / ntn and feature tile b % ntn), K staged through LDS in
 // chunks of 64 (float4 copies, all of a chunk's loads issued together, the next chunk loading
 // while the current one is used). Thread (row = tid / 16, c = tid % 16) owns features c, c+16,
 // c+32, c+48.
@@ -32,9 +33,10 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
   __shared__ __attribute__((aligned(16))) float As[kBM * kLd];
   __shared__ __attribute__((aligned(16))) float B0[kBN * kLd];
   __shared__ __attribute__((aligned(16))) float B1[(GATEUP ? kBN : 1) * kLd];
-  const TileInfo ti = find_tile(offsets, E, kBM, blockIdx.y, sh_tiles);
+  const int ntn = (N + kBN - 1) / kBN;
+  const TileInfo ti = find_tile(offsets, E, kBM, static_cast<int>(blockIdx.x / ntn), sh_tiles);
   if (ti.e < 0) return;
-  const int n0 = blockIdx.x * kBN;
+  const int n0 = static_cast<int>(blockIdx.x % ntn) * kBN;
   const int tid = threadIdx.x;
   const int row = tid / 16;
   const int c = tid % 16;
@@ -119,11 +121,13 @@ hipError_t launch_ffn_f32(const float* x, const float* wg, const float* wu, cons
   const int tiles = max_tiles(rows, E, kBM);
   if (tiles == 0) return hipSuccess;
   DownArgs none{};
-  dim3 g1((H + kBN - 1) / kBN, tiles);
+  // one row tile per ntn consecutive blocks; the contract's size limits (T * k * max(d, H) < 2^31,
+  // T <= 2^24, widths <= 65536) keep this below 2^24 blocks, a single grid dimension
+  const dim3 g1(static_cast<unsigned>(tiles) * static_cast<unsigned>((H + kBN - 1) / kBN));
   hipError_t err = launch_marked(ffn_f32_kernel<true>, g1, dim3(256), s, gu, x, wg, wu, d, H, E,
                                  k, offsets, sorted_rows, h, none);
   if (err != hipSuccess) return err;
-  dim3 g2((d + kBN - 1) / kBN, tiles);
+  const dim3 g2(static_cast<unsigned>(tiles) * static_cast<unsigned>((d + kBN - 1) / kBN));
   ffn_f32_kernel<false><<<g2, 256, 0, s>>>(h, wd, nullptr, H, d, E, k, offsets, sorted_rows,
                                            nullptr, down);
   return hipGetLastError();

@@ -21,9 +21,10 @@ enum DownOut {
 
 struct DownArgs {
   int mode;                 // DownOut
-  float* out;               // expert_out or y
+  void* out;                // expert_out (fp32) or y (fp32, or bf16 bits when y_bf16)
   const float* topk_w;      // [T, k]
   int k;
+  int y_bf16;               // kDownStoreY: y holds bf16 (the fp32 value rounded to nearest even)
 };
 
 // Outputs of the routing tail (any may be NULL except ids and w).
@@ -35,11 +36,9 @@ struct RouteOut {
   int d;
 };
 
-// Stage marker for the optional timing events: an external event node while `s` is being
-// captured into a graph, a plain event record otherwise (defined in moe_api.hip).
+// Stage marker for the optional timing events: an event record on `s` (defined in moe_api.hip;
+// the layer refuses timing events while `s` is being captured into a graph).
 hipError_t record_stage_event(void* ev, hipStream_t s);
-// True while `s` is being captured into a graph (defined in moe_api.hip).
-bool stream_capturing(hipStream_t s);
 
 // Optional timing events around one kernel (hipEvent_t handles, or NULL).
 struct StageMarks {
@@ -47,14 +46,14 @@ struct StageMarks {
   void* end;
 };
 
-// Launches `kernel` on `s`. With both marks set and `s` not being captured, the launch goes
-// through hipExtLaunchKernelGGL so that the two events take the kernel's own start and end times;
-// otherwise the marks that are set are recorded before and after the launch.
+// Launches `kernel` on `s`. With both marks set the launch goes through hipExtLaunchKernelGGL
+// so that the two events take the kernel's own start and end times; otherwise the marks that are
+// set are recorded before and after the launch.
 template <typename... Params, typename... Args>
 hipError_t launch_marked(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
                          const StageMarks& m, Args... args) {
   hipError_t err;
-  if (m.start && m.end && !stream_capturing(s)) {
+  if (m.start && m.end) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<hipEvent_t>(m.start),
                           static_cast<hipEvent_t>(m.end), 0, args...);
     return hipGetLastError();
@@ -153,8 +152,9 @@ hipError_t launch_quantize_groups_q4(const void* w, long long rows, int K, bool 
                                      uint32_t* qpar, hipStream_t s);
 
 // ---------------------------------------------------------------- combine (combine.hip)
-// row_pos == NULL: expert_out is indexed by the assignment row itself.
+// row_pos == NULL: expert_out is indexed by the assignment row itself. y_bf16: y holds bf16 bits
+// (the fp32 sum rounded once to nearest even), else fp32.
 hipError_t launch_combine(const float* expert_out, const int32_t* row_pos, const float* w, int T,
-                          int d, int k, float* y, hipStream_t s);
+                          int d, int k, void* y, bool y_bf16, hipStream_t s);
 
 }  // namespace moe

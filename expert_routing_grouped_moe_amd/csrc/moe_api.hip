@@ -19,19 +19,27 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Size limits of the contract (include/moe.h, "Shapes"): with at most 2^24 tokens, widths of at
+// most 65536 and fewer than 2^31 elements in every activation-sized buffer, every launch of the
+// library stays below 2^31 work-items and every grid dimension within its hardware limit.
+constexpr int kMaxTokens = 1 << 24;
+constexpr int kMaxWidth = 65536;
+constexpr long long kMaxElems = 1ll << 31;
+
 int check_dims(int T, int d, int E, int H, int k, int dtype) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (T < 0 || E < 1 || E > moe::kMaxE || k < 1 || k > moe::kMaxK || k > E) return MOE_ERR_SHAPE;
-  if (d <= 0 || H <= 0) return MOE_ERR_SHAPE;
+  if (T < 0 || T > kMaxTokens || E < 1 || E > moe::kMaxE || k < 1 || k > moe::kMaxK || k > E)
+    return MOE_ERR_SHAPE;
+  if (d <= 0 || H <= 0 || d > kMaxWidth || H > kMaxWidth) return MOE_ERR_SHAPE;
   const int mult = dtype == MOE_BF16 ? 64 : 4;
   if (d % mult != 0 || H % mult != 0) return MOE_ERR_SHAPE;
-  if (static_cast<long long>(T) * k >= (1ll << 31)) return MOE_ERR_SHAPE;
+  if (static_cast<long long>(T) * k * (d > H ? d : H) >= kMaxElems) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
 int check_route_dims(int T, int E, int k) {
-  if (T < 0 || E < 1 || E > moe::kMaxE || k < 1 || k > moe::kMaxK || k > E) return MOE_ERR_SHAPE;
-  if (static_cast<long long>(T) * k >= (1ll << 31)) return MOE_ERR_SHAPE;
+  if (T < 0 || T > kMaxTokens || E < 1 || E > moe::kMaxE || k < 1 || k > moe::kMaxK || k > E)
+    return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -58,13 +66,15 @@ struct Layout {
     offsets = o;     o += up(static_cast<size_t>(E + 1) * 4);
     sorted_rows = o; o += up(rows * 4);
     row_pos = o;     o += up(rows * 4);
-    // fp32 expert outputs staged for the combine kernel: k > 2 always; k == 2 outside the
-    // streaming (decode) path, where the down epilogue would otherwise issue T*k*d atomic adds
-    const bool stage = k > 2 || (k == 2 && !(dtype == MOE_BF16 && moe::ffn_bf16_streaming(T, d, E, H, k)));
-    eo = o;          o += stage ? up(rows * d * 4) : 0;
-    // partial logit tiles of the split router (bf16, small batches)
-    const int rks = dtype == MOE_BF16 ? moe::route_split_ks(T, d, E) : 0;
-    rpart = o;       o += up(static_cast<size_t>(rks) * T * E * 4);
+    // fp32 expert outputs staged for the combine kernel whenever k > 1 (the streaming path adds
+    // k == 2 outputs straight into an fp32 y and leaves this region unused; a bf16 y needs it)
+    eo = o;          o += k > 1 ? up(rows * d * 4) : 0;
+    // partial logit tiles of the split router (bf16, batches of at most kRouteSplitMaxT tokens),
+    // sized for min(T, kRouteSplitMaxT) tokens so that the total never shrinks as T grows (a
+    // workspace sized for a large batch serves every smaller one)
+    const int tr = T < moe::kRouteSplitMaxT ? T : moe::kRouteSplitMaxT;
+    const int rks = dtype == MOE_BF16 ? moe::route_split_ks(tr, d, E) : 0;
+    rpart = o;       o += up(static_cast<size_t>(rks) * tr * E * 4);
     total = o;
   }
 };
@@ -80,15 +90,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 // HIP call would otherwise be reported against this call's first launch.
 void clear_stale_error() { (void)hipGetLastError(); }
 
-// Stage marker: an external event node while the stream is being captured, a plain record
-// otherwise.
+// Stage marker (host launches only: moe_layer_forward refuses prof_events during capture).
 hipError_t record_event(void* ev, hipStream_t s) {
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  const hipError_t e = hipStreamIsCapturing(s, &cs);
-  if (e != hipSuccess) return e;
-  if (cs == hipStreamCaptureStatusActive)
-    return hipEventRecordWithFlags(static_cast<hipEvent_t>(ev), s, hipEventRecordExternal);
   return hipEventRecord(static_cast<hipEvent_t>(ev), s);
+}
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
 }
 
 #define MOE_TRY(expr)                          \
@@ -101,10 +110,6 @@ hipError_t record_event(void* ev, hipStream_t s) {
 
 namespace moe {
 hipError_t record_stage_event(void* ev, hipStream_t s) { return record_event(ev, s); }
-bool stream_capturing(hipStream_t s) {
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
-}
 }  // namespace moe
 
 extern "C" {
@@ -131,7 +136,8 @@ size_t moe_workspace_size(int T, int d, int E, int H, int k, int dtype) {
 int moe_router_logits(const void* x, const void* w_router, const float* router_bias, int T, int d,
                       int E, int dtype, float* logits, void* stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (T < 0 || E < 1 || E > moe::kMaxE || d <= 0) return MOE_ERR_SHAPE;
+  if (T < 0 || T > kMaxTokens || E < 1 || E > moe::kMaxE || d <= 0) return MOE_ERR_SHAPE;
+  if (static_cast<long long>(T) * d >= kMaxElems) return MOE_ERR_SHAPE;
   if (d % (dtype == MOE_BF16 ? 64 : 4) != 0) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !logits) return MOE_ERR_NULL;
@@ -195,7 +201,7 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
   const Layout lay(T, d, E, H, k, dtype);
   if (!ws || ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_SHAPE;
-  const DownArgs down{moe::kDownExpertOut, expert_out, nullptr, k};
+  const DownArgs down{moe::kDownExpertOut, expert_out, nullptr, k, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_error();
   if (dtype == MOE_BF16) {
@@ -210,9 +216,15 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
       expert_offsets, sorted_rows, at<float>(ws, lay.h), down, s, moe::StageMarks{}));
 }
 
+// Quantiser limits: fewer than 2^25 rows (one wave per row) and 2^36 elements (one lane per
+// group of 64), so that every launch stays below 2^31 work-items.
+constexpr long long kMaxQuantRows = 1ll << 25;
+constexpr long long kMaxQuantElems = 1ll << 36;
+
 int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* q, float* scales,
                          void* stream) {
   if (rows < 0 || K < 1 || K % 16 != 0) return MOE_ERR_SHAPE;
+  if (rows >= kMaxQuantRows || rows * K >= kMaxQuantElems) return MOE_ERR_SHAPE;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (!w || !q || !scales) return MOE_ERR_NULL;
@@ -225,6 +237,7 @@ int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* 
 int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_t* q,
                            uint32_t* qpar, void* stream) {
   if (rows < 0 || K < 128 || K % 128 != 0) return MOE_ERR_SHAPE;
+  if (rows >= kMaxQuantRows || rows * K >= kMaxQuantElems) return MOE_ERR_SHAPE;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (!w || !q || !qpar) return MOE_ERR_NULL;
@@ -235,15 +248,18 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
 }
 
 int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
-                int d, int k, float* y, void* stream) {
-  if (T < 0 || d <= 0 || d % 4 != 0 || k < 1 || k > moe::kMaxK) return MOE_ERR_SHAPE;
+                int d, int k, void* y, int y_dtype, void* stream) {
+  if (T < 0 || T > kMaxTokens || d <= 0 || d % 4 != 0 || k < 1 || k > moe::kMaxK)
+    return MOE_ERR_SHAPE;
+  if (static_cast<long long>(T) * k * d >= kMaxElems) return MOE_ERR_SHAPE;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!expert_out || !row_pos || !topk_w || !y) return MOE_ERR_NULL;
   if (!aligned16(expert_out) || !aligned16(row_pos) || !aligned16(topk_w) || !aligned16(y))
     return MOE_ERR_SHAPE;
   clear_stale_error();
   return hip_status(moe::launch_combine(expert_out, row_pos, topk_w, T, d, k, y,
-                                        static_cast<hipStream_t>(stream)));
+                                        y_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
 int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
@@ -256,7 +272,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   if (st != MOE_OK) return st;
   // expert weight type: 0 (a zero-initialised struct) or the ABI-1 layout means the activation
   // dtype
-  const bool abi2 = a->struct_size >= sizeof(moe_layer_args);
+  const bool abi2 = a->struct_size >= MOE_LAYER_ARGS_V2_SIZE;
   const int w_dtype = (abi2 && a->w_dtype != 0) ? a->w_dtype : dtype;
   moe::QuantWeights qw{};
   if (w_dtype != dtype) {
@@ -269,6 +285,9 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
     qw = moe::QuantWeights{w_dtype == MOE_I8 ? moe::kWI8 : moe::kWQ4, a->w_gate_scale,
                            a->w_up_scale, a->w_down_scale};
   }
+  const bool abi4 = a->struct_size >= offsetof(moe_layer_args, y_dtype) + sizeof(a->y_dtype);
+  const int y_dtype = abi4 ? a->y_dtype : MOE_F32;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!a->x || !a->w_router || !a->w_gate || !a->w_up || !a->w_down || !a->y) return MOE_ERR_NULL;
   const void* ptrs[] = {a->x, a->w_router, a->router_bias, a->sel_bias, a->w_gate, a->w_up,
@@ -279,6 +298,8 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   if (!ws || ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // stage events are host-launch timing: refused, with nothing enqueued, during graph capture
+  if (a->prof_events && capturing(s)) return MOE_ERR_UNSUPPORTED;
   clear_stale_error();
   void* const* ev = a->prof_events;
   auto mark = [&](int i) -> hipError_t { return ev ? record_event(ev[i], s) : hipSuccess; };
@@ -292,15 +313,17 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   float* eo = at<float>(ws, lay.eo);
   // few rows per expert (decode): the expert kernels find their rows from the ids themselves
   const bool streaming = dtype == MOE_BF16 && moe::ffn_bf16_streaming(T, d, E, H, k);
-  // k == 2 adds two weighted outputs into a cleared y with fp32 atomics (deterministic: two
-  // addends onto 0) on the streaming path; elsewhere, and for k > 2, expert outputs are staged
-  // and combined in slot order
-  const bool atomic_y = k == 2 && streaming;
-  float* zero_y = atomic_y ? a->y : nullptr;
+  // k == 2 adds two weighted outputs into a cleared fp32 y with fp32 atomics (deterministic: two
+  // addends onto 0) on the streaming path; elsewhere, for k > 2 and for a bf16 y, expert outputs
+  // are staged and combined in slot order
+  const bool y_bf16 = y_dtype == MOE_BF16;
+  const bool atomic_y = k == 2 && streaming && !y_bf16;
+  float* zero_y = atomic_y ? static_cast<float*>(a->y) : nullptr;
 
   DownArgs down{};
   down.topk_w = w;
   down.k = k;
+  down.y_bf16 = y_bf16 ? 1 : 0;
   if (k == 1) {
     down.mode = moe::kDownStoreY;
     down.out = a->y;
@@ -351,7 +374,7 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   // staged expert outputs (by assignment row on the streaming path, in dispatch order
   // otherwise) are combined in slot order
   if (k > 1 && !atomic_y)
-    MOE_TRY(moe::launch_combine(eo, streaming ? nullptr : row_pos, w, T, d, k, a->y, s));
+    MOE_TRY(moe::launch_combine(eo, streaming ? nullptr : row_pos, w, T, d, k, a->y, y_bf16, s));
   MOE_TRY(mark(4));
   return MOE_OK;
 }

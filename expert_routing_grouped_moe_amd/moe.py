@@ -15,7 +15,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
-MOE_ABI_VERSION = 3  # include/moe.h; the library must report the same value
+MOE_ABI_VERSION = 4  # include/moe.h; the library must report the same value
 
 MOE_OK = 0
 MOE_ERR_NULL = -1
@@ -62,6 +62,7 @@ class MoeLayerArgs(Structure):
         ("prof_events", c_void_p),   # void* const*: MOE_PROF_EVENTS hipEvent_t handles or NULL
         ("w_dtype", c_int32),
         ("w_gate_scale", c_void_p), ("w_up_scale", c_void_p), ("w_down_scale", c_void_p),
+        ("y_dtype", c_int32),        # ABI 4: MOE_F32 or MOE_BF16
     ]
 
 
@@ -94,7 +95,7 @@ def _load() -> ctypes.CDLL:
                                    c_size_t, c_void_p]
     lib.moe_combine.restype = c_int
     lib.moe_combine.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
-                                c_void_p]
+                                c_int, c_void_p]
     lib.moe_layer_forward.restype = c_int
     lib.moe_layer_forward.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_size_t, c_void_p]
     lib.moe_quantize_rows_i8.restype = c_int
@@ -255,16 +256,26 @@ def moe_expert_ffn(x, w_gate, w_up, w_down, k, expert_offsets, sorted_rows, expe
     return expert_out
 
 
-def moe_combine(expert_out, row_pos, topk_w, y=None, stream=None):
+def _y_code(y) -> int:
+    if y.dtype == torch.float32:
+        return MOE_F32
+    if y.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"y has dtype {y.dtype}: float32 or bfloat16")
+
+
+def moe_combine(expert_out, row_pos, topk_w, y=None, stream=None, y_dtype=torch.float32):
+    """y [T, d] = sum_j topk_w[:, j] * expert_out[row_pos[t*k + j]]; y is float32 or bfloat16
+    (``y`` passed in decides, else ``y_dtype``)."""
     T, k = topk_w.shape
     d = expert_out.shape[1]
     _need(expert_out, "expert_out", (T * k, d), torch.float32)
     _need(row_pos, "row_pos", (T * k,), torch.int32)
     _need(topk_w, "topk_w", (T, k), torch.float32)
-    y = _empty((T, d), torch.float32, expert_out) if y is None else y
-    _need(y, "y", (T, d), torch.float32)
+    y = _empty((T, d), y_dtype, expert_out) if y is None else y
+    _need(y, "y", (T, d))
     _check(LIB.moe_combine(_ptr(expert_out), _ptr(row_pos), _ptr(topk_w), T, d, k, _ptr(y),
-                           _stream(stream)), "moe_combine")
+                           _y_code(y), _stream(stream)), "moe_combine")
     return y
 
 
@@ -296,7 +307,7 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
             _need(w_scales[2], "w_down_scale", (E, d), torch.float32)
     _need(router_bias, "router_bias", (E,), torch.float32)
     _need(sel_bias, "sel_bias", (E,), torch.float32)
-    _need(y, "y", (T, d), torch.float32)
+    _need(y, "y", (T, d))
     _need(logits, "logits", (T, E), torch.float32)
     _need(topk_ids, "topk_ids", (T, k), torch.int32)
     _need(topk_w, "topk_w", (T, k), torch.float32)
@@ -309,6 +320,7 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
     if wt in (torch.int8, torch.uint8):
         a.w_gate_scale, a.w_up_scale, a.w_down_scale = (t.data_ptr() for t in w_scales)
     a.scoring = _scoring_code(scoring)
+    a.y_dtype = _y_code(y)
     for name, t in (("x", x), ("w_router", w_router), ("router_bias", router_bias),
                     ("sel_bias", sel_bias), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down),
                     ("y", y), ("logits", logits), ("topk_ids", topk_ids), ("topk_w", topk_w),
@@ -319,13 +331,15 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
 
 def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
                       sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
-                      expert_counts=None, workspace=None, stream=None, args=None, w_scales=None):
-    """The fused layer. Returns y [T, d] fp32. Optional outputs are written when passed. With
-    quantised expert weights (moe_quantize_rows_i8 or moe_quantize_groups_q4 codes) pass their
-    scale arrays as w_scales."""
+                      expert_counts=None, workspace=None, stream=None, args=None, w_scales=None,
+                      y_dtype=torch.float32):
+    """The fused layer. Returns y [T, d], float32 unless ``y`` (or ``y_dtype``) is bfloat16.
+    Optional outputs are written when passed. With quantised expert weights
+    (moe_quantize_rows_i8 or moe_quantize_groups_q4 codes) pass their scale arrays as
+    w_scales."""
     T, d = x.shape
     E, H, _ = w_gate.shape
-    y = _empty((T, d), torch.float32, x) if y is None else y
+    y = _empty((T, d), y_dtype, x) if y is None else y
     if args is None:
         args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias,
                                sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales)

@@ -32,14 +32,18 @@
  *                synchronises, or allocates, so every call may be captured into a HIP graph.
  *                Launch shapes depend only on the scalar arguments, never on routing results.
  *   Dtypes       `dtype` (MOE_F32 or MOE_BF16) is the type of x and of every weight matrix.
- *                Logits, biases, routing weights, expert outputs and y are always fp32.
+ *                Logits, biases, routing weights and expert outputs are always fp32; y is fp32
+ *                unless a `y_dtype` argument asks for bf16 (the sum is formed in fp32 and
+ *                rounded once to nearest even).
  *   Errors       A negative return means nothing was enqueued, except MOE_ERR_HIP, which reports
  *                a failed launch (work enqueued before it by the same call may have run).
  *                Device data is never validated: NaN logits or expert ids outside [0, E) are
  *                outside the contract. No C++ exception crosses this interface.
- *   Shapes       1 <= E <= 256, 1 <= k <= min(E, 8), T >= 0 (T == 0 enqueues nothing and
- *                returns MOE_OK), T * k < 2^31, d and H multiples of 64 (bf16) or of 4 (fp32),
- *                d, H >= 64 for bf16. Violations return MOE_ERR_SHAPE / MOE_ERR_UNSUPPORTED.
+ *   Shapes       1 <= E <= 256, 1 <= k <= min(E, 8), 0 <= T <= 2^24 (T == 0 enqueues nothing
+ *                and returns MOE_OK), d and H multiples of 64 (bf16) or of 4 (fp32) and at most
+ *                65536, and T * k * max(d, H) < 2^31 (every activation-sized buffer has fewer
+ *                than 2^31 elements; this keeps every launch within the hardware's grid limits).
+ *                Violations return MOE_ERR_SHAPE / MOE_ERR_UNSUPPORTED.
  *   Reentrancy   Stateless and thread-safe; calls on different streams may run concurrently
  *                when their buffers do not overlap.
  */
@@ -53,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
   MOE_OK = 0,
@@ -111,6 +115,7 @@ size_t moe_workspace_size(int T, int d, int E, int H, int k, int dtype);
  *   w_router  [E, d]  dtype      router weight
  *   router_bias [E]   fp32/NULL  added to every token's logits (NULL = no bias)
  *   logits    [T, E]  fp32       output; accumulated in fp32 (bf16 products are exact in fp32)
+ * Sizes: 0 <= T <= 2^24, 1 <= E <= 256, d a multiple of 64 (bf16) or 4 (fp32), T * d < 2^31.
  */
 int moe_router_logits(const void* x, const void* w_router, const float* router_bias,
                       int T, int d, int E, int dtype, float* logits, void* stream);
@@ -178,11 +183,15 @@ int moe_expert_ffn(const void* x, int T, int d, const void* w_gate, const void* 
 /*
  * Combine, step 7: y[t] = sum_{j=0}^{k-1} topk_w[t, j] * expert_out[row_pos[t*k + j]], summed in
  * slot order in fp32 (zonos2.cpp INTERNALS, "Model architecture", Router row: prob-weighted sum;
- * "Notes": F32 residual stream).
- *   expert_out [T*k, d] fp32, row_pos [T*k] int32, topk_w [T, k] fp32 -> y [T, d] fp32
+ * "Notes": F32 residual stream, hence the fp32 default).
+ *   expert_out [T*k, d] fp32, row_pos [T*k] int32, topk_w [T, k] fp32 -> y [T, d]
+ *   y_dtype    MOE_F32 (y is float) or MOE_BF16 (y holds bf16 bits: the fp32 sum rounded once to
+ *              nearest even); anything else returns MOE_ERR_UNSUPPORTED
+ * Sizes: 0 <= T <= 2^24, 1 <= k <= 8, d a multiple of 4, T * k * d < 2^31. Changed in ABI 4
+ * (y_dtype added).
  */
 int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
-                int d, int k, float* y, void* stream);
+                int d, int k, void* y, int y_dtype, void* stream);
 
 /* Arguments of the fused layer call. Set struct_size = sizeof(struct moe_layer_args). */
 typedef struct moe_layer_args {
@@ -197,7 +206,7 @@ typedef struct moe_layer_args {
   const void* w_gate;        /* [E, H, d]                                                 */
   const void* w_up;          /* [E, H, d]                                                 */
   const void* w_down;        /* [E, d, H]                                                 */
-  float* y;                  /* [T, d] fp32 output                                        */
+  void* y;                   /* [T, d] output: fp32, or bf16 when y_dtype = MOE_BF16      */
   /* Optional outputs (NULL = not written). */
   float* logits;             /* [T, E] fp32 router logits                                 */
   int32_t* topk_ids;         /* [T, k]                                                    */
@@ -206,10 +215,10 @@ typedef struct moe_layer_args {
   /* Optional stage timing (NULL = none): an array of MOE_PROF_EVENTS hipEvent_t handles passed
      as void*, owned by the caller. [0] before routing, [1] after routing (logits, top-k,
      weights), [2] start and [3] end of the gate/up + SwiGLU kernel, [4] after the down projection
-     and combine. Outside graph capture [2] and [3] are taken by the gate/up launch itself
-     (hipExtLaunchKernelGGL start/stop events), so [2] -> [3] is that kernel's duration; the
-     others, and all five while the stream is being captured, are event records enqueued at the
-     stage boundary (external event nodes, hipEventRecordExternal, during capture). */
+     and combine. [2] and [3] are taken by the gate/up launch itself (hipExtLaunchKernelGGL
+     start/stop events), so [2] -> [3] is that kernel's duration; the others are event records
+     enqueued at the stage boundary. Host launches only: a non-NULL prof_events on a stream that
+     is being captured into a graph returns MOE_ERR_UNSUPPORTED with nothing enqueued. */
   void* const* prof_events;
   /* ABI 2. w_dtype = 0, or a struct_size that ends before w_dtype (MOE_LAYER_ARGS_V1_SIZE),
      means the expert weights have the activation dtype (as does w_dtype = dtype).
@@ -232,9 +241,14 @@ typedef struct moe_layer_args {
   const void* w_gate_scale;   /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
   const void* w_up_scale;     /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
   const void* w_down_scale;   /* MOE_I8: float [E, d];  MOE_Q4: uint32 [E, d, H / 64] */
+  /* ABI 4. Type of y: MOE_F32 (also when struct_size ends before this field,
+     MOE_LAYER_ARGS_V2_SIZE) or MOE_BF16 (the fp32 sum of the weighted expert outputs rounded once
+     to nearest even). Anything else returns MOE_ERR_UNSUPPORTED. */
+  int32_t y_dtype;
 } moe_layer_args;
 
 #define MOE_LAYER_ARGS_V1_SIZE offsetof(moe_layer_args, w_dtype)
+#define MOE_LAYER_ARGS_V2_SIZE offsetof(moe_layer_args, y_dtype)
 
 #define MOE_PROF_EVENTS 5
 

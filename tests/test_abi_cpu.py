@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.moe_abi_version() == 3 == moe.MOE_ABI_VERSION
+    assert moe.moe_abi_version() == 4 == moe.MOE_ABI_VERSION
     hdr = re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read())
     assert hdr and int(hdr.group(1)) == moe.MOE_ABI_VERSION
     for st in (0, -1, -2, -3, -4, -5):
@@ -53,9 +53,41 @@ def test_workspace_size():
     # k >= 2 outside the weight-streaming path stages fp32 expert outputs: T*k*d*4 more bytes
     assert L.moe_workspace_size(64, 128, 8, 256, 2, 0) - L.moe_workspace_size(64, 128, 8, 256, 1, 0) \
         >= 64 * 2 * 128 * 4
-    # the streaming path (bf16, few rows per expert, d and H multiples of 256) adds k == 2 outputs
-    # into y directly and stages nothing
-    assert L.moe_workspace_size(64, 1024, 64, 512, 2, 1) < 64 * 2 * 1024 * 4
+    # every k >= 2 shape reserves the staged outputs (a bf16 y is combined from them, also on the
+    # weight-streaming path, which adds k == 2 outputs into an fp32 y directly)
+    assert L.moe_workspace_size(64, 1024, 64, 512, 2, 1) >= 64 * 2 * 1024 * 4
+
+
+@pytest.mark.parametrize("d,E,H,k,dt", [(1024, 64, 512, 2, 1), (2048, 16, 2816, 1, 1),
+                                        (128, 8, 256, 1, 0), (256, 8, 256, 8, 1),
+                                        (1024, 64, 512, 1, 1), (256, 256, 256, 2, 1)])
+def test_workspace_never_shrinks_as_T_grows(d, E, H, k, dt):
+    # a workspace sized for the largest batch must serve every smaller one (the graph ladder and
+    # callers that reuse one buffer rely on it), across the routing and expert kernel switches
+    L = moe.LIB
+    Ts = list(range(1, 700)) + [1000, 2047, 2048, 2049, 4096, 8192, 20000]
+    sizes = [L.moe_workspace_size(T, d, E, H, k, dt) for T in Ts]
+    assert all(s > 0 for s in sizes)
+    bad = [(Ts[i], Ts[i + 1]) for i in range(len(Ts) - 1) if sizes[i + 1] < sizes[i]]
+    assert not bad, bad[:4]
+
+
+def test_size_limits():
+    L = moe.LIB
+    assert L.moe_workspace_size(1 << 24, 64, 8, 64, 1, 1) > 0
+    assert L.moe_workspace_size((1 << 24) + 1, 64, 8, 64, 1, 1) == 0       # T > 2^24
+    assert L.moe_workspace_size(1 << 20, 2048, 16, 2048, 1, 1) == 0       # T*k*max(d, H) = 2^31
+    assert L.moe_workspace_size((1 << 20) - 1, 2048, 16, 2048, 1, 1) > 0
+    assert L.moe_workspace_size(1 << 19, 1024, 64, 2048, 2, 1) == 0       # 2^19 * 2 * 2048
+    assert L.moe_workspace_size(4, 65536 + 64, 8, 256, 1, 1) == 0         # d > 65536
+    assert L.moe_workspace_size(4, 256, 8, 65536 + 64, 1, 1) == 0         # H > 65536
+    call = lambda T, E=8, k=1: L.moe_route(FAKE, None, T, E, k, 0, FAKE, FAKE, FAKE, None)
+    assert call((1 << 24) + 1) == moe.MOE_ERR_SHAPE
+    assert L.moe_router_logits(FAKE, FAKE, None, (1 << 24) + 1, 128, 8, 1, FAKE, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_router_logits(FAKE, FAKE, None, 1 << 20, 2048, 8, 1, FAKE, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_combine(FAKE, FAKE, FAKE, 1 << 19, 2048, 2, FAKE, 0, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_quantize_rows_i8(FAKE, 1 << 25, 64, 1, FAKE, FAKE, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_quantize_groups_q4(FAKE, 1 << 24, 1 << 12, 1, FAKE, FAKE, None) == moe.MOE_ERR_SHAPE
 
 
 def test_route_validation():
@@ -84,9 +116,11 @@ def test_permute_combine_logits_validation():
     assert perm(k=9) == moe.MOE_ERR_SHAPE
     assert perm(c=None) == moe.MOE_ERR_NULL
     assert perm(sr=MISALIGNED) == moe.MOE_ERR_SHAPE
-    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 6, 1, FAKE, None) == moe.MOE_ERR_SHAPE     # d % 4
-    assert L.moe_combine(FAKE, None, FAKE, 4, 8, 1, FAKE, None) == moe.MOE_ERR_NULL
-    assert L.moe_combine(FAKE, FAKE, FAKE, 0, 8, 1, FAKE, None) == moe.MOE_OK
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 6, 1, FAKE, 0, None) == moe.MOE_ERR_SHAPE     # d % 4
+    assert L.moe_combine(FAKE, None, FAKE, 4, 8, 1, FAKE, 0, None) == moe.MOE_ERR_NULL
+    assert L.moe_combine(FAKE, FAKE, FAKE, 0, 8, 1, FAKE, 0, None) == moe.MOE_OK
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 8, 1, FAKE, 2, None) == moe.MOE_ERR_UNSUPPORTED  # y_dtype
+    assert L.moe_combine(FAKE, None, FAKE, 4, 8, 1, FAKE, 1, None) == moe.MOE_ERR_NULL
     assert L.moe_router_logits(FAKE, FAKE, None, 4, 128, 8, 2, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_router_logits(FAKE, FAKE, None, 4, 96, 8, 1, FAKE, None) == moe.MOE_ERR_SHAPE
     assert L.moe_router_logits(FAKE, None, None, 4, 128, 8, 1, FAKE, None) == moe.MOE_ERR_NULL
@@ -135,6 +169,13 @@ def test_layer_forward_validation():
     assert run(_args(logits=MISALIGNED.value)) == moe.MOE_ERR_SHAPE
     assert run(_args(), n=ws - 256) == moe.MOE_ERR_WORKSPACE
     assert run(_args(), w=None) == moe.MOE_ERR_WORKSPACE
+    # y_dtype (ABI 4): fp32 or bf16; layouts ending before the field mean fp32
+    assert run(_args(y_dtype=2)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(y_dtype=1), n=0) == moe.MOE_ERR_WORKSPACE
+    assert run(_args(y_dtype=2, struct_size=moe.MoeLayerArgs.y_dtype.offset), n=0) == \
+        moe.MOE_ERR_WORKSPACE
+    # timing events pass validation like any other argument (the capture check comes last)
+    assert run(_args(prof_events=FAKE.value), n=0) == moe.MOE_ERR_WORKSPACE
 
 
 def test_layer_int8_weight_validation():

@@ -110,3 +110,21 @@ def test_kernel_hash_ignores_comments_only(bench):
     c = "int f(int x) { return 3 * x; }\n"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_dominant_kernel_names(bench):
+    mk = lambda T, d, E, k, H, dt="bf16": SimpleNamespace(T=T, d=d, E=E, k=k, H=H, dtype=dt)
+    # decode shapes: the weight-streaming gate/up kernel, two-group passes while (H/16)*E <= 2048
+    # (2816 / 16) * 16 = 2816 blocks: one-group passes; (512 / 16) * 64 = 2048: two-group passes
+    assert bench.dominant_kernel(mk(64, 2048, 16, 1, 2816)) == "ffn_stream_kernel<true, 1, 0>"
+    assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512)) == "ffn_stream_kernel<true, 2, 0>"
+    assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512), "q4") == "ffn_stream_kernel<true, 2, 2>"
+    # prefill shapes: the grouped GEMM, wide XCD-ordered tiles once experts average 256 rows
+    assert bench.dominant_kernel(mk(8192, 2048, 16, 1, 2816)).startswith("gemm_dma_kernel<true, 256, 256")
+    assert bench.dominant_kernel(mk(4096, 1024, 64, 2, 512)).startswith("gemm_dma_kernel<true, 128, 256")
+    assert bench.dominant_kernel(mk(64, 128, 8, 1, 256, "f32")) == "ffn_f32_kernel<true>"
+
+
+def test_bench_defaults_headline_the_skewed_prefill(bench):
+    assert bench.HEADLINE == "zonos2-skewed-prefill"
+    assert bench.FIVE[-1] == bench.HEADLINE and len(bench.FIVE) == 5

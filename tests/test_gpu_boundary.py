@@ -1,0 +1,204 @@
+"""Boundary behaviour on the GPU: a bf16 output stream (y_dtype), the profiling events (host
+launches only; refused with nothing enqueued during graph capture), an fp32 layer whose row tiles
+exceed the 65535 limit of a second grid dimension, and fp16 saturation of h at large
+activations."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as orc
+from expert_routing_grouped_moe_amd import inputs as gen
+
+from _parity import DEV, TOL, check_layer, run_layer, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipGraphGetNodes.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.hipGraphDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _layer(dev, inp, y, ws, args, stream=None):
+    from expert_routing_grouped_moe_amd import moe
+    return moe.LIB.moe_layer_forward(ctypes.byref(args), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                     moe._stream(stream))
+
+
+def _setup(name, y_dtype):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs(name)
+    dev = upload(inp)
+    y = torch.empty((inp.T, inp.d), dtype=y_dtype, device=DEV)
+    ws = torch.empty(moe.moe_workspace_size(inp.T, inp.d, inp.E, inp.H, inp.k,
+                                            moe.MOE_BF16 if inp.dtype == "bf16" else moe.MOE_F32),
+                     dtype=torch.uint8, device=DEV)
+    args = moe.make_layer_args(dev["x"], dev["w_router"], dev["w_gate"], dev["w_up"],
+                               dev["w_down"], inp.k, inp.scoring, y, dev["router_bias"],
+                               dev["sel_bias"])
+    return inp, dev, y, ws, args
+
+
+# -------------------------------------------------------------------------- bf16 output stream
+
+# every expert-kernel family and combine rule: fp32 path (k = 1), streaming k = 1 (stored into
+# y), streaming k = 2 (fp32 atomics, staged for a bf16 y), grouped GEMM k = 2 (staged), grouped
+# GEMM k = 1 with XCD-ordered tiles (stored into y)
+BF16_Y = ["tiny-fp32", "zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill",
+          "zonos2-skewed-prefill"]
+
+
+@pytest.mark.parametrize("name", BF16_Y)
+def test_layer_bf16_y(name):
+    """y_dtype = bf16 gives the fp32 result rounded once to nearest even: bit for bit where the
+    fp32 run takes the same combine, within one bf16 rounding of it where the fp32 run adds two
+    addends atomically; and within the layer bound of the oracle plus the bf16 rounding."""
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp, dev, y16, ws, args16 = _setup(name, torch.bfloat16)
+    assert args16.y_dtype == moe.MOE_BF16
+    y16.fill_(float("nan"))
+    assert _layer(dev, inp, y16, ws, args16) == moe.MOE_OK
+    y32 = torch.empty((inp.T, inp.d), dtype=torch.float32, device=DEV)
+    args32 = moe.make_layer_args(dev["x"], dev["w_router"], dev["w_gate"], dev["w_up"],
+                                 dev["w_down"], inp.k, inp.scoring, y32, dev["router_bias"],
+                                 dev["sel_bias"])
+    assert _layer(dev, inp, y32, ws, args32) == moe.MOE_OK
+    torch.cuda.synchronize()
+    rounded = y32.to(torch.bfloat16)              # round to nearest even
+    streaming_k2 = inp.dtype == "bf16" and inp.k == 2 and inp.T * inp.k <= 2048
+    if streaming_k2:
+        # the staged combine sums w0 o0 + w1 o1 with a fused multiply-add, the fp32 atomics add
+        # the two rounded products: they differ by at most an fp32 rounding of the larger term
+        a = y16.float().cpu().numpy().astype(np.float64)
+        b = y32.cpu().numpy().astype(np.float64)
+        assert (np.abs(a - b) <= np.abs(b) * 2.0 ** -8 + 2.0 ** -18 * np.abs(b).max()).all()
+    else:
+        assert torch.equal(y16.view(torch.int16), rounded.view(torch.int16))
+    ref = orc.layer_ref(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, inp.k, inp.scoring,
+                        router_bias=inp.router_bias, sel_bias=inp.sel_bias)["y"]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    tol = TOL[inp.dtype] * rms
+    got = y16.float().cpu().numpy().astype(np.float64)
+    # |y16 - y32| <= 2^-9 |y32| (one rounding) and |y32 - ref| <= tol (near ties aside: the
+    # workloads' tokens are all decided, which the fp32 parity tests check)
+    bound = tol + 2.0 ** -9 * (np.abs(ref) + tol)
+    assert (np.abs(got - ref) <= bound).all(), float(np.max(np.abs(got - ref) - bound))
+
+
+def test_combine_bf16_y():
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    rng = np.random.default_rng(3)
+    T, d, k = 77, 520, 3
+    eo = torch.from_numpy(rng.standard_normal((T * k, d)).astype(np.float32)).to(DEV)
+    pos = torch.from_numpy(rng.permutation(T * k).astype(np.int32)).to(DEV)
+    w = torch.from_numpy(rng.random((T, k)).astype(np.float32)).to(DEV)
+    y32 = moe.moe_combine(eo, pos, w)
+    y16 = moe.moe_combine(eo, pos, w, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
+# ------------------------------------------------------------------------------ profiling events
+
+def test_prof_events_refused_during_capture():
+    """A non-NULL prof_events while the stream is being captured returns MOE_ERR_UNSUPPORTED and
+    enqueues nothing: the captured graph has no nodes."""
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    hip = _hip()
+    inp, dev, y, ws, args = _setup("zonos3mini-decode-cfg", torch.float32)
+    evs = [ctypes.c_void_p() for _ in range(moe.MOE_PROF_EVENTS)]
+    for e in evs:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    arr = (ctypes.c_void_p * moe.MOE_PROF_EVENTS)(*[e.value for e in evs])
+    args.prof_events = ctypes.cast(arr, ctypes.c_void_p).value
+    stream = torch.cuda.Stream()
+    s = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert hip.hipStreamBeginCapture(s, 1) == 0          # thread-local capture mode
+    st = moe.LIB.moe_layer_forward(ctypes.byref(args), ctypes.c_void_p(ws.data_ptr()), ws.numel(), s)
+    g = ctypes.c_void_p()
+    assert hip.hipStreamEndCapture(s, ctypes.byref(g)) == 0
+    n = ctypes.c_size_t(99)
+    assert hip.hipGraphGetNodes(g, None, ctypes.byref(n)) == 0
+    hip.hipGraphDestroy(g)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    assert n.value == 0
+    # the same call on the same stream outside capture runs and times the gate/up kernel
+    y.fill_(float("nan"))
+    torch.cuda.synchronize()
+    assert moe.LIB.moe_layer_forward(ctypes.byref(args), ctypes.c_void_p(ws.data_ptr()),
+                                     ws.numel(), s) == moe.MOE_OK
+    stream.synchronize()
+    ms = []
+    for i in range(moe.MOE_PROF_EVENTS - 1):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), evs[i], evs[i + 1]) == 0
+        ms.append(f.value)
+    assert ms[2] > 0 and sum(ms) > 0, ms                # [2] -> [3] is the gate/up kernel
+    assert not torch.isnan(y).any().item()
+    # and gives the same output as a call without events
+    args.prof_events = None
+    y2 = y.clone()
+    assert _layer(dev, inp, y, ws, args) == moe.MOE_OK
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    for e in evs:
+        hip.hipEventDestroy(e)
+
+
+# -------------------------------------------------------------------------- fp32 grid extents
+
+def test_f32_layer_more_row_tiles_than_a_grid_dimension():
+    """1.1 M tokens of an fp32 layer: 68750 row tiles of 16, more than a second grid dimension
+    holds (65535); the row tiles run along the first dimension. Checked on sampled tokens."""
+    T, d, E, k, H = 1_100_000, 64, 4, 1, 64
+    assert (T * k + 15) // 16 > 65535
+    inp = gen.make_inputs_custom(T, d, E, k, H, orc.SOFTMAX, "f32", seed=17)
+    res = run_layer(inp, with_logits=False)
+    np.testing.assert_array_equal(res["expert_counts"],
+                                  np.bincount(res["topk_ids"].ravel(), minlength=E))
+    rng = np.random.default_rng(2)
+    tokens = np.sort(np.concatenate([rng.choice(T, 300, replace=False), [0, T - 1]]))
+    print(check_layer(inp, res, tokens=tokens))
+
+
+# ------------------------------------------------------------------------------ h saturation
+
+def test_h_saturates_at_fp16_max():
+    """The bf16 path stores h in fp16, saturated at +-65504 (no infinities from finite h). With
+    activations scaled by 1024 most |h| exceed that; the output then equals the down product of
+    the clamped h (fp64 here), not the unclamped layer."""
+    T, d, E, k, H = 64, 128, 1, 1, 128
+    inp = gen.make_inputs_custom(T, d, E, k, H, orc.SOFTMAX, "bf16", seed=23)
+    inp.x = (inp.x * np.float32(1024)).astype(np.float32)   # exact: a power of two
+    inp.bits["x"] = gen.bf16_round_bits(inp.x)
+    res = run_layer(inp)
+    y = res["y"].astype(np.float64)
+    assert np.isfinite(y).all()
+    X = inp.x.astype(np.float64)
+    g = X @ inp.w_gate[0].astype(np.float64).T
+    u = X @ inp.w_up[0].astype(np.float64).T
+    h = orc.silu_ref(g) * u
+    assert np.mean(np.abs(h) > 65504) > 0.5
+    w = res["topk_w"][:, :1].astype(np.float64)               # E = 1: the weight is 1
+    np.testing.assert_array_equal(w, 1.0)
+    y_clamped = np.clip(h, -65504, 65504) @ inp.w_down[0].astype(np.float64).T
+    y_plain = h @ inp.w_down[0].astype(np.float64).T
+    rms = float(np.sqrt(np.mean(y_clamped ** 2)))
+    assert np.max(np.abs(y - y_clamped)) <= TOL["bf16"] * rms
+    assert np.max(np.abs(y - y_plain)) > 10 * TOL["bf16"] * rms

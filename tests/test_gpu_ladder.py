@@ -39,6 +39,11 @@ CASES = [
     ("zonos2-decode", None, [8, 16, 32, 64], [5, 64, 17]),
     ("prefill-shape", (2048, 256, 8, 2, 256, orc.SELECTED_SOFTMAX, 0.5), [512, 1024, 2048],
      [700, 2048, 513]),
+    # ZONOS3-Mini widths with a largest batch past the split router's limit (256 tokens): the
+    # workspace sized for 300 tokens must also hold the split router's partials of the smaller
+    # buckets
+    ("zonos3mini-widths-T300", (300, 1024, 64, 2, 512, orc.SELECTED_SOFTMAX, 0.5),
+     [16, 64, 256, 300], [300, 16, 200, 64, 256]),
 ]
 
 
