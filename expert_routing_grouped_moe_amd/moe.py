@@ -39,7 +39,9 @@ SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELEC
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_quantize_rows_i8", "moe_quantize_groups_q4", "moe_ladder_create", "moe_ladder_run",
-           "moe_ladder_destroy")
+           "moe_ladder_destroy", "moe_layer_forward_noalloc")
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MOE_LADDER_MAX_BUCKETS = 256
 
@@ -98,6 +100,8 @@ def _load() -> ctypes.CDLL:
                                 c_int, c_void_p]
     lib.moe_layer_forward.restype = c_int
     lib.moe_layer_forward.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_size_t, c_void_p]
+    lib.moe_layer_forward_noalloc.restype = c_int
+    lib.moe_layer_forward_noalloc.argtypes = [POINTER(MoeLayerArgs), c_void_p]
     lib.moe_quantize_rows_i8.restype = c_int
     lib.moe_quantize_rows_i8.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
                                          c_void_p, c_void_p]
@@ -348,6 +352,22 @@ def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     _check(LIB.moe_layer_forward(ctypes.byref(args), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "moe_layer_forward")
+    return y
+
+
+def moe_layer_forward_noalloc(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
+                              sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
+                              expert_counts=None, stream=None, args=None, w_scales=None,
+                              y_dtype=torch.float32):
+    """The fused layer on the library's fixed scratch array (no workspace argument, nothing
+    allocated by the library; see moe_layer_forward_noalloc in include/moe.h). Returns y."""
+    T, d = x.shape
+    y = _empty((T, d), y_dtype, x) if y is None else y
+    if args is None:
+        args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias,
+                               sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales)
+    _check(LIB.moe_layer_forward_noalloc(ctypes.byref(args), _stream(stream)),
+           "moe_layer_forward_noalloc")
     return y
 
 

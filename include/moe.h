@@ -262,6 +262,28 @@ typedef struct moe_layer_args {
 int moe_layer_forward(const moe_layer_args* args, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The fused layer for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid device allocation): moe_layer_forward with its workspace in a
+ * fixed device array of the library (MOE_NOALLOC_SCRATCH_BYTES per GPU, created with the
+ * library's code object on each GPU it runs on and held until the process ends) instead of a
+ * caller-provided buffer. The caller still passes every input and output through `a`.
+ *   - Shapes whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE
+ *     with nothing enqueued (the five model workloads of this library need at most 45 MB).
+ *   - Allocates nothing: no hipMalloc, no hipFree. The first call on a device looks up the
+ *     array's device address (hipGetSymbolAddress, with that device current) and keeps it; make
+ *     that first call outside graph capture.
+ *   - Every call on one GPU shares that GPU's array and finds the previous call's contents
+ *     there (nothing in it needs clearing: every region is written before it is read). Calls
+ *     that overlap in time on one GPU (different streams, or host threads racing) race on it:
+ *     serialise them.
+ *   - Results are identical to moe_layer_forward with its own workspace (same kernels).
+ * Added in ABI 4.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int moe_layer_forward_noalloc(const moe_layer_args* a, void* stream);
+
+/*
  * Symmetric per-row int8 codes of a row-major [rows, K] weight matrix (an expert stack is
  * rows = E * N rows of length K): for each row r,
  *   scales[r] = fp32(max_i |w[r,i]| / 127)                       (one IEEE round-to-nearest-even

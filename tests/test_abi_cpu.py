@@ -178,6 +178,26 @@ def test_layer_forward_validation():
     assert run(_args(prof_events=FAKE.value), n=0) == moe.MOE_ERR_WORKSPACE
 
 
+def test_layer_forward_noalloc_validation():
+    # checked on the host before any device call: sizes past the fixed scratch array are refused
+    L = moe.LIB
+    run = lambda a: L.moe_layer_forward_noalloc(ctypes.byref(a), None)
+    assert L.moe_layer_forward_noalloc(None, None) == moe.MOE_ERR_NULL
+    assert run(_args(struct_size=8)) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(T=0)) == moe.MOE_OK
+    assert run(_args(k=3, E=2)) == moe.MOE_ERR_SHAPE
+    big = dict(T=16384, d=2048, E=16, H=2816, k=1)          # h alone is 92 MB
+    assert L.moe_workspace_size(16384, 2048, 16, 2816, 1, 1) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert run(_args(**big)) == moe.MOE_ERR_WORKSPACE
+    hdr = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert hdr and int(hdr.group(1)) << int(hdr.group(2)) == moe.MOE_NOALLOC_SCRATCH_BYTES
+    # the five workloads fit
+    for (T, d, E, H, k, dt) in ((64, 128, 8, 256, 1, 0), (64, 2048, 16, 2816, 1, 1),
+                                (64, 1024, 64, 512, 2, 1), (4096, 1024, 64, 512, 2, 1),
+                                (8192, 2048, 16, 2816, 1, 1)):
+        assert 0 < L.moe_workspace_size(T, d, E, H, k, dt) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_layer_int8_weight_validation():
     L = moe.LIB
     # a decode shape of the weight-streaming path (d, H multiples of 256, few rows per expert)
