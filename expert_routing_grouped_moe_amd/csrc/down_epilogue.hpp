@@ -47,4 +47,28 @@ __device__ __forceinline__ void down_put(const DownArgs& a, const DownRow& r, in
   }
 }
 
+// Four consecutive outputs n .. n + 3 (fp32 bits in v), delivered as down_put does for each:
+// one 16-byte store (8 bytes for a bf16 y) where the mode stores.
+__device__ __forceinline__ void down_put4(const DownArgs& a, const DownRow& r, int n, u32x4 v) {
+  if (a.mode == kDownAtomicY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      unsafeAtomicAdd(static_cast<float*>(r.dst) + n + i, r.scale * __uint_as_float(v[i]));
+  } else if (a.mode == kDownStoreY) {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = r.scale * __uint_as_float(v[i]);
+    if (a.y_bf16) {
+      const uint32_t lo = f32_to_bf16_bits(o[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16);
+      const uint32_t hi = f32_to_bf16_bits(o[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(o[3])) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(r.dst) + n) = make_uint2(lo, hi);
+    } else {
+      store16(static_cast<float*>(r.dst) + n, u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                                    __float_as_uint(o[2]), __float_as_uint(o[3])});
+    }
+  } else {
+    store16(static_cast<float*>(r.dst) + n, v);
+  }
+}
+
 }  // namespace moe

@@ -282,33 +282,57 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     if (wave_live) compute(kt % RING);
   }
   wait_vmcnt<0>();                          // prologue re-reads (K < 3 steps) have landed too
+  block_barrier();                          // every wave is done with the ring: reuse it below
 
+  // Epilogue through LDS: each wave stages one 16-row block of its results at a time in a private
+  // part of the ring, then writes whole 16-byte pieces of output rows (gate/up: 8 fp16 h values;
+  // down: 4 fp32 values), so that every store instruction covers 4 rows x 64 (h) or 256 (y) bytes.
+  if (!wave_live) return;
+  constexpr int CW = GATEUP ? WN / 2 : WN;             // output columns per wave
+  constexpr int EB = GATEUP ? 2 : 4;                   // bytes per output element
+  constexpr int PITCH = CW * EB + 16;                  // staging row pitch in bytes (padded)
+  char* stage = reinterpret_cast<char*>(ring) + wave * 16 * PITCH;
+  const int c0 = n0 + wn * CW;                         // first output column of this wave
+  constexpr int PR = CW * EB / 16;                     // 16-byte pieces per staged row
+  static_assert(PR >= 1 && 64 % PR == 0, "pieces per row");
+  constexpr int RPI = 64 / PR;                         // staged rows covered per instruction
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    if (mb >= live_mb) continue;
+    if (mb >= live_mb) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = wm * WROWS + mb * 16 + (lane >> 4) * 4 + r;
-      if (row >= ti.rows) continue;
-      const int p = ti.row0 + row;
-      if (GATEUP) {
+      const int sr = (lane >> 4) * 4 + r;              // staged row (0..15)
+      if constexpr (GATEUP) {
 #pragma unroll
         for (int cb = 0; cb < NBK / 2; ++cb) {
-          const int f = n0 + wn * (WN / 2) + cb * 16 + l16;
-          if (f < N) {
-            const float hv = silu(acc[mb][cb][r]) * acc[mb][cb + NBK / 2][r];
-            h_out[static_cast<long long>(p) * N + f] = f32_to_f16_bits_sat(hv);
-          }
+          const float hv = silu(acc[mb][cb][r]) * acc[mb][cb + NBK / 2][r];
+          *reinterpret_cast<uint16_t*>(stage + sr * PITCH + (cb * 16 + l16) * 2) = f32_to_f16_bits_sat(hv);
         }
       } else {
-        const DownRow dr = down_row(down, sorted_rows[p], p, N);
 #pragma unroll
-        for (int cb = 0; cb < NBK; ++cb) {
-          const int f = n0 + wn * WN + cb * 16 + l16;
-          if (f < N) down_put(down, dr, f, acc[mb][cb][r]);
+        for (int cb = 0; cb < NBK; ++cb)
+          *reinterpret_cast<float*>(stage + sr * PITCH + (cb * 16 + l16) * 4) = acc[mb][cb][r];
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging is in LDS
+#pragma unroll
+    for (int it = 0; it < 16 / RPI; ++it) {
+      const int sr = it * RPI + lane / PR;             // staged row this lane writes
+      const int pc = lane % PR;                        // its 16-byte piece
+      const int row = wm * WROWS + mb * 16 + sr;
+      const int col = c0 + pc * (16 / EB);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + sr * PITCH + pc * 16);
+      if (row < ti.rows && col < N) {
+        const int p = ti.row0 + row;
+        if constexpr (GATEUP) {
+          store16(h_out + static_cast<long long>(p) * N + col, v);
+        } else {
+          const DownRow dr = down_row(down, sorted_rows[p], p, N);
+          down_put4(down, dr, col, v);
         }
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next block's writes
   }
 }
 
