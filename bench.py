@@ -13,9 +13,10 @@ prefill) are timed in the same run and reported under `workloads`, each with its
 
 Cold weights: each workload's expert weights are kept in several identical copies and
 consecutive steps rotate through them, so that no step finds its weights in the 256 MB Infinity
-Cache left over from the step before (the copies together exceed 1.5 GB). One HIP graph per copy
-holds one captured step (the decode loop of the pages replays a captured graph); the timed region
-replays exactly `--steps` of them, after exactly `--warmup` untimed ones, bracketed by
+Cache left over from the step before (the copies together exceed 1.5 GB). The steps are replayed
+from HIP graphs (the decode loop of the pages replays a captured graph): one graph holding a whole
+cycle of steps over the copies, and one single-step graph per copy for a partial cycle, so that the
+timed region runs exactly `--steps` steps after exactly `--warmup` untimed ones, bracketed by
 synchronizations. `value` = T / (wall time per step).
 
 Kernel durations come from a second, host-launched pass over the same copies with the layer's
@@ -331,6 +332,13 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
         with torch.cuda.graph(g, stream=stream):
             one_step(c, False)
         graphs.append(g)
+    # one more graph holding a whole cycle of steps (copies 0 .. ncopies-1 in order): replayed
+    # where a cycle fits, so that fewer graph launches sit between steps; the single-step graphs
+    # cover the rest, so exactly the requested number of steps runs
+    cycle = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cycle, stream=stream):
+        for c in range(ncopies):
+            one_step(c, False)
     y.fill_(float("nan"))
     graphs[0].replay()
     torch.cuda.synchronize()
@@ -341,9 +349,15 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
             with torch.cuda.stream(stream):
                 for i in range(first, first + n):
                     one_step(i % ncopies, False)
-        else:
-            for i in range(first, first + n):
+            return
+        i, end = first, first + n
+        while i < end:
+            if i % ncopies == 0 and end - i >= ncopies:
+                cycle.replay()
+                i += ncopies
+            else:
                 graphs[i % ncopies].replay()
+                i += 1
 
     run_steps(warmup, 0)
     torch.cuda.synchronize()
@@ -409,7 +423,8 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
                                       "q4": "4-bit affine, groups of 64, bf16 scale and bias"
                                       }.get(weights, inp.dtype),
                    "timing": ("host launches" if eager else
-                              "HIP graph replay, one captured step per weight copy")},
+                              "HIP graph replay: cycles of one step per weight copy, single "
+                              "steps for a partial cycle")},
         "step_hbm_gbps": alg["step_bytes"] / step_s / 1e9,
         "step_hbm_frac": alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
         "step_tflops": alg["step_flops"] / step_s / 1e12,
@@ -427,7 +442,7 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
     for evs in events:
         for e in evs:
             hip.hipEventDestroy(e)
-    del graphs, copies, base, x, wr, y, ws
+    del graphs, cycle, copies, base, x, wr, y, ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
