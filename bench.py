@@ -245,7 +245,7 @@ def dominant_kernel(inp, weights="native"):
 
 def gemm_kernel_name(rows, E, gateup):
     """Name of the grouped-GEMM instantiation for `rows` assignment rows over E experts."""
-    if rows >= 256 * E:     # experts average a full 256-row tile: XCD-ordered wide tiles
+    if rows >= 256 * E:     # experts average a full 256-row tile: the wide tiles
         return ("gemm_dma_kernel<true, 256, 256, 2, 64, 64>" if gateup
                 else "gemm_dma_kernel<false, 256, 128, 3, 64, 32>")
     return ("gemm_dma_kernel<true, 128, 256, 3, 64, 32>" if gateup

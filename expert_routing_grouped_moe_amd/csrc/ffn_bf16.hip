@@ -37,27 +37,20 @@ namespace {
 // ------------------------------------------------------------------------------------ prefill
 
 // Block -> tile. `tiles` is the exact number of row tiles (computed on the device from the
-// offsets); blocks past the last tile exit.
-//  * plain (few rows per expert, little reuse of a weight tile): column tiles fastest;
-//  * XCD-aware: the hardware hands block b to XCD b % kXcds (kXcds L2 domains of 4 MB); XCD x
-//    takes a contiguous range of the tile order, and that order runs through groups of kXcdGroup
-//    row tiles with the row tile fastest, so the blocks sharing an XCD's L2 at one time also share
-//    most of their A and B tiles. Lines that miss the L2 come from the Infinity Fabric at little
-//    more than HBM speed (~7 TB/s measured even for data resident in the Infinity Cache); on the
-//    skewed prefill this cut the fetched bytes by ~40 % and the time by ~8 %.
+// offsets); blocks past the last tile exit. XCD-aware order: the hardware hands block b to XCD
+// b % kXcds (kXcds L2 domains of 4 MB); XCD x takes a contiguous range of the tile order, and that
+// order runs through groups of kXcdGroup row tiles with the row tile fastest, so the blocks sharing
+// an XCD's L2 at one time also share most of their A and B tiles. Lines that miss the L2 come from
+// the Infinity Fabric at little more than HBM speed (~7 TB/s measured even for data resident in
+// the Infinity Cache). Against column tiles fastest over the whole grid: skewed prefill ~40 % fewer
+// bytes fetched and ~8 % less time; ZONOS3-Mini prefill (about one row tile per expert) ~2 % less
+// time per step.
 constexpr int kXcds = 8;
 constexpr int kXcdGroup = 4;
 
-__device__ __forceinline__ bool prefill_tile_of_block(int ntn, int tiles, bool xcd, int* m,
-                                                      int* n) {
+__device__ __forceinline__ bool prefill_tile_of_block(int ntn, int tiles, int* m, int* n) {
   const long long total = static_cast<long long>(ntn) * tiles;
   const long long b = blockIdx.x;
-  if (!xcd) {
-    if (b >= total) return false;
-    *m = static_cast<int>(b / ntn);
-    *n = static_cast<int>(b % ntn);
-    return true;
-  }
   const long long per = (total + kXcds - 1) / kXcds;
   const long long j = b / kXcds;
   if (j >= per) return false;
@@ -73,15 +66,15 @@ __device__ __forceinline__ bool prefill_tile_of_block(int ntn, int tiles, bool x
   return true;
 }
 
-// Blocks a launch needs for up to `max_row_tiles` row tiles. XCD-aware: tile L sits at block
+// Blocks a launch needs for up to `max_row_tiles` row tiles: tile L sits at block
 // (L % per) * kXcds + L / per, which reaches up to kXcds * per - 1 >= total - 1.
-inline long long prefill_grid(long long max_row_tiles, int ntn, bool xcd) {
+inline long long prefill_grid(long long max_row_tiles, int ntn) {
   const long long total = max_row_tiles * ntn;
-  return xcd ? (total + kXcds - 1) / kXcds * kXcds : total;
+  return (total + kXcds - 1) / kXcds * kXcds;
 }
 
-// XCD-aware order once the experts average a full row tile or more (weight tiles reused).
-inline bool prefill_xcd_order(int rows, int E, int bm) {
+// The wide tiles once the experts average a full 256-row tile or more.
+inline bool prefill_wide_tiles(int rows, int E, int bm) {
   return rows >= static_cast<long long>(bm) * E;
 }
 
@@ -147,7 +140,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
     const uint16_t* __restrict__ W1, int K, int N, int E, int k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
-    uint16_t* __restrict__ h_out, DownArgs down, bool xcd) {
+    uint16_t* __restrict__ h_out, DownArgs down) {
   constexpr int WMW = BM / WROWS;           // waves along M (WROWS rows each)
   constexpr int WNW = BN / 64;              // waves along N (64 columns each)
   constexpr int NW = WMW * WNW;             // waves per block
@@ -169,7 +162,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
   const int ntn = (N + FEAT - 1) / FEAT;
   const int tiles = tile_scan(offsets, E, BM, sh_tiles);
   int mt, nt;
-  if (!prefill_tile_of_block(ntn, tiles, xcd, &mt, &nt)) return;
+  if (!prefill_tile_of_block(ntn, tiles, &mt, &nt)) return;
   const TileInfo ti = tile_lookup(E, BM, mt, sh_tiles);
   if (ti.e < 0) return;
   const int tid = threadIdx.x;
@@ -612,13 +605,13 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
 }  // namespace
 
 // Prefill tile configurations, chosen from the shape (eight or sixteen waves of 64 x 64, 3-slot
-// rings of 32-wide K steps at two blocks per CU unless stated otherwise):
-//  * fewer rows than a full 256-row tile per expert on average (plain tile order, zonos3mini
-//    prefill): 128 x 256 tiles for both products (gate/up: 128 gate + 128 up features). Against
+// rings of 32-wide K steps at two blocks per CU unless stated otherwise; XCD-aware tile order):
+//  * fewer rows than a full 256-row tile per expert on average (zonos3mini prefill): 128 x 256
+//    tiles for both products (gate/up: 128 gate + 128 up features). Against
 //    256 x 128 tiles the grid shrinks from 632 to ~440 blocks (one round of the block slots),
 //    small experts pad half as many rows, and each weight fragment of the down product is
 //    converted to fp16 by two waves instead of four: gate/up 55 -> 48 us, down 55 -> 47 us.
-//  * a full row tile per expert or more (XCD-ordered tiles, zonos2 skewed prefill): gate/up on
+//  * a full row tile per expert or more (zonos2 skewed prefill): gate/up on
 //    256 x 256 tiles with 64-wide K steps in a 2-slot ring (128 KB, one block per CU): 128-byte row
 //    segments copy from L2 at twice the rate of 64-byte ones and the wider tile copies a third
 //    less per product (gate/up 215 against 233 us). The down product keeps 256 x 128 tiles
@@ -666,17 +659,17 @@ hipError_t launch_streaming(const uint16_t* x, const void* wg, const void* wu, c
 // One grouped-GEMM launch: BM x BN tiles (gate/up: BN / 2 gate and BN / 2 up features) with
 // BK-wide K steps in a RING-slot ring, 64 x 64 waves.
 template <bool GATEUP, int BM, int BN, int RING, int BK>
-hipError_t launch_gemm(int rows, int E, bool xcd, hipStream_t s, const StageMarks& marks,
+hipError_t launch_gemm(int rows, int E, hipStream_t s, const StageMarks& marks,
                        const uint16_t* A, const void* W0, const void* W1, int K, int N, int k,
                        const RowSource& rs, uint16_t* h, const DownArgs& down) {
   constexpr int NT = BM / kTileWaveRows * (BN / 64) * kWave;
   constexpr int FEAT = GATEUP ? BN / 2 : BN;
   const int ntn = (N + FEAT - 1) / FEAT;
-  const long long grid = prefill_grid(max_tiles(rows, E, BM), ntn, xcd);
+  const long long grid = prefill_grid(max_tiles(rows, E, BM), ntn);
   return launch_marked(gemm_dma_kernel<GATEUP, BM, BN, RING, kTileWaveRows, BK>,
                        dim3(static_cast<unsigned>(grid)), dim3(NT), s, marks, A,
                        static_cast<const uint16_t*>(W0), static_cast<const uint16_t*>(W1), K, N,
-                       E, k, rs.offsets, rs.sorted_rows, h, down, xcd);
+                       E, k, rs.offsets, rs.sorted_rows, h, down);
 }
 
 }  // namespace
@@ -701,18 +694,16 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, co
   if (qw.fmt != kWBf16) return hipErrorInvalidValue;
   // grouped GEMM over the dispatch order; 1-D grids sized for the worst-case tile count
   const StageMarks no_marks{};
-  if (prefill_xcd_order(rows, E, kTileM)) {
-    err = launch_gemm<true, 256, 256, 2, 64>(rows, E, true, s, gu, x, wg, wu, d, H, k, rs, h,
-                                             none);
+  if (prefill_wide_tiles(rows, E, kTileM)) {
+    err = launch_gemm<true, 256, 256, 2, 64>(rows, E, s, gu, x, wg, wu, d, H, k, rs, h, none);
     if (err != hipSuccess) return err;
-    return launch_gemm<false, 256, 128, 3, 32>(rows, E, true, s, no_marks, h, wd, nullptr, H, d,
-                                               k, rs, nullptr, down);
+    return launch_gemm<false, 256, 128, 3, 32>(rows, E, s, no_marks, h, wd, nullptr, H, d, k, rs,
+                                               nullptr, down);
   }
-  err = launch_gemm<true, 128, 256, 3, 32>(rows, E, false, s, gu, x, wg, wu, d, H, k, rs, h,
-                                           none);
+  err = launch_gemm<true, 128, 256, 3, 32>(rows, E, s, gu, x, wg, wu, d, H, k, rs, h, none);
   if (err != hipSuccess) return err;
-  return launch_gemm<false, 128, 256, 3, 32>(rows, E, false, s, no_marks, h, wd, nullptr, H, d, k,
-                                             rs, nullptr, down);
+  return launch_gemm<false, 128, 256, 3, 32>(rows, E, s, no_marks, h, wd, nullptr, H, d, k, rs,
+                                             nullptr, down);
 }
 
 }  // namespace moe

@@ -119,7 +119,7 @@ def test_dominant_kernel_names(bench):
     assert bench.dominant_kernel(mk(64, 2048, 16, 1, 2816)) == "ffn_stream_kernel<true, 1, 0>"
     assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512)) == "ffn_stream_kernel<true, 2, 0>"
     assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512), "q4") == "ffn_stream_kernel<true, 2, 2>"
-    # prefill shapes: the grouped GEMM, wide XCD-ordered tiles once experts average 256 rows
+    # prefill shapes: the grouped GEMM, wide tiles once experts average 256 rows
     assert bench.dominant_kernel(mk(8192, 2048, 16, 1, 2816)).startswith("gemm_dma_kernel<true, 256, 256")
     assert bench.dominant_kernel(mk(4096, 1024, 64, 2, 512)).startswith("gemm_dma_kernel<true, 128, 256")
     assert bench.dominant_kernel(mk(64, 128, 8, 1, 256, "f32")) == "ffn_f32_kernel<true>"

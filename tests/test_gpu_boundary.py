@@ -54,7 +54,7 @@ def _setup(name, y_dtype):
 
 # every expert-kernel family and combine rule: fp32 path (k = 1), streaming k = 1 (stored into
 # y), streaming k = 2 (fp32 atomics, staged for a bf16 y), grouped GEMM k = 2 (staged), grouped
-# GEMM k = 1 with XCD-ordered tiles (stored into y)
+# GEMM k = 1 with the wide tiles (stored into y)
 BF16_Y = ["tiny-fp32", "zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill",
           "zonos2-skewed-prefill"]
 

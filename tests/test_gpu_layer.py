@@ -64,10 +64,10 @@ EDGE = [
     ("prefill-zonos2-widths", 1200, 2048, 16, 1, 2816, orc.SOFTMAX, "bf16", None, None),
     # many experts: 29 empty, 20 with 1..32 rows, 15 larger (one with 1212 rows)
     ("prefill-small-experts", 1500, 256, 64, 2, 256, orc.SELECTED_SOFTMAX, "bf16", 2.0, None),
-    # >= one full row tile per expert on average: XCD-ordered tiles, here with empty experts
+    # >= one full row tile per expert on average: the wide tiles, here with empty experts
     ("prefill-xcd-hot-expert", 2100, 128, 8, 1, 192, orc.SOFTMAX, "bf16", None, "hot5"),
     # k = 1 with long down reductions (H >= 1024, 32 or 34 K steps; the weighted output is stored
-    # straight into y): XCD-ordered tiles with one hot expert, and a ragged last tile
+    # straight into y): the wide tiles with one hot expert, and a ragged last tile
     ("prefill-long-down-hot", 2100, 256, 8, 1, 1024, orc.SOFTMAX, "bf16", None, "hot5"),
     ("prefill-long-down-ragged", 333, 128, 4, 1, 1088, orc.SOFTMAX, "bf16", None, None),
     ("f32-prefill", 600, 128, 4, 1, 128, orc.SOFTMAX, "f32", None, None),
@@ -94,7 +94,7 @@ def test_layer_edge_cases(case):
     name, T, d, E, k, H, scoring, dtype, sbv, rb = case
     if name.startswith("stream-"):  # the shape rule of the weight-streaming path
         assert T * k <= 2048 and T * k <= 32 * E and d % 256 == 0 and H % 256 == 0, name
-    if "xcd" in name:               # XCD-ordered tiles: a full 256-row tile per expert or more
+    if "xcd" in name:               # the wide tiles: a full 256-row tile per expert or more
         assert T * k >= 256 * E, name
     router_bias = None
     if rb == "hot5":
@@ -111,8 +111,8 @@ def test_layer_edge_cases(case):
 
 LARGE = [
     # beyond the workloads' sizes: 65536 assignment rows over 64 experts (row tiles of 256 narrow
-    # tiles, plain tile order), and 32768 tokens over 16 experts (the wide gate/up tiles, XCD
-    # order, 11 rounds of block slots), checked on sampled tokens
+    # tiles), and 32768 tokens over 16 experts (the wide gate/up tiles, 11 rounds of block slots),
+    # checked on sampled tokens
     ("32k-top2-of-64", 32768, 1024, 64, 2, 512, orc.SELECTED_SOFTMAX, 0.5),
     ("32k-top1-of-16", 32768, 2048, 16, 1, 2816, orc.SOFTMAX, None),
 ]
