@@ -421,15 +421,16 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
                                             const void* __restrict__ W1,
                                             const void* __restrict__ S0,
                                             const void* __restrict__ S1, int K, int N, int k,
-                                            int e, const int* lr, int m0, int rows, int hbase,
-                                            uint16_t* __restrict__ h_out, const DownArgs& down) {
+                                            int e, int slab, const int* lr, int m0, int rows,
+                                            int hbase, uint16_t* __restrict__ h_out,
+                                            const DownArgs& down) {
   constexpr bool W8 = WF == kWI8, W4 = WF == kWQ4;
   constexpr int WR = W8 ? 2 : (W4 ? 1 : 4);   // weight registers (u32x4) per matrix per block
   const int lane = lane_id();
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int kq = W8 ? 32 * grp : 8 * grp;     // lane's first k inside a 128-k block
-  const int f = blockIdx.x * kStFeat + l16;  // weight row (N % 16 == 0)
+  const int f = slab * kStFeat + l16;        // weight row (N % 16 == 0)
   const long long row0 = static_cast<long long>(e) * N + f;
   // bytes: bf16 2 per weight, int8 1, 4-bit one half (a lane's 16 bytes of a block hold the
   // codes of its k = 32 c + 8 g runs, as packed by moe_quantize_groups_q4)
@@ -455,7 +456,9 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     pa[g] = A + arow * K + kq;
   }
   const int nb = NB > 0 ? NB : K / 128;       // even: K % 256 == 0 on this path
-  const int rot = ((blockIdx.y * gridDim.x + blockIdx.x) * 5) % nb;
+  // the same for the whole wave; without the explicit broadcast the compiler keeps the rotated
+  // block indices in vector registers and the kernel's register use doubles
+  const int rot = __builtin_amdgcn_readfirstlane(((e * (N / kStFeat) + slab) * 5) % nb);
 
   u32x4 a[2][NG][4], bg[2][WR], bu[2][WR];     // two blocks in flight, slot = block % 2
   uint2 pgs[2], pus[2];                        // 4-bit: the block's (scale, bias) pairs
@@ -554,24 +557,68 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   }
 }
 
-// Grid (N / 16, E), one wave per block: block (x, e) computes features [16 x, 16 x + 16) of
-// expert e for all of the expert's rows, up to 16 MAXG rows per pass over the weights (a further
-// pass mostly hits the caches). MAXG = 2 lets an expert with 17..32 rows, common under a
-// selection bias, read its weights once, at the cost of registers (fewer resident waves).
-// WF (WeightFormat): bf16 weights; int8 codes with fp32 row scales S0 (gate or down) and S1
-// (up); or packed 4-bit codes with (scale, bias) pairs S0 and S1.
+// Grid (N / 16, E), one wave per block. Each block computes 16 features of one expert for all of
+// the expert's rows, up to 16 MAXG rows per pass over the weights (a further pass mostly hits the
+// caches). MAXG = 2 lets an expert with 17..32 rows, common under a selection bias, read its
+// weights once, at the cost of registers (fewer resident waves). WF (WeightFormat): bf16 weights;
+// int8 codes with fp32 row scales S0 (gate or down) and S1 (up); or packed 4-bit codes with
+// (scale, bias) pairs S0 and S1.
+// Block to (expert, slab): with fewer than kStCompactMinE experts, block (x, y) takes slab x of
+// expert y. With more, most experts have no rows on a decode step, and a CU whose blocks all fell
+// on routed experts carried about twice the average load and set the kernel's end (ZONOS3-Mini
+// decode: the median wave ended ~15 us after the start, the last ~22 us). There the blocks are
+// work items over the experts that have rows: item i = y (N / 16) + x takes slab i % (N / 16) of
+// the (i / (N / 16))-th such expert, and items past the last one exit at once, so the active items
+// sit at the start of the grid and spread evenly over the CUs (blocks are dispatched in order,
+// round robin over the XCDs). Gate/up 21.3 -> 19.9 us on that workload; with 16 experts, all of
+// them routed on a decode step, the extra count pass only cost time.
+constexpr int kStCompactMinE = 32;
+
 template <bool GATEUP, int MAXG, int WF>
 __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ W0, const void* __restrict__ W1,
     const void* __restrict__ S0, const void* __restrict__ S1, int K, int N, int k,
     RowSource rs, uint16_t* __restrict__ h_out, DownArgs down) {
   __shared__ int lr[kMaxScanRows];
-  const int e = blockIdx.y;
+  __shared__ int cnt[kMaxE];
+  const int lane = lane_id();
+  const int E = gridDim.y;
+  int e = blockIdx.y, slab = blockIdx.x;
+  if (E >= kStCompactMinE) {
+    const int slabs = gridDim.x;
+    const int item = blockIdx.y * slabs + blockIdx.x;
+    // rows per expert: from the ids (one LDS add per id) or from the dispatch offsets
+    for (int i = lane; i < E; i += kWave) cnt[i] = rs.ids ? 0 : rs.offsets[i + 1] - rs.offsets[i];
+    if (rs.ids) {
+      __builtin_amdgcn_wave_barrier();
+      for (int r = lane; r < rs.n_rows; r += kWave)
+        atomicAdd(&cnt[min(max(rs.ids[r], 0), E - 1)], 1);
+    }
+    __syncthreads();
+    if (rs.counts_out && item < E && lane == 0) rs.counts_out[item] = cnt[item];
+    // the (item / slabs)-th expert with rows
+    int a = item / slabs;
+    e = -1;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+      const unsigned long long m = __ballot(c0 + lane < E && cnt[c0 + lane] > 0);
+      const int pc = __popcll(m);
+      if (a < pc) {
+        unsigned long long mm = m;
+        for (int i = 0; i < a; ++i) mm &= mm - 1;     // drop the a lowest set bits
+        e = c0 + __ffsll(static_cast<long long>(mm)) - 1;
+        break;
+      }
+      a -= pc;
+    }
+    if (e < 0) return;                                // past the last expert with rows
+    slab = item % slabs;
+  }
   int count, hbase;
   if (rs.ids) {
     count = scan_rows(rs.ids, rs.n_rows, e, lr);
     hbase = -1;
-    if (rs.counts_out && blockIdx.x == 0 && threadIdx.x == 0) rs.counts_out[e] = count;
+    if (E < kStCompactMinE && rs.counts_out && blockIdx.x == 0 && lane == 0)
+      rs.counts_out[e] = count;
   } else {
     hbase = rs.offsets[e];
     count = rs.offsets[e + 1] - hbase;
@@ -586,10 +633,10 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
     auto tile = [&](auto nb_const) {
       constexpr int NB = decltype(nb_const)::value;
       if (MAXG > 1 && rows > 16)
-        stream_tile<GATEUP, MAXG, WF, NB>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase,
-                                          h_out, down);
+        stream_tile<GATEUP, MAXG, WF, NB>(A, W0, W1, S0, S1, K, N, k, e, slab, lr, m0, rows,
+                                          hbase, h_out, down);
       else
-        stream_tile<GATEUP, 1, WF, NB>(A, W0, W1, S0, S1, K, N, k, e, lr, m0, rows, hbase,
+        stream_tile<GATEUP, 1, WF, NB>(A, W0, W1, S0, S1, K, N, k, e, slab, lr, m0, rows, hbase,
                                        h_out, down);
     };
     switch (K) {
