@@ -99,6 +99,11 @@ hipError_t launch_route_fused_bf16(const uint16_t* x, const uint16_t* wr, const 
 hipError_t launch_dispatch(const int32_t* ids, int n_rows, int E, int32_t* offsets,
                            int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,
                            hipStream_t s);
+// counts[e] = #{r < n_rows : ids[r] == e} (one block; E <= kMaxE)
+hipError_t launch_counts(const int32_t* ids, int n_rows, int E, int32_t* counts, hipStream_t s);
+// Byte offset, inside the layer's workspace, of the expert ids that moe_layer_forward writes there
+// when the caller passes no topk_ids (same sizes as moe_workspace_size).
+size_t layer_ids_offset(int T, int d, int E, int H, int k, int dtype);
 
 // ---------------------------------------------------------------- experts (ffn_*.hip)
 // Where a grouped FFN finds the rows of expert e:

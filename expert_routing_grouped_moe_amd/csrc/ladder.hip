@@ -1,18 +1,24 @@
 // Graph ladder: one captured HIP graph of the whole layer per batch-size bucket, so that a decode
 // loop whose batch width changes from step to step replays a graph instead of launching kernels
 // (zonos2.cpp INTERNALS, "Performance": the decode graph is captured once and replayed). Host code
-// only; every graph is a capture of moe_layer_forward itself.
+// only; every graph is a capture of moe_layer_forward itself. A bucket larger than the step's T
+// also routes the padding rows, so when the caller wants expert counts they are recounted from the
+// first T rows' ids after the replay.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
 #include <new>
 
+#include "kernels.hpp"
 #include "moe.h"
 
 struct moe_graph_ladder {
   int n;
   int32_t bucket[MOE_LADDER_MAX_BUCKETS];
   hipGraphExec_t exec[MOE_LADDER_MAX_BUCKETS];
+  const int32_t* ids[MOE_LADDER_MAX_BUCKETS];  // where bucket i's graph leaves the expert ids
+  int32_t* counts;                             // the caller's expert_counts, or NULL
+  int k, E;
 };
 
 namespace {
@@ -48,6 +54,9 @@ int moe_ladder_create(const moe_layer_args* a, const int32_t* buckets, int n_buc
   moe_graph_ladder* l = new (std::nothrow) moe_graph_ladder;
   if (!l) return MOE_ERR_HIP;
   l->n = 0;
+  l->counts = a->expert_counts;
+  l->k = a->k;
+  l->E = a->E;
   moe_layer_args ab;
   std::memset(&ab, 0, sizeof(ab));
   std::memcpy(&ab, a, a->struct_size);
@@ -75,6 +84,11 @@ int moe_ladder_create(const moe_layer_args* a, const int32_t* buckets, int n_buc
     }
     l->bucket[i] = buckets[i];
     l->exec[i] = exec;
+    l->ids[i] = a->topk_ids ? a->topk_ids
+                            : reinterpret_cast<const int32_t*>(
+                                  static_cast<const char*>(ws) +
+                                  moe::layer_ids_offset(buckets[i], a->d, a->E, a->H, a->k,
+                                                        a->dtype));
     l->n = i + 1;
   }
   *out = l;
@@ -88,8 +102,13 @@ int moe_ladder_run(const moe_graph_ladder* l, int T, void* stream, int32_t* buck
   while (l->bucket[i] < T) ++i;
   if (bucket_out) *bucket_out = l->bucket[i];
   (void)hipGetLastError();
-  return hipGraphLaunch(l->exec[i], static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
-                                                                                  : MOE_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipGraphLaunch(l->exec[i], s) != hipSuccess) return MOE_ERR_HIP;
+  // the graph counted the padding rows T..b-1 as well
+  if (l->counts && l->bucket[i] > T &&
+      moe::launch_counts(l->ids[i], T * l->k, l->E, l->counts, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 void moe_ladder_destroy(moe_graph_ladder* l) {

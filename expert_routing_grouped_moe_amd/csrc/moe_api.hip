@@ -110,6 +110,9 @@ bool capturing(hipStream_t s) {
 
 namespace moe {
 hipError_t record_stage_event(void* ev, hipStream_t s) { return record_event(ev, s); }
+size_t layer_ids_offset(int T, int d, int E, int H, int k, int dtype) {
+  return Layout(T, d, E, H, k, dtype).ids;
+}
 }  // namespace moe
 
 extern "C" {

@@ -169,7 +169,24 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   }
 }
 
+// counts[e] = number of ids equal to e among ids[0..n): one block, an LDS histogram.
+__global__ __launch_bounds__(kDispThreads) void counts_kernel(const int32_t* __restrict__ ids,
+                                                              int n, int E,
+                                                              int32_t* __restrict__ counts) {
+  __shared__ int hist[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kDispThreads) hist[e] = 0;
+  __syncthreads();
+  for (int r = threadIdx.x; r < n; r += kDispThreads) atomicAdd(&hist[clamp_id(ids[r], E)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kDispThreads) counts[e] = hist[e];
+}
+
 }  // namespace
+
+hipError_t launch_counts(const int32_t* ids, int n_rows, int E, int32_t* counts, hipStream_t s) {
+  counts_kernel<<<1, kDispThreads, 0, s>>>(ids, n_rows, E, counts);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const int32_t* ids, int n_rows, int E, int32_t* offsets,
                            int32_t* sorted_rows, int32_t* row_pos, int32_t* counts_out,

@@ -339,10 +339,11 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
  *   a bucket (nothing is kept), MOE_ERR_HIP (capture or instantiation failed).
  * moe_ladder_run: replays, on `stream`, the graph of the smallest bucket b >= T (1 <= T <= the
  *   largest bucket, else MOE_ERR_SHAPE). Rows T..b-1 are computed as extra tokens from whatever x
- *   holds there (their outputs go to rows T..b-1 of y and of the optional outputs, and they count
- *   in expert_counts); rows below T are exactly what moe_layer_forward on the first T rows gives
- *   whenever both calls take the same kernel path. *bucket_out (if not NULL) receives b.
- *   Capturable (a graph launch).
+ *   holds there (their outputs go to rows T..b-1 of y and of the optional outputs); rows below T
+ *   are exactly what moe_layer_forward on the first T rows gives whenever both calls take the same
+ *   kernel path. expert_counts (if given) counts the first T rows only: when b > T a small kernel
+ *   recounts it from their ids after the replay. *bucket_out (if not NULL) receives b.
+ *   Capturable (a graph launch, and that kernel).
  * moe_ladder_destroy: releases the ladder (NULL is a no-op); the caller's stream work using it must
  *   have completed.
  */

@@ -1,6 +1,7 @@
 """Graph ladder (moe_ladder_*): one captured graph of the layer per batch-size bucket. The rows
 below T of a replayed bucket equal moe_layer_forward on the first T rows bit for bit when both take
-the same kernel path, the layer output matches the oracle, and buckets replay in any order."""
+the same kernel path, the expert counts cover those T rows only (not the bucket's padding rows),
+the layer output matches the oracle, and buckets replay in any order."""
 import numpy as np
 import pytest
 
@@ -16,20 +17,24 @@ def _direct(dv, inp, T):
     import torch
     from expert_routing_grouped_moe_amd import moe
     ids = torch.empty((T, inp.k), dtype=torch.int32, device=DEV)
+    counts = torch.empty((inp.E,), dtype=torch.int32, device=DEV)
     y = moe.moe_layer_forward(dv["x"][:T], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"],
                               inp.k, inp.scoring, router_bias=dv["router_bias"],
-                              sel_bias=dv["sel_bias"], topk_ids=ids)
+                              sel_bias=dv["sel_bias"], topk_ids=ids, expert_counts=counts)
     torch.cuda.synchronize()
-    return y.cpu().numpy(), ids.cpu().numpy()
+    return y.cpu().numpy(), ids.cpu().numpy(), counts.cpu().numpy()
 
 
-def _ladder(dv, inp, buckets, stream):
+def _ladder(dv, inp, buckets, stream, with_ids=True):
     import torch
     from expert_routing_grouped_moe_amd import moe
-    ids = torch.empty((inp.T, inp.k), dtype=torch.int32, device=DEV)
+    ids = torch.empty((inp.T, inp.k), dtype=torch.int32, device=DEV) if with_ids else None
+    counts = torch.full((inp.E,), -1, dtype=torch.int32, device=DEV)
     lad = moe.MoeGraphLadder(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"],
                              inp.k, inp.scoring, buckets, router_bias=dv["router_bias"],
-                             sel_bias=dv["sel_bias"], topk_ids=ids, stream=stream)
+                             sel_bias=dv["sel_bias"], topk_ids=ids, expert_counts=counts,
+                             stream=stream)
+    lad.counts = counts
     return lad, ids
 
 
@@ -67,9 +72,34 @@ def test_ladder_rows_equal_direct_calls(case):
             assert used == min(b for b in buckets if b >= T)
             y_l = lad.y[:T].cpu().numpy()
             ids_l = ids[:T].cpu().numpy()
-            y_d, ids_d = _direct(dv, inp, T)
+            counts_l = lad.counts.cpu().numpy()
+            y_d, ids_d, counts_d = _direct(dv, inp, T)
             np.testing.assert_array_equal(ids_l, ids_d)
             np.testing.assert_array_equal(y_l, y_d)
+            # the first T rows only, also when the bucket is larger
+            np.testing.assert_array_equal(counts_l, np.bincount(ids_d.ravel(), minlength=inp.E))
+            np.testing.assert_array_equal(counts_l, counts_d)
+    finally:
+        lad.close()
+
+
+@pytest.mark.parametrize("name", ["zonos3mini-decode-cfg", "zonos2-decode"])
+def test_ladder_counts_without_topk_ids(name):
+    """With no topk_ids buffer the ids live in the workspace, at an offset that depends on the
+    bucket; the recount after a padded replay must find them there."""
+    import torch
+    inp = gen.make_inputs(name)
+    dv = upload(inp)
+    stream = torch.cuda.Stream()
+    lad, _ = _ladder(dv, inp, [8, 16, 64], stream, with_ids=False)
+    try:
+        for T in (5, 64, 11, 16, 1):
+            with torch.cuda.stream(stream):
+                lad.run(T, stream)
+            stream.synchronize()
+            _, ids_d, counts_d = _direct(dv, inp, T)
+            np.testing.assert_array_equal(lad.counts.cpu().numpy(), counts_d)
+            assert int(counts_d.sum()) == T * inp.k
     finally:
         lad.close()
 
