@@ -116,18 +116,6 @@ __device__ __forceinline__ void wait_steps_behind(int behind) {
   }
 }
 
-// 16 bytes per lane from `g` into LDS at byte address lds + 16 * lane (lds wave-uniform). Issued
-// as inline asm so that the compiler's own wait-count tracking (which would otherwise wait for
-// every outstanding DMA before any LDS read) leaves the pipeline alone; the waits are explicit.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

@@ -17,9 +17,9 @@
 // winner, the softmax maximum and the softmax sum are reduced across the row with DPP row
 // rotations (8, 4, 2, 1), after which every lane of the row holds the same value. The bf16
 // routing kernel first computes the 16 x E logit tile on the matrix cores with 8 waves that split
-// the experts (16 per MFMA tile) and, when there are few experts, the d-long reduction, so that
-// each wave issues all of its loads at once; partial tiles are added in a fixed order, so the
-// logits are the same on every call.
+// the experts (16 per MFMA tile) and, when there are few experts, the d-long reduction; each wave
+// copies its operands into LDS in 128-k chunks of whole 128-byte lines (router_product_128) and
+// partial tiles are added in a fixed order, so the logits are the same on every call.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,7 +33,6 @@ constexpr int kTailThreads = kTokTile * kQ; // 256
 // waves of the fused routing kernel: 16 measured the same at T = 64 and 4096, 15 % slower at 8192
 constexpr int kFusedWaves = 8;
 constexpr int kFusedThreads = kFusedWaves * kWave;
-constexpr int kBatch = 8;                   // MFMA steps whose loads are issued together
 static_assert(kFusedThreads >= kMaxE, "one thread per expert for the bias preload");
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
@@ -97,6 +96,46 @@ __device__ __forceinline__ float row_sum(float v) {
   v = v + row_ror<4>(v);
   v = v + row_ror<2>(v);
   return v + row_ror<1>(v);
+}
+
+// ------------------------------------------------------------- router product, 16 x 16 tiles
+// acc += A[16 rows, k0 .. k0 + 128) . B[16 rows, same k]^T as four 32-k MFMA steps in k order,
+// with the same fragments as loading each lane's operands (row l % 16, k 32 s + 8 (l / 16) of step
+// s) straight from global memory; k at or past kend contributes zeros (kend - k0 is a multiple
+// of 8). Loaded that way, each load instruction reads 16 rows x 64 bytes, half lines, which on
+// this chip copy at about half the rate of whole 128-byte lines (the routing kernels' product
+// phase took twice as long). Here the operands are copied into a wave-private LDS area (4 KB per
+// operand) with global_load_lds_dwordx4, each instruction 4 rows x 256 bytes, piece p of row r
+// stored at p ^ r so that the 16-row fragment reads are conflict-free, and read back as fragments.
+// rows[i]: the row this lane copies in instruction i (row 4 i + l / 16 of the tile), any valid
+// address for rows that are not used.
+constexpr int kProdScratch = 2 * 16 * 128;   // bf16 elements of LDS per wave (8 KB)
+
+__device__ __forceinline__ f32x4 router_product_128(const uint16_t* const (&arow)[4],
+                                                    const uint16_t* const (&brow)[4], int k0,
+                                                    int kend, uint16_t* scratch, f32x4 acc) {
+  const int lane = lane_id();
+  const uint32_t la = lds_addr(scratch), lb = la + 16 * 128 * 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int p = (lane & 15) ^ r;          // the logical piece that lands in this lane's slot
+    const int kk = min(k0 + 8 * p, kend - 8);
+    dma16(arow[i] + kk, la + 1024u * i);
+    dma16(brow[i] + kk, lb + 1024u * i);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int fr = lane & 15;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int p = 4 * m + (lane >> 4);
+    u32x4 af = *reinterpret_cast<const u32x4*>(scratch + fr * 128 + ((p ^ fr) * 8));
+    const u32x4 bf = *reinterpret_cast<const u32x4*>(scratch + 16 * 128 + fr * 128 + ((p ^ fr) * 8));
+    if (k0 + 8 * p >= kend) af = u32x4{0u, 0u, 0u, 0u};
+    acc = mfma16x16x32(af, bf, acc);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // fragments read before the next copy
+  return acc;
 }
 
 // Selection + weights for the token whose logits are `row` (LDS). All kQ lanes of the token's
@@ -272,11 +311,16 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int r16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
-  const int t = t0 + r16;
-  const bool tok_ok = t < T;
-  const uint16_t* xrow = x + static_cast<long long>(min(t, T - 1)) * d;
   const int kslice = d / ksplit;  // a multiple of 8 (d % 64 == 0, ksplit <= 8)
+  // per-wave product scratch after the tables, 16-byte aligned
+  uint16_t* scratch =
+      reinterpret_cast<uint16_t*>((reinterpret_cast<uintptr_t>(hist + E) + 15) & ~uintptr_t{15}) +
+      wave * kProdScratch;
+  // the token rows this lane copies (rows past T copy row T - 1; their logits are not used)
+  const uint16_t* xr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    xr[i] = x + static_cast<long long>(min(t0 + 4 * i + (lane >> 4), T - 1)) * d;
 
   // the per-expert vectors are loaded now and stored to LDS after the products, so their latency
   // hides behind the tile loads
@@ -289,23 +333,15 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_bf16_kernel(
     const int ks = task / neb;
     const int kbeg = ks * kslice;
     const int kend = kbeg + kslice;
-    const int e = eb * 16 + r16;
-    const bool e_ok = e < E;
-    const uint16_t* wrow = wr + static_cast<long long>(min(e, E - 1)) * d;
+    const uint16_t* wrw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wrw[i] = wr + static_cast<long long>(min(eb * 16 + 4 * i + (lane >> 4), E - 1)) * d;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kbeg; k0 < kend; k0 += 32 * kBatch) {
-      u32x4 a[kBatch], b[kBatch];
-#pragma unroll
-      for (int s = 0; s < kBatch; ++s) {
-        const int kk = k0 + 32 * s + kq;  // kend - kk is a multiple of 8: kk < kend -> 8 in range
-        const bool ok = kk < kend;
-        a[s] = (ok && tok_ok) ? load16(xrow + kk) : u32x4{0u, 0u, 0u, 0u};
-        b[s] = (ok && e_ok) ? load16(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int s = 0; s < kBatch; ++s) acc = mfma16x16x32(a[s], b[s], acc);
-    }
-    if (e_ok) {
+    for (int k0 = kbeg; k0 < kend; k0 += 128)
+      acc = router_product_128(xr, wrw, k0, kend, scratch, acc);
+    const int e = eb * 16 + r16;
+    if (e < E) {
       float* dst = part + ks * kTokTile * ld;
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[((lane >> 4) * 4 + r) * ld + e] = acc[r];
@@ -347,25 +383,21 @@ __global__ __launch_bounds__(kWave) void logit_partial_kernel(
     int slice, float* __restrict__ part) {
   const int t0 = blockIdx.x * kTokTile, e0 = blockIdx.y * 16, ks = blockIdx.z;
   const int kbeg = ks * slice, kend = min(d, kbeg + slice);
+  __shared__ __attribute__((aligned(16))) uint16_t scratch[kProdScratch];
   const int lane = lane_id();
   const int r16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
   // rows past T or E read a valid row; their products are never stored
-  const uint16_t* xrow = x + static_cast<long long>(min(t0 + r16, T - 1)) * d;
-  const uint16_t* wrow = wr + static_cast<long long>(min(e0 + r16, E - 1)) * d;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = kbeg; k0 < kend; k0 += 32 * kBatch) {
-    u32x4 a[kBatch], b[kBatch];
+  const uint16_t* xr[4];
+  const uint16_t* wrw[4];
 #pragma unroll
-    for (int st = 0; st < kBatch; ++st) {
-      const int kk = k0 + 32 * st + kq;  // kend - kk is a multiple of 8: kk < kend -> 8 in range
-      const bool ok = kk < kend;
-      a[st] = ok ? load16(xrow + kk) : u32x4{0u, 0u, 0u, 0u};
-      b[st] = ok ? load16(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int st = 0; st < kBatch; ++st) acc = mfma16x16x32(a[st], b[st], acc);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    xr[i] = x + static_cast<long long>(min(t0 + r, T - 1)) * d;
+    wrw[i] = wr + static_cast<long long>(min(e0 + r, E - 1)) * d;
   }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kbeg; k0 < kend; k0 += 128)
+    acc = router_product_128(xr, wrw, k0, kend, scratch, acc);
   const int e = e0 + r16;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -463,7 +495,7 @@ size_t tail_smem(int E) {
 
 size_t fused_smem(int E, int d) {
   return sizeof(float) * (static_cast<size_t>(route_ksplit(E, d)) * kTokTile * (E + 1) + 2 * E) +
-         sizeof(int) * E;
+         sizeof(int) * E + 16 + sizeof(uint16_t) * kFusedWaves * kProdScratch;
 }
 
 }  // namespace
