@@ -65,10 +65,6 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return out;
 }
 
-// D = A(16x32) * B(32x16) + C on the CDNA4 matrix cores, fp32 accumulate.
-// Lane l supplies row (l % 16) of A and column (l % 16) of B, eight consecutive k each
-// (k = 8 * (l / 16) + 0..7); it receives C rows 4 * (l / 16) + 0..3 of column (l % 16).
-// Any fixed lane->k assignment used identically for A and B gives the same sum over k.
 // 16 bytes per lane from `g` into LDS at byte address lds + 16 * lane (lds wave-uniform). Issued
 // as inline asm so that the compiler's own wait-count tracking (which would otherwise wait for
 // every outstanding DMA before any LDS read) leaves the pipeline alone; the waits are explicit.
@@ -81,6 +77,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// D = A(16x32) * B(32x16) + C on the CDNA4 matrix cores, fp32 accumulate.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, eight consecutive k each
+// (k = 8 * (l / 16) + 0..7); it receives C rows 4 * (l / 16) + 0..3 of column (l % 16).
+// Any fixed lane->k assignment used identically for A and B gives the same sum over k.
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
