@@ -252,6 +252,63 @@ def gemm_kernel_name(rows, E, gateup):
             else "gemm_dma_kernel<false, 128, 256, 3, 64, 32>")
 
 
+def ep_shard_timing(gpus=8, calls=48):
+    """One GPU's share of expert parallelism at its real shape, on this one GPU: the skewed
+    prefill's 16 experts split over `gpus` GPUs, the share that owns experts 0..16/gpus - 1 (expert
+    0 takes ~40 % of the tokens: the busiest shard). The routing comes from the library
+    (moe_router_logits + moe_route on the whole batch), the shard's token rows are gathered on the
+    host side of the boundary, grouped with moe_permute and run through moe_expert_ffn with cold
+    weights (rotating copies past the Infinity Cache); back-to-back calls, mean per call. The
+    all-to-all exchange around it is not run (one GPU); its bytes are reported."""
+    import numpy as np
+    import torch
+    from expert_routing_grouped_moe_amd import inputs as gen
+    from expert_routing_grouped_moe_amd import moe
+
+    dev = "cuda:0"
+    inp = gen.make_inputs(HEADLINE)
+    T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
+    if gpus < 2 or E % gpus:
+        return {"gpus": gpus, "error": f"{E} experts do not split evenly over {gpus} GPUs"}
+    per = E // gpus
+    bf = lambda key: torch.from_numpy(inp.bits[key].view(np.int16)).view(torch.bfloat16).to(dev)
+    x = bf("x")
+    rb = torch.from_numpy(inp.router_bias).to(dev)
+    logits = moe.moe_router_logits(x, bf("w_router"), router_bias=rb)
+    ids, _, _ = moe.moe_route(logits, k, inp.scoring)
+    ids_h = ids.cpu().numpy()
+    tokens = np.nonzero((ids_h[:, 0] >= 0) & (ids_h[:, 0] < per))[0]
+    x_sh = x[torch.from_numpy(tokens).to(dev)].contiguous()
+    local = ids[torch.from_numpy(tokens).to(dev)].contiguous()
+    counts = torch.bincount(local.view(-1).long(), minlength=per).to(torch.int32)
+    offsets, rows, _ = moe.moe_permute(local, counts, per)
+    base = {key: bf(key)[:per].contiguous() for key in ("w_gate", "w_up", "w_down")}
+    wbytes = sum(t.numel() * t.element_size() for t in base.values())
+    ncopies = max(2, math.ceil(1.6e9 / wbytes))
+    copies = [base] + [{key: t.clone() for key, t in base.items()} for _ in range(ncopies - 1)]
+    n = len(tokens)
+    out = torch.empty((n, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, moe.moe_workspace_size(n, d, per, H, k, moe.MOE_BF16)),
+                     dtype=torch.uint8, device=dev)
+    call = lambda c: moe.moe_expert_ffn(x_sh, c["w_gate"], c["w_up"], c["w_down"], k, offsets,
+                                        rows, expert_out=out, workspace=ws)
+    for c in copies:
+        call(c)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(calls):
+        call(copies[i % ncopies])
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / calls * 1e6
+    flops = 6.0 * d * H * n
+    return {"gpus": gpus, "experts": list(range(per)), "rows": counts.cpu().tolist(),
+            "us_per_call": us, "tflops": flops / us / 1e6,
+            "mfma_frac": flops / us / 1e6 / BF16_PEAK_TFLOPS,
+            "exchange_bytes": {"x_rows_in_bf16": n * d * 2, "outputs_back_fp32": n * d * 4},
+            "note": "moe_expert_ffn on one GPU's expert share, cold weights; the all-to-alls "
+                    "around it are not run (one GPU)"}
+
+
 def run_workload(name, steps, warmup, weights="native", warm=False, eager=False, ladder=0,
                  cpu_budget=0.0, event_steps=200):
     """Times `steps` layer steps of workload `name` (after `warmup` untimed ones) and returns its
@@ -474,6 +531,9 @@ def main():
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB ten times (counter calibration)")
+    ap.add_argument("--ep-shard", type=int, default=8, metavar="GPUS",
+                    help="also time moe_expert_ffn on the busiest expert shard of the skewed "
+                         "prefill split over GPUS GPUs (one GPU's share; 0 = skip)")
     ap.add_argument("--ladder", type=int, default=0, metavar="STEPS",
                     help="also time STEPS decode steps of seeded random batch widths 1..T, launched "
                          "directly and replayed from a graph ladder (buckets 1, 2, 4, ..., T)")
@@ -540,6 +600,10 @@ def main():
         result["ladder"] = head["ladder"]
     if "cpu_baseline" in head:
         result["cpu_baseline"] = head["cpu_baseline"]
+    if not args.only and args.ep_shard > 1 and args.weights == "native":
+        result["ep_shard"] = ep_shard_timing(args.ep_shard)
+        print(f"[bench] ep shard of {args.ep_shard}: {result['ep_shard']['us_per_call']:.1f} us/call",
+              file=sys.stderr, flush=True)
     if others:
         table = {args.workload: {key: v for key, v in head.items() if key != "cpu_baseline"}}
         table.update(others)
