@@ -35,6 +35,36 @@ def test_router_logits_within_bound(name):
     assert np.abs(L - ref).max() < 1e-3
 
 
+# router products over shapes that exercise the copy of whole 128-byte line chunks: reduction
+# slices that end inside a 128-wide chunk (d = 192, 320, 1088, 2112), many or few experts, ragged T;
+# "fused" through moe_router_logits (the routing kernel's own product), "split" through the layer's
+# small-batch router (partial tiles over d slices, then selection) with the logits written out
+ROUTER_SHAPES = [("fused", 1, 64, 1), ("fused", 17, 192, 5), ("fused", 300, 1088, 64),
+                 ("fused", 33, 2112, 16), ("fused", 45, 320, 256), ("fused", 100, 1024, 100),
+                 ("split", 64, 1088, 64), ("split", 29, 320, 256), ("split", 200, 2112, 100)]
+
+
+@pytest.mark.parametrize("path,T,d,E", ROUTER_SHAPES)
+def test_router_product_shapes(path, T, d, E):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs_custom(T, d, E, 1, 64, orc.SOFTMAX, "bf16", seed=T + d + E)
+    dev = upload(inp)
+    if path == "fused":
+        L = moe.moe_router_logits(dev["x"], dev["w_router"])
+    else:
+        assert T <= 256 and E * d >= 65536          # the layer takes the split router here
+        L = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        moe.moe_layer_forward(dev["x"], dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                              1, inp.scoring, logits=L)
+    torch.cuda.synchronize()
+    L = L.cpu().numpy().astype(np.float64)
+    ref = orc.router_logits_ref(inp.x, inp.w_router)
+    B = orc.logit_error_bound(inp.x, inp.w_router)
+    assert (np.abs(L - ref) <= B[:, None]).all()
+    assert np.abs(L - ref).max() < 1e-3
+
+
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (64, 8, 1), (64, 64, 2), (1000, 16, 1), (8192, 16, 1),
                                    (6000, 16, 2), (20000, 8, 1),
                                    (4096, 64, 2), (333, 256, 8), (3000, 5, 3)])
