@@ -337,6 +337,23 @@ __device__ int scan_rows(const int32_t* __restrict__ ids, int n, int e, int* lr)
   return total;
 }
 
+// The same from ids already in registers (id[i] = ids[lane + 64 i], -1 past n; n <= 64 R).
+template <int R>
+__device__ int scan_rows_regs(const int (&id)[R], int e, int* lr) {
+  const int lane = lane_id();
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const bool m = id[i] == e;
+    const unsigned long long mask = __ballot(m);
+    if (m) lr[total + __popcll(mask & lt)] = kWave * i + lane;
+    total += __popcll(mask);
+  }
+  __syncthreads();
+  return total;
+}
+
 // 8 int8 codes (two dwords, lowest k first) as 8 bf16 values (exact: |code| <= 127 needs 7
 // significand bits): sign-extend, convert to fp32, keep the upper halves.
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t v, int sh) {
@@ -572,12 +589,27 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
   const int lane = lane_id();
   const int E = gridDim.y;
   int e = blockIdx.y, slab = blockIdx.x;
+  // with few ids the count pass keeps them in registers and the row scan reuses them (one read
+  // of the ids per block instead of two)
+  constexpr int kRegIds = 4;
+  int idr[kRegIds];
+  const bool ids_in_regs = E >= kStCompactMinE && rs.ids && rs.n_rows <= kRegIds * kWave;
   if (E >= kStCompactMinE) {
     const int slabs = gridDim.x;
     const int item = blockIdx.y * slabs + blockIdx.x;
     // rows per expert: from the ids (one LDS add per id) or from the dispatch offsets
     for (int i = lane; i < E; i += kWave) cnt[i] = rs.ids ? 0 : rs.offsets[i + 1] - rs.offsets[i];
-    if (rs.ids) {
+    if (ids_in_regs) {
+#pragma unroll
+      for (int i = 0; i < kRegIds; ++i) {
+        const int r = kWave * i + lane;
+        idr[i] = r < rs.n_rows ? rs.ids[r] : -1;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < kRegIds; ++i)
+        if (kWave * i + lane < rs.n_rows) atomicAdd(&cnt[min(max(idr[i], 0), E - 1)], 1);
+    } else if (rs.ids) {
       __builtin_amdgcn_wave_barrier();
       for (int r = lane; r < rs.n_rows; r += kWave)
         atomicAdd(&cnt[min(max(rs.ids[r], 0), E - 1)], 1);
@@ -603,7 +635,7 @@ __global__ __launch_bounds__(kWave) void ffn_stream_kernel(
   }
   int count, hbase;
   if (rs.ids) {
-    count = scan_rows(rs.ids, rs.n_rows, e, lr);
+    count = ids_in_regs ? scan_rows_regs(idr, e, lr) : scan_rows(rs.ids, rs.n_rows, e, lr);
     hbase = -1;
     if (E < kStCompactMinE && rs.counts_out && blockIdx.x == 0 && lane == 0)
       rs.counts_out[e] = count;
