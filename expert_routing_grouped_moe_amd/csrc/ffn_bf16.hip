@@ -531,7 +531,8 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   load(1, 1);
   // unrolled completely when NB is known: in straight-line code the compiler's wait counts leave
   // the next block in flight, while a loop back edge makes it wait for every outstanding load
-#pragma unroll (NB > 0 ? NB / 2 : 1)
+  constexpr int kUnroll = NB > 0 ? NB / 2 : 1;
+#pragma unroll kUnroll
   for (int sq = 0; sq < nb; sq += 2) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
