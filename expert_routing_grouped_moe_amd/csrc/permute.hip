@@ -14,7 +14,9 @@
 //  pass 2  thread i owns a contiguous run of rows (runs in thread order = rows in ascending
 //          order); a block-wide exclusive scan of the per-thread match counts places each of the
 //          block's rows, which it writes to sorted_rows and row_pos.
-// Rows are read 8 per thread per round with all 8 loads issued before use.
+// Rows are read 8 per thread per round with all 8 loads issued before use. With T*k <= 8192 one
+// round does both passes, each thread owning two runs of four rows (one in each half of the ids)
+// read with whole-line 16-byte loads.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,19 +44,36 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
   const int wave = tid / kWave;
 
   if (n <= kRound) {
-    // one round: the ids are read once, and one barrier serves both the counts and the scan
+    // one round: the ids are read once, and one barrier serves both the counts and the scan.
+    // Thread t owns two runs of four rows, 4 t .. 4 t + 3 and kRound / 2 + 4 t .. + 3, so that
+    // each wave's 16-byte loads cover whole lines (eight rows per thread in one run would leave
+    // every load instruction with half of each line, and took about twice as long); the counts
+    // of the two runs are scanned together, packed in one integer (each below 2^16).
+    constexpr int kHalf = kRound / 2;
     int v[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int r = tid * kPer + i;
-      v[i] = r < n ? clamp_id(ids[r], E) : E;
-    }
-    int less = 0, mine = 0;
+    for (int h = 0; h < 2; ++h) {
+      const int r0 = h * kHalf + 4 * tid;
+      if (r0 + 3 < n) {
+        const int4 q = *reinterpret_cast<const int4*>(ids + r0);
+        v[4 * h + 0] = clamp_id(q.x, E);
+        v[4 * h + 1] = clamp_id(q.y, E);
+        v[4 * h + 2] = clamp_id(q.z, E);
+        v[4 * h + 3] = clamp_id(q.w, E);
+      } else {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      less += v[i] < e;
-      mine += v[i] == e;
+        for (int i = 0; i < 4; ++i) v[4 * h + i] = r0 + i < n ? clamp_id(ids[r0 + i], E) : E;
+      }
     }
+    int less = 0, mine0 = 0, mine1 = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) less += v[i] < e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mine0 += v[i] == e;
+      mine1 += v[4 + i] == e;
+    }
+    const int mine = mine0 | (mine1 << 16);
     int incl = mine;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -73,19 +92,31 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
       if (w < wave) before += t;
       total += t;
     }
+    const int total0 = total & 0xffff, total1 = total >> 16;
     if (tid == 0) {
       offsets[e] = base;
-      if (counts_out) counts_out[e] = total;
+      if (counts_out) counts_out[e] = total0 + total1;
       if (e == E - 1) offsets[E] = n;
     }
-    int p = base + before + incl - mine;
+    const int excl = before + incl - mine;    // packed: earlier rows of run 0 | of run 1 << 16
+    int p0 = base + (excl & 0xffff);
+    int p1 = base + total0 + (excl >> 16);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < 4; ++i) {
       if (v[i] == e) {
-        const int r = tid * kPer + i;
-        sorted_rows[p] = r;
-        row_pos[r] = p;
-        ++p;
+        const int r = 4 * tid + i;
+        sorted_rows[p0] = r;
+        row_pos[r] = p0;
+        ++p0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (v[4 + i] == e) {
+        const int r = kHalf + 4 * tid + i;
+        sorted_rows[p1] = r;
+        row_pos[r] = p1;
+        ++p1;
       }
     }
     return;
