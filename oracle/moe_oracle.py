@@ -199,6 +199,24 @@ def pack_q4_ref(q):
     return dw.astype("<u4").view(np.uint8).reshape(q.shape[:-1] + (K // 2,))
 
 
+def pack_frag_ref(w):
+    """The library's fragment-major storage of a bf16 weight matrix [..., R, K] (R a multiple of
+    16, K of 32), for the decode kernels: the 16 x 32 block of rows 16 b .. 16 b + 15 and reduction
+    indices 32 s .. 32 s + 31 is stored as 512 consecutive values at (b * K / 32 + s) * 512, value
+    (r, k) of it at 128 ((k mod 32) div 8) + 8 (r mod 16) + (k mod 8), i.e. the 16 bytes that lane
+    (r mod 16) + 16 ((k mod 32) div 8) of a 16 x 16 x 32 MFMA takes as its operand, lanes in
+    order. A pure reordering: the values are unchanged. Returns the same shape, reordered."""
+    w = np.asarray(w)
+    R, K = w.shape[-2], w.shape[-1]
+    assert R % 16 == 0 and K % 32 == 0
+    lead = w.shape[:-2]
+    # [..., b, r16, s, q, i] -> [..., b, s, q, r16, i]
+    v = w.reshape(lead + (R // 16, 16, K // 32, 4, 8))
+    n = len(lead)
+    v = v.transpose(tuple(range(n)) + (n, n + 2, n + 3, n + 1, n + 4))
+    return np.ascontiguousarray(v).reshape(w.shape)
+
+
 def pack_q4_params_ref(s, b):
     """Per-group (scale, bias) as one uint32: bf16 bits of s in the low half, of b in the high."""
     sb = np.asarray(s, dtype=np.float32).view(np.uint32) >> np.uint32(16)

@@ -333,6 +333,36 @@ def test_q4_quantisation_invariants():
     np.testing.assert_array_equal(q2, qi)
 
 
+def test_frag_layout_feeds_the_matrix_core_product():
+    """The fragment-major order read as the CDNA4 16x16x32 MFMA reads its A operand: lane l of
+    fragment (b, s) supplies eight consecutive k of row l mod 16, k = 32 s + 8 (l div 16) + i
+    (matrix-core ISA, operand layout of V_MFMA_F32_16X16X32_BF16). Summing those lane products
+    per row must give the plain matrix-vector product W X, and every value must move once."""
+    rng = np.random.default_rng(29)
+    for lead, R, K in (((), 16, 32), ((3,), 48, 96), ((2,), 32, 256)):
+        W = rng.standard_normal(lead + (R, K))
+        X = rng.standard_normal((K, 5))
+        P = orc.pack_frag_ref(W)
+        assert P.shape == W.shape
+        np.testing.assert_array_equal(np.sort(P.ravel()), np.sort(W.ravel()))
+        flat = P.reshape(lead + (R * K,))
+        Y = np.zeros(lead + (R, 5))
+        for b in range(R // 16):
+            for s in range(K // 32):
+                frag = flat[..., (b * (K // 32) + s) * 512:(b * (K // 32) + s + 1) * 512]
+                for lane in range(64):
+                    vals = frag[..., 8 * lane:8 * lane + 8]           # this lane's 16 bytes
+                    ks = 32 * s + 8 * (lane // 16) + np.arange(8)
+                    Y[..., 16 * b + lane % 16, :] += vals @ X[ks]
+        np.testing.assert_allclose(Y, W @ X, rtol=1e-12, atol=1e-12)
+    # hand case: rows 0..15 of a 16 x 32 block with value 100 r + k; lane 17 (row 1, k 8..15)
+    W = (100 * np.arange(16)[:, None] + np.arange(32)[None, :]).astype(np.float64)
+    P = orc.pack_frag_ref(W).ravel()
+    np.testing.assert_array_equal(P[:8], np.arange(8))
+    np.testing.assert_array_equal(P[8 * 17:8 * 18], 108 + np.arange(8))
+    np.testing.assert_array_equal(P[8 * 63:], 1524 + np.arange(8))
+
+
 def test_q4_layer_on_exact_weights_equals_plain_layer():
     # weights that are exactly s * q + b: the 4-bit layer is the plain layer on the same weights
     inp = _case(T=16, d=128, E=4, k=2, H=128, scoring=orc.SOFTMAX, seed=15)
@@ -551,6 +581,7 @@ def _pins_pass():
         test_hand_q4_packing(hand)
         test_hand_fp32_rank_add(hand)
         test_hand_q4_param_words(hand)
+        test_frag_layout_feeds_the_matrix_core_product()
         test_hand_expert_counts()
         test_selection_admissible_rules()
         test_hand_swiglu_layer(hand, "swiglu_one_expert")
@@ -632,6 +663,9 @@ MUTATIONS = {
     # packed nibbles of odd and even k swapped
     "q4_pack_swap": ("pack_q4_ref", lambda orig: (lambda q: (lambda p: ((p & 15) << 4 | (p >> 4)).astype(np.uint8))(
         orig(q)))),
+    # fragment-major blocks with the row and k-quarter orders swapped inside each fragment
+    "frag_lane_order": ("pack_frag_ref", lambda orig: (lambda w: (lambda p: np.ascontiguousarray(
+        p.reshape(p.shape[:-2] + (-1, 4, 16, 8)).swapaxes(-3, -2)).reshape(p.shape))(orig(w)))),
     # (scale, bias) halves of the 4-bit parameter word swapped
     "q4_params_swap": ("pack_q4_params_ref", lambda orig: (lambda s, b: orig(b, s))),
     # expert counts shifted by one index (the total stays right)
