@@ -250,6 +250,18 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
                                                    static_cast<hipStream_t>(stream)));
 }
 
+int moe_pack_weights_frag(const void* w, int64_t rows, int K, void* out, void* stream) {
+  if (rows < 0 || rows % 16 != 0 || K < 32 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (rows * K >= kMaxQuantElems) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!w || !out) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(out)) return MOE_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(moe::launch_pack_frag(static_cast<const uint16_t*>(w), rows, K,
+                                          static_cast<uint16_t*>(out),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int moe_combine(const float* expert_out, const int32_t* row_pos, const float* topk_w, int T,
                 int d, int k, void* y, int y_dtype, void* stream) {
   if (T < 0 || T > kMaxTokens || d <= 0 || d % 4 != 0 || k < 1 || k > moe::kMaxK)
@@ -278,7 +290,10 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   const bool abi2 = a->struct_size >= MOE_LAYER_ARGS_V2_SIZE;
   const int w_dtype = (abi2 && a->w_dtype != 0) ? a->w_dtype : dtype;
   moe::QuantWeights qw{};
-  if (w_dtype != dtype) {
+  if (w_dtype == MOE_BF16_FRAG) {
+    if (dtype != MOE_BF16 || !moe::ffn_bf16_streaming(T, d, E, H, k)) return MOE_ERR_UNSUPPORTED;
+    qw = moe::QuantWeights{moe::kWFrag, nullptr, nullptr, nullptr};
+  } else if (w_dtype != dtype) {
     if ((w_dtype != MOE_I8 && w_dtype != MOE_Q4) || dtype != MOE_BF16 ||
         !moe::ffn_bf16_streaming(T, d, E, H, k))
       return MOE_ERR_UNSUPPORTED;

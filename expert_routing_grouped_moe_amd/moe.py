@@ -15,7 +15,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
-MOE_ABI_VERSION = 4  # include/moe.h; the library must report the same value
+MOE_ABI_VERSION = 5  # include/moe.h; the library must report the same value
 
 MOE_OK = 0
 MOE_ERR_NULL = -1
@@ -28,6 +28,7 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_I8 = 2
 MOE_Q4 = 3
+MOE_BF16_FRAG = 4
 
 MOE_SCORING_SOFTMAX = 0
 MOE_SCORING_SELECTED_SOFTMAX = 1
@@ -39,7 +40,7 @@ SCORING = {"softmax": MOE_SCORING_SOFTMAX, "selected_softmax": MOE_SCORING_SELEC
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router_logits",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_quantize_rows_i8", "moe_quantize_groups_q4", "moe_ladder_create", "moe_ladder_run",
-           "moe_ladder_destroy", "moe_layer_forward_noalloc")
+           "moe_ladder_destroy", "moe_layer_forward_noalloc", "moe_pack_weights_frag")
 
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -108,6 +109,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_groups_q4.restype = c_int
     lib.moe_quantize_groups_q4.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
                                            c_void_p, c_void_p]
+    lib.moe_pack_weights_frag.restype = c_int
+    lib.moe_pack_weights_frag.argtypes = [c_void_p, ctypes.c_int64, c_int, c_void_p, c_void_p]
     lib.moe_ladder_create.restype = c_int
     lib.moe_ladder_create.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_int, c_void_p, c_size_t,
                                       c_void_p, POINTER(c_void_p)]
@@ -285,13 +288,18 @@ def moe_combine(expert_out, row_pos, topk_w, y=None, stream=None, y_dtype=torch.
 
 def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias=None,
                     sel_bias=None, logits=None, topk_ids=None, topk_w=None, expert_counts=None,
-                    w_scales=None):
+                    w_scales=None, w_format="plain"):
     """Quantised expert weights: int8 codes (moe_quantize_rows_i8) with ``w_scales`` = their
     (gate, up, down) fp32 row scales, or uint8 packed 4-bit codes (moe_quantize_groups_q4) with
-    ``w_scales`` = their int32 (scale, bias) pair arrays."""
+    ``w_scales`` = their int32 (scale, bias) pair arrays. ``w_format="frag"``: bf16 expert stacks
+    reordered by moe_pack_weights_frag (same shapes and dtype as the plain stacks)."""
     T, d = x.shape
     E, H, _ = w_gate.shape
+    if w_format not in ("plain", "frag"):
+        raise ValueError(f"w_format must be 'plain' or 'frag', not {w_format!r}")
     wt = w_gate.dtype if w_gate.dtype in (torch.int8, torch.uint8) else x.dtype
+    if w_format == "frag" and (wt != torch.bfloat16 or x.dtype != torch.bfloat16):
+        raise ValueError("w_format='frag' needs bfloat16 activations and expert stacks")
     q4 = wt == torch.uint8
     _need(x, "x", (T, d))
     _need(w_router, "w_router", (E, d), x.dtype)
@@ -321,6 +329,8 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
     a.T, a.d, a.E, a.H, a.k = T, d, E, H, k
     a.dtype = _dtype_code(x)
     a.w_dtype = {torch.int8: MOE_I8, torch.uint8: MOE_Q4}.get(wt, a.dtype)
+    if w_format == "frag":
+        a.w_dtype = MOE_BF16_FRAG
     if wt in (torch.int8, torch.uint8):
         a.w_gate_scale, a.w_up_scale, a.w_down_scale = (t.data_ptr() for t in w_scales)
     a.scoring = _scoring_code(scoring)
@@ -336,17 +346,18 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
 def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
                       sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
                       expert_counts=None, workspace=None, stream=None, args=None, w_scales=None,
-                      y_dtype=torch.float32):
+                      y_dtype=torch.float32, w_format="plain"):
     """The fused layer. Returns y [T, d], float32 unless ``y`` (or ``y_dtype``) is bfloat16.
     Optional outputs are written when passed. With quantised expert weights
     (moe_quantize_rows_i8 or moe_quantize_groups_q4 codes) pass their scale arrays as
-    w_scales."""
+    w_scales; with fragment-major bf16 stacks (moe_pack_weights_frag) pass w_format="frag"."""
     T, d = x.shape
     E, H, _ = w_gate.shape
     y = _empty((T, d), y_dtype, x) if y is None else y
     if args is None:
         args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias,
-                               sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales)
+                               sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales,
+                               w_format)
     ws_bytes = moe_workspace_size(T, d, E, H, k, args.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
@@ -358,14 +369,15 @@ def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias
 def moe_layer_forward_noalloc(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias=None,
                               sel_bias=None, y=None, logits=None, topk_ids=None, topk_w=None,
                               expert_counts=None, stream=None, args=None, w_scales=None,
-                              y_dtype=torch.float32):
+                              y_dtype=torch.float32, w_format="plain"):
     """The fused layer on the library's fixed scratch array (no workspace argument, nothing
     allocated by the library; see moe_layer_forward_noalloc in include/moe.h). Returns y."""
     T, d = x.shape
     y = _empty((T, d), y_dtype, x) if y is None else y
     if args is None:
         args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bias,
-                               sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales)
+                               sel_bias, logits, topk_ids, topk_w, expert_counts, w_scales,
+                               w_format)
     _check(LIB.moe_layer_forward_noalloc(ctypes.byref(args), _stream(stream)),
            "moe_layer_forward_noalloc")
     return y
@@ -404,6 +416,21 @@ def moe_quantize_groups_q4(w, q=None, qpar=None, stream=None):
     return q, qpar
 
 
+def moe_pack_weights_frag(w, out=None, stream=None):
+    """Fragment-major copy of the bf16 weights w [..., R, K] (R % 16 == 0, K % 32 == 0) for the
+    decode path (w_format="frag"): same shape and dtype, values reordered (moe_pack_weights_frag
+    in include/moe.h)."""
+    if w.dtype != torch.bfloat16 or w.dim() < 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous bfloat16 tensor of at least two dimensions")
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    out = torch.empty_like(w) if out is None else out
+    _need(out, "out", tuple(w.shape), torch.bfloat16)
+    _check(LIB.moe_pack_weights_frag(_ptr(w), rows, K, _ptr(out), _stream(stream)),
+           "moe_pack_weights_frag")
+    return out
+
+
 class MoeGraphLadder:
     """moe_ladder_create / moe_ladder_run / moe_ladder_destroy over torch tensors: the layer is
     captured once per bucket of batch sizes on the buffers given here (every token-indexed tensor
@@ -413,13 +440,13 @@ class MoeGraphLadder:
 
     def __init__(self, x, w_router, w_gate, w_up, w_down, k, scoring, buckets, y=None,
                  router_bias=None, sel_bias=None, logits=None, topk_ids=None, topk_w=None,
-                 expert_counts=None, w_scales=None, stream=None):
+                 expert_counts=None, w_scales=None, stream=None, w_format="plain"):
         T, d = x.shape
         E, H, _ = w_gate.shape
         self.y = _empty((T, d), torch.float32, x) if y is None else y
         self.args = make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, self.y,
                                     router_bias, sel_bias, logits, topk_ids, topk_w,
-                                    expert_counts, w_scales)
+                                    expert_counts, w_scales, w_format)
         ws_bytes = moe_workspace_size(T, d, E, H, k, self.args.dtype)
         self.workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
         self._keep = (x, w_router, w_gate, w_up, w_down, router_bias, sel_bias, logits, topk_ids,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
   MOE_OK = 0,
@@ -77,7 +77,11 @@ enum moe_dtype {
   /* 4-bit affine expert weights, one bf16 (scale, bias) pair per group of 64 along the reduction
      index, codes in the packed order of moe_quantize_groups_q4. Only as moe_layer_args.w_dtype,
      with bf16 activations, on the decode path. Added in ABI 3. */
-  MOE_Q4 = 3
+  MOE_Q4 = 3,
+  /* bf16 expert weights in the fragment-major order of moe_pack_weights_frag (the same values,
+     reordered). Only as moe_layer_args.w_dtype, with bf16 activations, on the decode path.
+     Added in ABI 5. */
+  MOE_BF16_FRAG = 4
 };
 
 enum moe_scoring {
@@ -236,7 +240,11 @@ typedef struct moe_layer_args {
      INTERNALS, "Recommended: F16 spine + K-quant experts") need dtype = MOE_BF16 and the
      weight-streaming regime (T*k <= 2048, T*k <= 32*E, d and H multiples of 256): anything else
      returns MOE_ERR_UNSUPPORTED. Missing quantisation arrays: MOE_ERR_NULL. They must be 16-byte
-     aligned. */
+     aligned.
+     w_dtype = MOE_BF16_FRAG (ABI 5): w_gate, w_up and w_down hold the bf16 stacks reordered by
+     moe_pack_weights_frag (rows = E * H, K = d for gate and up; rows = E * d, K = H for down);
+     the quantisation arrays are not read. Same regime and dtype conditions as above; the result
+     equals the plain bf16 layer's bit for bit. */
   int32_t w_dtype;
   const void* w_gate_scale;   /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
   const void* w_up_scale;     /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
@@ -319,6 +327,22 @@ int moe_quantize_rows_i8(const void* w, int64_t rows, int K, int dtype, int8_t* 
  */
 int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_t* q,
                            uint32_t* qpar, void* stream);
+
+/*
+ * Fragment-major copy of a bf16 weight matrix for the decode path (MOE_BF16_FRAG). The runtime on
+ * the pages converts checkpoints once, offline, into its own storage (zonos2.cpp INTERNALS,
+ * "Converting to GGUF"); this order is the library's own. For a row-major [rows, K] bf16 matrix w
+ * (an expert stack is rows = E * N rows of length K), out holds the same rows * K values with
+ *   w[r, k] at  ((r / 16) * (K / 32) + k / 32) * 512 + ((k % 32) / 8) * 128 + (r % 16) * 8 + k % 8
+ * (integer division): every 16 x 32 block is 1 KiB, stored as the 64 sixteen-byte operands that
+ * lanes 0..63 of a 16 x 16 x 32 matrix-core step take (lane l: row l % 16, eight consecutive k from
+ * 8 (l / 16)), so a wave reads each step's weights as one contiguous kilobyte.
+ * w, out: device bf16 bits, 16-byte aligned, not overlapping. rows % 16 == 0, rows >= 0 (0 is a
+ * no-op), 32 <= K, K % 32 == 0, rows * K < 2^36; else MOE_ERR_SHAPE. NULL pointers (rows > 0):
+ * MOE_ERR_NULL. Exact (a reordering). Asynchronous on `stream`, capturable, allocates nothing.
+ * Added in ABI 5.
+ */
+int moe_pack_weights_frag(const void* w, int64_t rows, int K, void* out, void* stream);
 
 /*
  * Graph ladder (serving-side decode). zonos2.cpp INTERNALS, "Performance": the decode graph is

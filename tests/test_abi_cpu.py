@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert moe.moe_abi_version() == 4 == moe.MOE_ABI_VERSION
+    assert moe.moe_abi_version() == 5 == moe.MOE_ABI_VERSION
     hdr = re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read())
     assert hdr and int(hdr.group(1)) == moe.MOE_ABI_VERSION
     for st in (0, -1, -2, -3, -4, -5):
@@ -290,3 +290,46 @@ def test_binding_checks_shapes_before_calling():
         moe.moe_router_logits(x, torch.zeros(8, 64, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         moe.moe_router_logits(x.half(), torch.zeros(8, 128, dtype=torch.half))
+
+
+def test_frag_weights_validation():
+    L = moe.LIB
+    # moe_pack_weights_frag: rows % 16, K % 32, K >= 32, rows * K < 2^36; NULL; alignment
+    pack = lambda w=FAKE, rows=32, K=64, out=FAKE: L.moe_pack_weights_frag(w, rows, K, out, None)
+    assert pack(rows=0) == moe.MOE_OK
+    assert pack(rows=0, w=None) == moe.MOE_OK
+    assert pack(rows=-16) == moe.MOE_ERR_SHAPE
+    assert pack(rows=24) == moe.MOE_ERR_SHAPE
+    assert pack(K=48) == moe.MOE_ERR_SHAPE
+    assert pack(K=0) == moe.MOE_ERR_SHAPE
+    assert pack(rows=1 << 26, K=1 << 10) == moe.MOE_ERR_SHAPE
+    assert pack(w=None) == moe.MOE_ERR_NULL
+    assert pack(out=None) == moe.MOE_ERR_NULL
+    assert pack(w=MISALIGNED) == moe.MOE_ERR_SHAPE
+    assert pack(out=MISALIGNED) == moe.MOE_ERR_SHAPE
+    # MOE_BF16_FRAG in the layer: bf16 activations on the weight-streaming path; no scale arrays
+    T, d, E, H = 16, 256, 8, 256
+    ws = L.moe_workspace_size(T, d, E, H, 1, 1)
+    run = lambda a, n=ws: L.moe_layer_forward(ctypes.byref(a), FAKE, n, None)
+    fr = dict(T=T, d=d, E=E, H=H, w_dtype=moe.MOE_BF16_FRAG)
+    assert run(_args(**{**fr, "T": 0})) == moe.MOE_OK
+    assert run(_args(**fr), n=0) == moe.MOE_ERR_WORKSPACE            # accepted up to the workspace
+    assert run(_args(**{**fr, "dtype": 0})) == moe.MOE_ERR_UNSUPPORTED          # fp32 activations
+    assert run(_args(**{**fr, "d": 128, "H": 128})) == moe.MOE_ERR_UNSUPPORTED  # not streaming
+    assert run(_args(**{**fr, "T": 2048, "k": 2}), n=1 << 40) == moe.MOE_ERR_UNSUPPORTED  # prefill
+
+
+def test_python_pack_wrapper_checks_its_input():
+    import torch
+    with pytest.raises(ValueError):
+        moe.moe_pack_weights_frag(torch.zeros((16, 32), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        moe.moe_pack_weights_frag(torch.zeros((32,), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        moe.make_layer_args(torch.zeros((4, 256)), torch.zeros((8, 256)), torch.zeros((8, 256, 256)),
+                            torch.zeros((8, 256, 256)), torch.zeros((8, 256, 256)), 1, "softmax",
+                            torch.zeros((4, 256)), w_format="frag")
+    with pytest.raises(ValueError):
+        moe.make_layer_args(torch.zeros((4, 256)), torch.zeros((8, 256)), torch.zeros((8, 256, 256)),
+                            torch.zeros((8, 256, 256)), torch.zeros((8, 256, 256)), 1, "softmax",
+                            torch.zeros((4, 256)), w_format="tiled")

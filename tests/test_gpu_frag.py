@@ -1,0 +1,161 @@
+"""Fragment-major bf16 expert weights (MOE_BF16_FRAG) on the decode path: moe_pack_weights_frag
+bit-exact against the oracle's order, and moe_layer_forward on packed stacks (packed by the
+oracle, so the layer test does not depend on the GPU packer) equal to the plain bf16 layer bit
+for bit (the same values in the same lanes and the same sum order), through the workspace entry
+point, the no-alloc entry point and the graph ladder; plus the oracle check of one workload."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as orc
+from expert_routing_grouped_moe_amd import inputs as gen
+
+from _parity import DEV, check_layer, run_layer, upload
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("w_gate", "w_up", "w_down")
+
+
+def _bits_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _frag(inp):
+    """The expert stacks packed by the oracle, on the device."""
+    return {key: _bits_dev(orc.pack_frag_ref(inp.bits[key])) for key in KEYS}
+
+
+def _outs(inp):
+    import torch
+    T, E, k = inp.T, inp.E, inp.k
+    return dict(logits=torch.empty((T, E), dtype=torch.float32, device=DEV),
+                topk_ids=torch.empty((T, k), dtype=torch.int32, device=DEV),
+                topk_w=torch.empty((T, k), dtype=torch.float32, device=DEV),
+                expert_counts=torch.empty((E,), dtype=torch.int32, device=DEV))
+
+
+def _run_frag(inp, dv, fw, noalloc=False):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    outs = _outs(inp)
+    fn = moe.moe_layer_forward_noalloc if noalloc else moe.moe_layer_forward
+    y = fn(dv["x"], dv["w_router"], fw["w_gate"], fw["w_up"], fw["w_down"], inp.k, inp.scoring,
+           router_bias=dv["router_bias"], sel_bias=dv["sel_bias"], w_format="frag", **outs)
+    torch.cuda.synchronize()
+    res = {key: v.cpu().numpy() for key, v in outs.items()}
+    res["y"] = y.cpu().numpy()
+    return res
+
+
+def _same(a, b):
+    for key in ("y", "topk_ids", "topk_w", "expert_counts", "logits"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("shape", [(3, 48, 96), (16, 2816, 2048), (64, 1024, 512), (1, 16, 32)])
+def test_pack_frag_bit_exact(shape):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    rng = np.random.default_rng(sum(shape))
+    bits = gen.bf16_round_bits((rng.standard_normal(shape) * 0.05).astype(np.float32))
+    got = moe.moe_pack_weights_frag(_bits_dev(bits))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16),
+                                  orc.pack_frag_ref(bits))
+
+
+@pytest.mark.parametrize("name", ["zonos2-decode", "zonos3mini-decode-cfg", "zonos2-layer26-decode"])
+def test_frag_layer_equals_plain_layer(name):
+    inp = gen.make_inputs(name)
+    dv = upload(inp)
+    plain = run_layer(inp, dv)
+    res = _run_frag(inp, dv, _frag(inp))
+    _same(res, plain)
+    if name == "zonos3mini-decode-cfg":
+        print(f"{name} frag: {check_layer(inp, res)}")
+
+
+EDGE = [
+    # name, T, d, E, k, H, scoring, sel_bias_var, router_bias
+    ("T1", 1, 256, 16, 1, 256, orc.SOFTMAX, None, None),
+    ("sigmoid-k2", 64, 512, 16, 2, 512, orc.SIGMOID, None, None),
+    ("E256-k8", 64, 256, 256, 8, 256, orc.SELECTED_SOFTMAX, 0.5, None),
+    ("hot-expert", 200, 256, 16, 1, 256, orc.SOFTMAX, None, "hot5"),     # many passes
+    ("rows-17-32", 96, 256, 8, 2, 512, orc.SELECTED_SOFTMAX, 0.5, None),  # two-group passes
+    # six 128-k blocks per row: the rolled reduction loop
+    ("generic-K768", 48, 768, 16, 2, 768, orc.SELECTED_SOFTMAX, 0.5, None),
+    # the largest streaming batch (T k = 2048) with single-group down passes ((d / 16) E > 4096)
+    ("rows-2048-E64", 1024, 1280, 64, 2, 256, orc.SELECTED_SOFTMAX, 0.5, None),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_frag_layer_edge_cases(case):
+    name, T, d, E, k, H, scoring, sbv, rb = case
+    router_bias = None
+    if rb == "hot5":
+        router_bias = np.full(E, -30.0, np.float32)
+        router_bias[5] = 30.0
+    inp = gen.make_inputs_custom(T, d, E, k, H, scoring, "bf16", seed=7 * T + E + k,
+                                 sel_bias_var=sbv, router_bias=router_bias)
+    dv = upload(inp)
+    plain = run_layer(inp, dv)
+    res = _run_frag(inp, dv, _frag(inp))
+    _same(res, plain)
+    if rb == "hot5":
+        assert res["expert_counts"][5] == T
+
+
+def test_frag_layer_with_gpu_packer_and_noalloc():
+    """The library's packer feeding the layer, through both entry points, twice in a row (the
+    second call on fewer tokens)."""
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs("zonos3mini-decode-cfg")
+    dv = upload(inp)
+    fw = {key: moe.moe_pack_weights_frag(dv[key]) for key in KEYS}
+    plain = run_layer(inp, dv)
+    _same(_run_frag(inp, dv, fw), plain)
+    _same(_run_frag(inp, dv, fw, noalloc=True), plain)
+    sub = dataclasses.replace(inp, T=24, x=inp.x[:24], bits=dict(inp.bits, x=inp.bits["x"][:24]))
+    dsub = dict(dv, x=dv["x"][:24].contiguous())
+    _same(_run_frag(sub, dsub, fw, noalloc=True), run_layer(sub, dsub))
+
+
+def test_frag_ladder_equals_plain_calls():
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs("zonos2-decode")
+    dv = upload(inp)
+    fw = _frag(inp)
+    stream = torch.cuda.Stream()
+    y = torch.empty((inp.T, inp.d), dtype=torch.float32, device=DEV)
+    lad = moe.MoeGraphLadder(dv["x"], dv["w_router"], fw["w_gate"], fw["w_up"], fw["w_down"],
+                             inp.k, inp.scoring, [8, 32, 64], y=y, router_bias=dv["router_bias"],
+                             stream=stream, w_format="frag")
+    try:
+        for T in (64, 5, 32):
+            y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            lad.run(T, stream=stream)
+            stream.synchronize()
+            ref = moe.moe_layer_forward(dv["x"][:T], dv["w_router"], dv["w_gate"], dv["w_up"],
+                                        dv["w_down"], inp.k, inp.scoring,
+                                        router_bias=dv["router_bias"])
+            torch.cuda.synchronize()
+            assert torch.equal(y[:T], ref), T
+    finally:
+        lad.close()
+
+
+def test_frag_rejected_outside_decode_path():
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs_custom(3000, 256, 8, 1, 256, orc.SOFTMAX, "bf16", seed=9)
+    dv = upload(inp)
+    fw = _frag(inp)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_forward(dv["x"], dv["w_router"], fw["w_gate"], fw["w_up"], fw["w_down"], 1,
+                              inp.scoring, w_format="frag")
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
