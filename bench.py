@@ -106,7 +106,8 @@ def _hip():
 def algorithmic(inp, counts, weights="native"):
     """Bytes and FLOPs the step must move/do (touched experts only; intermediates excluded).
     int8 expert weights: one byte per weight plus the fp32 row scales of the touched experts;
-    q4: half a byte per weight plus one 4-byte (scale, bias) pair per group of 64."""
+    q4: half a byte per weight plus one 4-byte (scale, bias) pair per group of 64; frag: the bf16
+    weights reordered, two bytes per weight."""
     T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
     ab = 2 if inp.dtype == "bf16" else 4             # activations and router weights
     wb = {"int8": 1, "q4": 0.5}.get(weights, ab)     # expert weights
@@ -125,7 +126,7 @@ def algorithmic(inp, counts, weights="native"):
                 gu_flops=gu_flops)
 
 
-def ladder_timing(moe, inp, x, wr, copies, rb, sb, steps, quant=False):
+def ladder_timing(moe, inp, x, wr, copies, rb, sb, steps, quant=False, w_format="plain"):
     """Serving-side decode with a changing batch width: `steps` steps whose token counts are drawn
     uniformly from 1..T (seeded), run as direct moe_layer_forward calls, as replays of a graph
     ladder with one bucket per batch width, and as replays of a ladder with power-of-two buckets
@@ -142,7 +143,8 @@ def ladder_timing(moe, inp, x, wr, copies, rb, sb, steps, quant=False):
     qs = lambda c: ((c["w_gate_scale"], c["w_up_scale"], c["w_down_scale"]) if quant else None)
     mk = lambda buckets: [moe.MoeGraphLadder(x, wr, c["w_gate"], c["w_up"], c["w_down"], k,
                                              inp.scoring, buckets, router_bias=rb, sel_bias=sb,
-                                             w_scales=qs(c), stream=stream) for c in copies]
+                                             w_scales=qs(c), stream=stream, w_format=w_format)
+                          for c in copies]
     ladders = {"ladder": mk(exact), "ladder_pow2": mk(pow2)}
     ys = [torch.empty((T, inp.d), dtype=torch.float32, device=x.device) for _ in copies]
     wss = [torch.empty(max(1, moe.moe_workspace_size(T, inp.d, inp.E, inp.H, k, moe.MOE_BF16
@@ -153,7 +155,8 @@ def ladder_timing(moe, inp, x, wr, copies, rb, sb, steps, quant=False):
         c = copies[i % len(copies)]
         moe.moe_layer_forward(x[:t], wr, c["w_gate"], c["w_up"], c["w_down"], k, inp.scoring,
                               router_bias=rb, sel_bias=sb, y=ys[i % len(copies)][:t],
-                              workspace=wss[i % len(copies)], stream=stream, w_scales=qs(c))
+                              workspace=wss[i % len(copies)], stream=stream, w_scales=qs(c),
+                              w_format=w_format)
 
     def replay(name):
         return lambda i, t: ladders[name][i % len(copies)].run(int(t), stream)
@@ -239,7 +242,7 @@ def dominant_kernel(inp, weights="native"):
         return "ffn_f32_kernel<true>"
     if T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and T * k <= 32 * E:
         maxg = 2 if (H // 16) * E <= 2048 else 1
-        return "ffn_stream_kernel<true, %d, %d>" % (maxg, {"native": 0, "int8": 1, "q4": 2}[weights])
+        return "ffn_stream_kernel<true, %d, %d>" % (maxg, {"native": 0, "int8": 1, "q4": 2, "frag": 3}[weights])
     return gemm_kernel_name(T * k, E, True)
 
 
@@ -333,7 +336,11 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
     x = up("x")
     wr = up("w_router")
     base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
-    quant = weights != "native"
+    quant = weights in ("int8", "q4")
+    w_format = "frag" if weights == "frag" else "plain"
+    if w_format == "frag":
+        base = {key: moe.moe_pack_weights_frag(t) for key, t in base.items()}
+        torch.cuda.synchronize()
     if quant:
         qfn = moe.moe_quantize_rows_i8 if weights == "int8" else moe.moe_quantize_groups_q4
         qs = {key: qfn(t) for key, t in base.items()}
@@ -365,7 +372,8 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
                   if quant else None)
         arg_list.append(moe.make_layer_args(x, wr, copies[c]["w_gate"], copies[c]["w_up"],
                                             copies[c]["w_down"], k, inp.scoring, y, rb, sb,
-                                            expert_counts=counts, w_scales=scales))
+                                            expert_counts=counts, w_scales=scales,
+                                            w_format=w_format))
 
     stream = torch.cuda.Stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
@@ -458,7 +466,7 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
                 "measured_read_ceiling": HBM_READ_CEILING_GBS,
                 "frac_of_measured_ceiling": ach / HBM_READ_CEILING_GBS}
     roof["kernel"] = dominant_kernel(inp, weights)
-    traffic = measured_traffic(roof["kernel"], name + ("/" + weights if quant else ""))
+    traffic = measured_traffic(roof["kernel"], name + ("/" + weights if weights != "native" else ""))
     roof["traffic"] = traffic
     roof["traffic_source"] = ("profiles/traffic.md (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
                               if traffic is not None else "not measured for the current kernel")
@@ -477,7 +485,8 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
                    "scoring": inp.scoring, "seed": gen.WORKLOADS[name].seed,
                    "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
                    "expert_weights": {"int8": "int8, fp32 row scales",
-                                      "q4": "4-bit affine, groups of 64, bf16 scale and bias"
+                                      "q4": "4-bit affine, groups of 64, bf16 scale and bias",
+                                      "frag": "bf16, fragment-major (moe_pack_weights_frag)"
                                       }.get(weights, inp.dtype),
                    "timing": ("host launches" if eager else
                               "HIP graph replay: cycles of one step per weight copy, single "
@@ -496,7 +505,8 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
         "roofline": roof,
     }
     if ladder:
-        out["ladder"] = ladder_timing(moe, inp, x, wr, copies, rb, sb, ladder, quant=quant)
+        out["ladder"] = ladder_timing(moe, inp, x, wr, copies, rb, sb, ladder, quant=quant,
+                                      w_format=w_format)
     if cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(inp, cpu_budget)
     for evs in events:
@@ -522,11 +532,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
-    ap.add_argument("--weights", choices=("native", "int8", "q4"), default="native",
+    ap.add_argument("--weights", choices=("native", "int8", "q4", "frag"), default="native",
                     help="expert weights as given (bf16/fp32), int8 codes with per-row scales "
-                         "(moe_quantize_rows_i8) or 4-bit affine codes in groups of 64 "
-                         "(moe_quantize_groups_q4); quantised weights on decode shapes only, "
-                         "headline workload only")
+                         "(moe_quantize_rows_i8), 4-bit affine codes in groups of 64 "
+                         "(moe_quantize_groups_q4) or bf16 reordered fragment-major "
+                         "(moe_pack_weights_frag); these on decode shapes only, headline workload "
+                         "only")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -573,6 +584,17 @@ def main():
             print(f"[bench] {name}: {others[name]['ms_per_step'] * 1e3:.1f} us/step",
                   file=sys.stderr, flush=True)
 
+    # the decode workloads again on fragment-major bf16 weights (same values, reordered once)
+    frag = {}
+    if not args.only and args.weights == "native":
+        for name in ("zonos2-decode", "zonos3mini-decode-cfg"):
+            r = run_workload(name, args.other_steps, max(1, args.other_steps // 10), weights="frag",
+                             warm=args.warm, eager=args.eager)
+            frag[name] = {key: r[key] for key in ("ms_per_step", "tokens_per_s", "stage_median_us",
+                                                   "event_step_us", "roofline")}
+            print(f"[bench] {name} (fragment-major weights): {r['ms_per_step'] * 1e3:.1f} us/step",
+                  file=sys.stderr, flush=True)
+
     result = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -608,6 +630,8 @@ def main():
         table = {args.workload: {key: v for key, v in head.items() if key != "cpu_baseline"}}
         table.update(others)
         result["workloads"] = {name: table[name] for name in FIVE if name in table}
+    if frag:
+        result["decode_fragment_major_weights"] = frag
     print(json.dumps(result))
 
 
