@@ -199,21 +199,43 @@ def pack_q4_ref(q):
     return dw.astype("<u4").view(np.uint8).reshape(q.shape[:-1] + (K // 2,))
 
 
-def pack_frag_ref(w):
-    """The library's fragment-major storage of a bf16 weight matrix [..., R, K] (R a multiple of
-    16, K of 32), for the decode kernels: the 16 x 32 block of rows 16 b .. 16 b + 15 and reduction
-    indices 32 s .. 32 s + 31 is stored as 512 consecutive values at (b * K / 32 + s) * 512, value
-    (r, k) of it at 128 ((k mod 32) div 8) + 8 (r mod 16) + (k mod 8), i.e. the 16 bytes that lane
-    (r mod 16) + 16 ((k mod 32) div 8) of a 16 x 16 x 32 MFMA takes as its operand, lanes in
-    order. A pure reordering: the values are unchanged. Returns the same shape, reordered."""
+def pack_frag_ref(w, fmt="bf16"):
+    """The library's fragment-major storage of an expert weight matrix for the decode kernels: the
+    matrix is cut into slabs of 16 rows, and each slab is stored as consecutive 1024-byte chunks,
+    chunk i holding the 64 sixteen-byte pieces that the 64 lanes of a wave take in the decode
+    kernel's i-th load instruction over that slab, lane l's piece at byte 16 l; every piece comes
+    from row l mod 16 of the slab. Which bytes of the row lane l takes depends on the format:
+      bf16 [..., R, K] values (K a multiple of 32): the eight values k = 32 i + 8 (l div 16) + 0..7,
+        the A operand of lane l in a 16 x 16 x 32 MFMA (matrix-core ISA operand layout);
+      "i8" int8 codes [..., R, K] (K a multiple of 128): the 16 codes k = 128 (i div 2) +
+        32 (l div 16) + 16 (i mod 2) + 0..15 (per 128-k block, lane group g takes the 32 codes from
+        32 g on, as two loads);
+      "q4" packed 4-bit bytes [..., R, K / 2] in the order of pack_q4_ref (K a multiple of 128):
+        bytes 64 i + 16 (l div 16) + 0..15 of the packed row (block i, the codes lane group
+        l div 16 needs).
+    A pure reordering of the bytes. Returns the same shape and dtype."""
     w = np.asarray(w)
-    R, K = w.shape[-2], w.shape[-1]
-    assert R % 16 == 0 and K % 32 == 0
-    lead = w.shape[:-2]
-    # [..., b, r16, s, q, i] -> [..., b, s, q, r16, i]
-    v = w.reshape(lead + (R // 16, 16, K // 32, 4, 8))
-    n = len(lead)
-    v = v.transpose(tuple(range(n)) + (n, n + 2, n + 3, n + 1, n + 4))
+    R = w.shape[-2]
+    assert R % 16 == 0
+    lead, n = w.shape[:-2], w.ndim - 2
+    if fmt == "bf16":
+        K = w.shape[-1]
+        assert K % 32 == 0
+        v = w.reshape(lead + (R // 16, 16, K // 32, 4, 8))        # b, r16, i, g, value
+        order = (n, n + 2, n + 3, n + 1, n + 4)                     # b, i, g, r16, value
+    elif fmt == "i8":
+        K = w.shape[-1]
+        assert K % 128 == 0
+        v = w.reshape(lead + (R // 16, 16, K // 128, 4, 2, 16))   # b, r16, block, g, half, code
+        order = (n, n + 2, n + 4, n + 3, n + 1, n + 5)              # b, block, half, g, r16, code
+    elif fmt == "q4":
+        nb = w.shape[-1]
+        assert nb % 64 == 0
+        v = w.reshape(lead + (R // 16, 16, nb // 64, 4, 16))      # b, r16, block, g, byte
+        order = (n, n + 2, n + 3, n + 1, n + 4)                     # b, block, g, r16, byte
+    else:
+        raise ValueError(fmt)
+    v = v.transpose(tuple(range(n)) + order)
     return np.ascontiguousarray(v).reshape(w.shape)
 
 

@@ -363,6 +363,60 @@ def test_frag_layout_feeds_the_matrix_core_product():
     np.testing.assert_array_equal(P[8 * 63:], 1524 + np.arange(8))
 
 
+def _lane_pieces(P, R, K_bytes):
+    """Fragment-major bytes [R * K_bytes] as [slab, chunk, lane, 16 bytes]."""
+    return P.reshape(R // 16, K_bytes // 64, 64, 16)
+
+
+def test_frag_order_of_int8_codes():
+    """Each lane's 16 codes, taken as k = 128 (i div 2) + 32 g + 16 (i mod 2) + 0..15 of row
+    l mod 16 (g = l div 16, i the chunk), multiplied by X and summed per row, give the plain
+    product of the codes with X; every code moves once."""
+    rng = np.random.default_rng(31)
+    for R, K in ((16, 128), (48, 384)):
+        q = rng.integers(-127, 128, size=(R, K)).astype(np.int8)
+        X = rng.integers(-8, 9, size=(K, 3)).astype(np.int64)
+        P = orc.pack_frag_ref(q, "i8")
+        assert P.dtype == np.int8 and P.shape == q.shape
+        np.testing.assert_array_equal(np.sort(P.ravel()), np.sort(q.ravel()))
+        L = _lane_pieces(P.view(np.uint8).ravel(), R, K)
+        Y = np.zeros((R, 3), np.int64)
+        for b in range(R // 16):
+            for i in range(K // 64):
+                for lane in range(64):
+                    codes = L[b, i, lane].view(np.int8).astype(np.int64)
+                    k0 = 128 * (i // 2) + 32 * (lane // 16) + 16 * (i % 2)
+                    Y[16 * b + lane % 16] += codes @ X[k0:k0 + 16]
+        np.testing.assert_array_equal(Y, q.astype(np.int64) @ X)
+
+
+def test_frag_order_of_q4_codes():
+    """Each lane's 16 bytes read as four little-endian dwords c = 0..3 of block i, dword c holding
+    k = 128 i + 32 c + 8 g + j (j = 2m at bits 4m, j = 2m + 1 at bits 16 + 4m; the packed 4-bit
+    order), multiplied by X and summed per row, give the plain product of the codes with X."""
+    rng = np.random.default_rng(37)
+    for R, K in ((16, 128), (32, 512)):
+        codes = rng.integers(0, 16, size=(R, K))
+        X = rng.integers(-8, 9, size=(K, 3)).astype(np.int64)
+        packed = orc.pack_q4_ref(codes)
+        P = orc.pack_frag_ref(packed, "q4")
+        assert P.dtype == np.uint8 and P.shape == packed.shape
+        np.testing.assert_array_equal(np.sort(P.ravel()), np.sort(packed.ravel()))
+        L = _lane_pieces(P.ravel(), R, K // 2)
+        Y = np.zeros((R, 3), np.int64)
+        for b in range(R // 16):
+            for i in range(K // 128):
+                for lane in range(64):
+                    words = L[b, i, lane].copy().view("<u4")
+                    for c in range(4):
+                        for j in range(8):
+                            sh = 4 * (j // 2) + (16 if j % 2 else 0)
+                            code = int((words[c] >> sh) & 15)
+                            k = 128 * i + 32 * c + 8 * (lane // 16) + j
+                            Y[16 * b + lane % 16] += code * X[k]
+        np.testing.assert_array_equal(Y, codes @ X)
+
+
 def test_q4_layer_on_exact_weights_equals_plain_layer():
     # weights that are exactly s * q + b: the 4-bit layer is the plain layer on the same weights
     inp = _case(T=16, d=128, E=4, k=2, H=128, scoring=orc.SOFTMAX, seed=15)
@@ -582,6 +636,8 @@ def _pins_pass():
         test_hand_fp32_rank_add(hand)
         test_hand_q4_param_words(hand)
         test_frag_layout_feeds_the_matrix_core_product()
+        test_frag_order_of_int8_codes()
+        test_frag_order_of_q4_codes()
         test_hand_expert_counts()
         test_selection_admissible_rules()
         test_hand_swiglu_layer(hand, "swiglu_one_expert")
@@ -664,8 +720,13 @@ MUTATIONS = {
     "q4_pack_swap": ("pack_q4_ref", lambda orig: (lambda q: (lambda p: ((p & 15) << 4 | (p >> 4)).astype(np.uint8))(
         orig(q)))),
     # fragment-major blocks with the row and k-quarter orders swapped inside each fragment
-    "frag_lane_order": ("pack_frag_ref", lambda orig: (lambda w: (lambda p: np.ascontiguousarray(
-        p.reshape(p.shape[:-2] + (-1, 4, 16, 8)).swapaxes(-3, -2)).reshape(p.shape))(orig(w)))),
+    "frag_lane_order": ("pack_frag_ref", lambda orig: (lambda w, fmt="bf16": (lambda p: np.ascontiguousarray(
+        p.reshape(p.shape[:-2] + (-1, 4, 16, 8)).swapaxes(-3, -2)).reshape(p.shape) if fmt == "bf16" else p)(
+        orig(w, fmt)))),
+    # int8 fragment order with each lane group's two halves taken from 16-code steps (the bf16
+    # lane order applied to bytes)
+    "frag_i8_halves": ("pack_frag_ref", lambda orig: (lambda w, fmt="bf16": orig(w, "q4") if fmt == "i8"
+                                                      else orig(w, fmt))),
     # (scale, bias) halves of the 4-bit parameter word swapped
     "q4_params_swap": ("pack_q4_params_ref", lambda orig: (lambda s, b: orig(b, s))),
     # expert counts shifted by one index (the total stays right)
