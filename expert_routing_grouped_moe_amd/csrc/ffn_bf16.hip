@@ -413,11 +413,11 @@ __device__ __forceinline__ u32x4 q4x8_dequant(uint32_t v, uint32_t pair) {
 //    in the epilogue; 4-bit weights (W4): the bf16 k layout, a lane's 16 code bytes of the block
 //    in one load plus the (scale, bias) pairs of the block's two groups of 64, each weight formed
 //    as s * q + b in fp16 right before the MFMA (q4x8_dequant), the gate/up's
-//    bf16 token rows converted to fp16 for these products; fragment-major bf16 weights (WFR): the
-//    bf16 k layout, each step's 64 lanes x 16 bytes one contiguous kilobyte (eight whole 128-byte
-//    lines, where a row-major instruction covers half of each of 16 lines). The A rows (a token
-//    row of x or a row of h, both L2-resident) are read with the same k layout, one piece per
-//    step, for every group;
+//    bf16 token rows converted to fp16 for these products. Fragment-major storage of any of the
+//    three (WFR): the same bytes reach the same lanes, but each load instruction's 64 lanes x 16
+//    bytes are one contiguous kilobyte (eight whole 128-byte lines, where a row-major instruction
+//    covers half of each of 16 lines). The A rows (a token row of x or a row of h, both
+//    L2-resident) are read with the same k layout, one piece per step, for every group;
 //  * two blocks are in flight ahead of use;
 //  * waves start at different blocks of the reduction (a rotation by the wave's global index) so
 //    that concurrent waves spread over the HBM channels instead of reading the same offset of
@@ -431,7 +431,8 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
                                             int e, int slab, const int* lr, int m0, int rows,
                                             int hbase, uint16_t* __restrict__ h_out,
                                             const DownArgs& down) {
-  constexpr bool W8 = WF == kWI8, W4 = WF == kWQ4, WFR = WF == kWFrag;
+  constexpr int BASE = WF & ~kWFragMajor;
+  constexpr bool W8 = BASE == kWI8, W4 = BASE == kWQ4, WFR = (WF & kWFragMajor) != 0;
   constexpr int WR = W8 ? 2 : (W4 ? 1 : 4);   // weight registers (u32x4) per matrix per block
   const int lane = lane_id();
   const int l16 = lane & 15;
@@ -441,9 +442,9 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
   const long long row0 = static_cast<long long>(e) * N + f;
   // bytes: bf16 2 per weight, int8 1, 4-bit one half (a lane's 16 bytes of a block hold the
   // codes of its k = 32 c + 8 g runs, as packed by moe_quantize_groups_q4)
-  // fragment-major bf16: the wave's 16 rows are one run of K / 32 fragments of 1024 bytes, lane l
-  // at 16 l in each (row l % 16, k = 32 s + 8 (l / 16) + 0..7: the bf16 layout's values)
-  const long long wofs = WFR ? (row0 >> 4) * 32 * K + 16 * lane
+  // fragment-major: the wave's 16 rows are one run of 1024-byte chunks, one per load instruction
+  // (WR per block), lane l's 16 bytes at 16 l in each: the same bytes as in the row-major layout
+  const long long wofs = WFR ? (row0 >> 4) * 16 * (W4 ? K / 2 : (W8 ? K : 2 * K)) + 16 * lane
                              : (W4 ? row0 * (K / 2) + 16 * grp
                                    : (W8 ? row0 * K + kq : 2 * (row0 * K + kq)));
   const char* pg = static_cast<const char*>(W0) + wofs;
@@ -478,7 +479,7 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
     const int kb = blk * 128;
 #pragma unroll
     for (int c = 0; c < WR; ++c) {
-      const int off = WFR ? 1024 * (4 * blk + c)
+      const int off = WFR ? 1024 * (WR * blk + c)
                           : (W4 ? 64 * blk : (W8 ? kb + 16 * c : 2 * (kb + 32 * c)));  // bytes
       bg[j][c] = load16(pg + off);
       if constexpr (GATEUP) bu[j][c] = load16(pu + off);
@@ -518,7 +519,7 @@ __device__ __forceinline__ void stream_tile(const uint16_t* __restrict__ A,
       u32x4 wg = wop(bg[j], c, pgs[j]);
       u32x4 wu = wg;
       if constexpr (GATEUP) wu = wop(bu[j], c, pus[j]);
-      if constexpr (kF16Down && (WF == kWBf16 || WFR)) wg = bf16x8_to_f16x8(wg);
+      if constexpr (kF16Down && BASE == kWBf16) wg = bf16x8_to_f16x8(wg);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if constexpr (kF16Down) {
@@ -762,8 +763,15 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, co
       case kWBf16: return launch_streaming<kWBf16>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
       case kWI8: return launch_streaming<kWI8>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
       case kWQ4: return launch_streaming<kWQ4>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
-      case kWFrag:
-        return launch_streaming<kWFrag>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu, qw);
+      case kWBf16 | kWFragMajor:
+        return launch_streaming<kWBf16 | kWFragMajor>(x, wg, wu, wd, d, E, H, k, rs, h, down, s,
+                                                      gu, qw);
+      case kWI8 | kWFragMajor:
+        return launch_streaming<kWI8 | kWFragMajor>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu,
+                                                    qw);
+      case kWQ4 | kWFragMajor:
+        return launch_streaming<kWQ4 | kWFragMajor>(x, wg, wu, wd, d, E, H, k, rs, h, down, s, gu,
+                                                    qw);
       default: return hipErrorInvalidValue;
     }
   }

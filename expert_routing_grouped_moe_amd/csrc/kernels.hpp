@@ -127,7 +127,8 @@ enum WeightFormat {
   kWBf16 = 0,  // bf16 bits
   kWI8 = 1,    // int8 codes, fp32 row scales `gate`, `up`, `down` ([E,H], [E,H], [E,d])
   kWQ4 = 2,    // packed 4-bit codes, uint32 (scale, bias) pairs per group of 64 along K
-  kWFrag = 3   // bf16 bits in fragment-major order (moe_pack_weights_frag)
+  // flag on any of the above: the stacks' bytes in fragment-major order (moe_pack_weights_frag)
+  kWFragMajor = 4
 };
 struct QuantWeights {
   int fmt;           // WeightFormat
@@ -156,8 +157,11 @@ hipError_t launch_quantize_rows_i8(const void* w, long long rows, int K, bool bf
 // K % 128 == 0.
 hipError_t launch_quantize_groups_q4(const void* w, long long rows, int K, bool bf16, uint8_t* q,
                                      uint32_t* qpar, hipStream_t s);
-// bf16 [rows, K] -> fragment-major order (moe_pack_weights_frag); rows % 16 == 0, K % 32 == 0.
-hipError_t launch_pack_frag(const uint16_t* w, long long rows, int K, uint16_t* out, hipStream_t s);
+// Fragment-major order (moe_pack_weights_frag) of a [rows, row_bytes] matrix stored as `fmt`
+// (kWBf16, kWI8 or kWQ4; row_bytes = 2 K, K or K / 2); rows % 16 == 0, row_bytes % 64 == 0 (bf16)
+// or K % 128 == 0 (codes).
+hipError_t launch_pack_frag(const void* w, long long rows, int row_bytes, int fmt, void* out,
+                            hipStream_t s);
 
 // ---------------------------------------------------------------- combine (combine.hip)
 // row_pos == NULL: expert_out is indexed by the assignment row itself. y_bf16: y holds bf16 bits

@@ -250,15 +250,19 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
                                                    static_cast<hipStream_t>(stream)));
 }
 
-int moe_pack_weights_frag(const void* w, int64_t rows, int K, void* out, void* stream) {
-  if (rows < 0 || rows % 16 != 0 || K < 32 || K % 32 != 0) return MOE_ERR_SHAPE;
+int moe_pack_weights_frag(const void* w, int64_t rows, int K, int w_dtype, void* out,
+                          void* stream) {
+  if (w_dtype != MOE_BF16 && w_dtype != MOE_I8 && w_dtype != MOE_Q4) return MOE_ERR_UNSUPPORTED;
+  const int kmul = w_dtype == MOE_BF16 ? 32 : 128;
+  if (rows < 0 || rows % 16 != 0 || K < kmul || K % kmul != 0) return MOE_ERR_SHAPE;
   if (rows * K >= kMaxQuantElems) return MOE_ERR_SHAPE;
   if (rows == 0) return MOE_OK;
   if (!w || !out) return MOE_ERR_NULL;
   if (!aligned16(w) || !aligned16(out)) return MOE_ERR_SHAPE;
+  const int row_bytes = w_dtype == MOE_BF16 ? 2 * K : (w_dtype == MOE_I8 ? K : K / 2);
+  const int fmt = w_dtype == MOE_BF16 ? moe::kWBf16 : (w_dtype == MOE_I8 ? moe::kWI8 : moe::kWQ4);
   clear_stale_error();
-  return hip_status(moe::launch_pack_frag(static_cast<const uint16_t*>(w), rows, K,
-                                          static_cast<uint16_t*>(out),
+  return hip_status(moe::launch_pack_frag(w, rows, row_bytes, fmt, out,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -290,18 +294,25 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
   const bool abi2 = a->struct_size >= MOE_LAYER_ARGS_V2_SIZE;
   const int w_dtype = (abi2 && a->w_dtype != 0) ? a->w_dtype : dtype;
   moe::QuantWeights qw{};
-  if (w_dtype == MOE_BF16_FRAG) {
-    if (dtype != MOE_BF16 || !moe::ffn_bf16_streaming(T, d, E, H, k)) return MOE_ERR_UNSUPPORTED;
-    qw = moe::QuantWeights{moe::kWFrag, nullptr, nullptr, nullptr};
-  } else if (w_dtype != dtype) {
-    if ((w_dtype != MOE_I8 && w_dtype != MOE_Q4) || dtype != MOE_BF16 ||
+  if (w_dtype != dtype) {
+    // the prepared decode formats: int8 or 4-bit codes, and the fragment-major order of these or
+    // of bf16 weights
+    const bool frag = w_dtype == MOE_BF16_FRAG || w_dtype == MOE_I8_FRAG || w_dtype == MOE_Q4_FRAG;
+    const int base = w_dtype == MOE_BF16_FRAG ? MOE_BF16
+                     : (w_dtype == MOE_I8_FRAG ? MOE_I8 : (w_dtype == MOE_Q4_FRAG ? MOE_Q4 : w_dtype));
+    if ((base != MOE_BF16 && base != MOE_I8 && base != MOE_Q4) || dtype != MOE_BF16 ||
         !moe::ffn_bf16_streaming(T, d, E, H, k))
       return MOE_ERR_UNSUPPORTED;
-    if (!a->w_gate_scale || !a->w_up_scale || !a->w_down_scale) return MOE_ERR_NULL;
-    if (!aligned16(a->w_gate_scale) || !aligned16(a->w_up_scale) || !aligned16(a->w_down_scale))
-      return MOE_ERR_SHAPE;
-    qw = moe::QuantWeights{w_dtype == MOE_I8 ? moe::kWI8 : moe::kWQ4, a->w_gate_scale,
-                           a->w_up_scale, a->w_down_scale};
+    const int fmt = (base == MOE_I8 ? moe::kWI8 : (base == MOE_Q4 ? moe::kWQ4 : moe::kWBf16)) |
+                    (frag ? moe::kWFragMajor : 0);
+    if (base == MOE_BF16) {
+      qw = moe::QuantWeights{fmt, nullptr, nullptr, nullptr};
+    } else {
+      if (!a->w_gate_scale || !a->w_up_scale || !a->w_down_scale) return MOE_ERR_NULL;
+      if (!aligned16(a->w_gate_scale) || !aligned16(a->w_up_scale) || !aligned16(a->w_down_scale))
+        return MOE_ERR_SHAPE;
+      qw = moe::QuantWeights{fmt, a->w_gate_scale, a->w_up_scale, a->w_down_scale};
+    }
   }
   const bool abi4 = a->struct_size >= offsetof(moe_layer_args, y_dtype) + sizeof(a->y_dtype);
   const int y_dtype = abi4 ? a->y_dtype : MOE_F32;

@@ -1,6 +1,7 @@
 // Prepared expert weights for the decode path: 4-bit affine group codes
-// (moe_quantize_groups_q4, below), symmetric per-row int8 codes (moe_quantize_rows_i8) and bf16
-// weights reordered fragment-major (moe_pack_weights_frag, exact). The int8 codes:
+// (moe_quantize_groups_q4, below), symmetric per-row int8 codes (moe_quantize_rows_i8) and the
+// fragment-major order of any of these or of bf16 weights (moe_pack_weights_frag, exact). The int8
+// codes:
 //   s = fp32(max_i |w_i| / 127),   q_i = clamp(rint(fp32(w_i / s)), -127, 127)   (ties to even)
 // both divisions IEEE round-to-nearest-even (__fdiv_rn), so the codes are defined exactly; an
 // all-zero row gets s = 0 and q = 0. The pages run quantised expert stacks for decode
@@ -123,37 +124,39 @@ __global__ __launch_bounds__(256) void quantize_groups_q4_kernel(
   }
 }
 
-// Fragment-major bf16 weights (moe_pack_weights_frag): one thread per 16-byte piece of the output.
-// Fragment f = b (K / 32) + s holds rows 16 b .. 16 b + 15 and k = 32 s .. 32 s + 31 as 64 pieces,
-// piece l being the eight values of row 16 b + l % 16 at k = 32 s + 8 (l / 16) + 0..7: the operand
-// that lane l of a 16 x 16 x 32 matrix-core step takes. The writes are contiguous; each wave reads
-// 16 rows x 64 bytes (a one-time preparation).
-__global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restrict__ w,
-                                                        long long pieces, int K,
-                                                        uint16_t* __restrict__ out) {
+// Fragment-major weights (moe_pack_weights_frag): one thread per 16-byte piece of the output. A
+// slab of 16 rows is stored as row_bytes / 64 chunks of 1024 bytes; lane l's piece of chunk i is a
+// piece of row l % 16: piece 4 i + l / 16 of the row for bf16 values and packed 4-bit codes (the
+// 64 bytes of each row in chunk i go to four lane groups in order), piece 8 (i / 2) + 2 (l / 16) +
+// i % 2 for int8 codes (lane group g's 32 codes of a 128-k block, as two pieces). The writes are
+// contiguous; each wave reads 16 rows x 64 bytes (a one-time preparation).
+__global__ __launch_bounds__(256) void pack_frag_kernel(const uint8_t* __restrict__ w,
+                                                        long long pieces, int row_bytes, bool i8,
+                                                        uint8_t* __restrict__ out) {
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
-  const int steps = K / 32;
+  const int chunks = row_bytes / 64;   // per slab
   for (long long p = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; p < pieces;
        p += stride) {
-    const long long frag = p >> 6;
+    const long long chunk = p >> 6;
     const int l = static_cast<int>(p & 63);
-    const long long b = frag / steps;
-    const int st = static_cast<int>(frag - b * steps);
+    const long long b = chunk / chunks;
+    const int i = static_cast<int>(chunk - b * chunks);
     const long long row = 16 * b + (l & 15);
-    const int k0 = 32 * st + 8 * (l >> 4);
-    store16(out + 8 * p, load16(w + row * K + k0));
+    const int piece = i8 ? 8 * (i >> 1) + 2 * (l >> 4) + (i & 1) : 4 * i + (l >> 4);
+    store16(out + 16 * p, load16(w + row * row_bytes + 16 * piece));
   }
 }
 
 }  // namespace
 
-hipError_t launch_pack_frag(const uint16_t* w, long long rows, int K, uint16_t* out,
+hipError_t launch_pack_frag(const void* w, long long rows, int row_bytes, int fmt, void* out,
                             hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const long long pieces = rows * K / 8;
+  const long long pieces = rows * row_bytes / 16;
   const long long blocks = (pieces + 255) / 256;
   const unsigned grid = static_cast<unsigned>(blocks < (1ll << 20) ? blocks : (1ll << 20));
-  pack_frag_kernel<<<grid, 256, 0, s>>>(w, pieces, K, out);
+  pack_frag_kernel<<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(w), pieces, row_bytes,
+                                        fmt == kWI8, static_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ MOE_BF16 = 1
 MOE_I8 = 2
 MOE_Q4 = 3
 MOE_BF16_FRAG = 4
+MOE_I8_FRAG = 5
+MOE_Q4_FRAG = 6
 
 MOE_SCORING_SOFTMAX = 0
 MOE_SCORING_SELECTED_SOFTMAX = 1
@@ -110,7 +112,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_groups_q4.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
                                            c_void_p, c_void_p]
     lib.moe_pack_weights_frag.restype = c_int
-    lib.moe_pack_weights_frag.argtypes = [c_void_p, ctypes.c_int64, c_int, c_void_p, c_void_p]
+    lib.moe_pack_weights_frag.argtypes = [c_void_p, ctypes.c_int64, c_int, c_int, c_void_p,
+                                          c_void_p]
     lib.moe_ladder_create.restype = c_int
     lib.moe_ladder_create.argtypes = [POINTER(MoeLayerArgs), c_void_p, c_int, c_void_p, c_size_t,
                                       c_void_p, POINTER(c_void_p)]
@@ -291,15 +294,18 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
                     w_scales=None, w_format="plain"):
     """Quantised expert weights: int8 codes (moe_quantize_rows_i8) with ``w_scales`` = their
     (gate, up, down) fp32 row scales, or uint8 packed 4-bit codes (moe_quantize_groups_q4) with
-    ``w_scales`` = their int32 (scale, bias) pair arrays. ``w_format="frag"``: bf16 expert stacks
-    reordered by moe_pack_weights_frag (same shapes and dtype as the plain stacks)."""
+    ``w_scales`` = their int32 (scale, bias) pair arrays. ``w_format="frag"``: the expert stacks
+    (bf16, int8 or packed 4-bit) reordered by moe_pack_weights_frag (same shapes and dtypes as the
+    row-major stacks; scales unchanged)."""
     T, d = x.shape
     E, H, _ = w_gate.shape
     if w_format not in ("plain", "frag"):
         raise ValueError(f"w_format must be 'plain' or 'frag', not {w_format!r}")
     wt = w_gate.dtype if w_gate.dtype in (torch.int8, torch.uint8) else x.dtype
-    if w_format == "frag" and (wt != torch.bfloat16 or x.dtype != torch.bfloat16):
-        raise ValueError("w_format='frag' needs bfloat16 activations and expert stacks")
+    if w_format == "frag" and (wt not in (torch.bfloat16, torch.int8, torch.uint8) or
+                               x.dtype != torch.bfloat16):
+        raise ValueError("w_format='frag' needs bfloat16 activations and bfloat16, int8 or "
+                         "packed 4-bit expert stacks")
     q4 = wt == torch.uint8
     _need(x, "x", (T, d))
     _need(w_router, "w_router", (E, d), x.dtype)
@@ -330,7 +336,7 @@ def make_layer_args(x, w_router, w_gate, w_up, w_down, k, scoring, y, router_bia
     a.dtype = _dtype_code(x)
     a.w_dtype = {torch.int8: MOE_I8, torch.uint8: MOE_Q4}.get(wt, a.dtype)
     if w_format == "frag":
-        a.w_dtype = MOE_BF16_FRAG
+        a.w_dtype = {torch.int8: MOE_I8_FRAG, torch.uint8: MOE_Q4_FRAG}.get(wt, MOE_BF16_FRAG)
     if wt in (torch.int8, torch.uint8):
         a.w_gate_scale, a.w_up_scale, a.w_down_scale = (t.data_ptr() for t in w_scales)
     a.scoring = _scoring_code(scoring)
@@ -350,7 +356,7 @@ def moe_layer_forward(x, w_router, w_gate, w_up, w_down, k, scoring, router_bias
     """The fused layer. Returns y [T, d], float32 unless ``y`` (or ``y_dtype``) is bfloat16.
     Optional outputs are written when passed. With quantised expert weights
     (moe_quantize_rows_i8 or moe_quantize_groups_q4 codes) pass their scale arrays as
-    w_scales; with fragment-major bf16 stacks (moe_pack_weights_frag) pass w_format="frag"."""
+    w_scales; with fragment-major stacks (moe_pack_weights_frag) pass w_format="frag"."""
     T, d = x.shape
     E, H, _ = w_gate.shape
     y = _empty((T, d), y_dtype, x) if y is None else y
@@ -417,16 +423,19 @@ def moe_quantize_groups_q4(w, q=None, qpar=None, stream=None):
 
 
 def moe_pack_weights_frag(w, out=None, stream=None):
-    """Fragment-major copy of the bf16 weights w [..., R, K] (R % 16 == 0, K % 32 == 0) for the
-    decode path (w_format="frag"): same shape and dtype, values reordered (moe_pack_weights_frag
-    in include/moe.h)."""
-    if w.dtype != torch.bfloat16 or w.dim() < 2 or not w.is_contiguous():
-        raise ValueError("w must be a contiguous bfloat16 tensor of at least two dimensions")
-    K = w.shape[-1]
-    rows = w.numel() // K if K else 0
+    """Fragment-major copy of decode weights for w_format="frag": w [..., R, K] bf16 values
+    (K % 32 == 0), int8 codes (moe_quantize_rows_i8, K % 128 == 0) or uint8 packed 4-bit codes
+    [..., R, K / 2] (moe_quantize_groups_q4, K % 128 == 0); R % 16 == 0. Returns the same shape
+    and dtype, bytes reordered (moe_pack_weights_frag in include/moe.h)."""
+    codes = {torch.bfloat16: MOE_BF16, torch.int8: MOE_I8, torch.uint8: MOE_Q4}
+    if w.dtype not in codes or w.dim() < 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous bfloat16, int8 or uint8 tensor of at least two "
+                         "dimensions")
+    K = w.shape[-1] * (2 if w.dtype == torch.uint8 else 1)
+    rows = w.numel() // w.shape[-1] if w.shape[-1] else 0
     out = torch.empty_like(w) if out is None else out
-    _need(out, "out", tuple(w.shape), torch.bfloat16)
-    _check(LIB.moe_pack_weights_frag(_ptr(w), rows, K, _ptr(out), _stream(stream)),
+    _need(out, "out", tuple(w.shape), w.dtype)
+    _check(LIB.moe_pack_weights_frag(_ptr(w), rows, K, codes[w.dtype], _ptr(out), _stream(stream)),
            "moe_pack_weights_frag")
     return out
 

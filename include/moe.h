@@ -78,10 +78,13 @@ enum moe_dtype {
      index, codes in the packed order of moe_quantize_groups_q4. Only as moe_layer_args.w_dtype,
      with bf16 activations, on the decode path. Added in ABI 3. */
   MOE_Q4 = 3,
-  /* bf16 expert weights in the fragment-major order of moe_pack_weights_frag (the same values,
+  /* bf16 expert weights, int8 codes (with MOE_I8's scales) or packed 4-bit codes (with MOE_Q4's
+     (scale, bias) pairs) in the fragment-major order of moe_pack_weights_frag (the same bytes,
      reordered). Only as moe_layer_args.w_dtype, with bf16 activations, on the decode path.
      Added in ABI 5. */
-  MOE_BF16_FRAG = 4
+  MOE_BF16_FRAG = 4,
+  MOE_I8_FRAG = 5,
+  MOE_Q4_FRAG = 6
 };
 
 enum moe_scoring {
@@ -241,10 +244,11 @@ typedef struct moe_layer_args {
      weight-streaming regime (T*k <= 2048, T*k <= 32*E, d and H multiples of 256): anything else
      returns MOE_ERR_UNSUPPORTED. Missing quantisation arrays: MOE_ERR_NULL. They must be 16-byte
      aligned.
-     w_dtype = MOE_BF16_FRAG (ABI 5): w_gate, w_up and w_down hold the bf16 stacks reordered by
-     moe_pack_weights_frag (rows = E * H, K = d for gate and up; rows = E * d, K = H for down);
-     the quantisation arrays are not read. Same regime and dtype conditions as above; the result
-     equals the plain bf16 layer's bit for bit. */
+     w_dtype = MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG (ABI 5): w_gate, w_up and w_down hold the
+     bf16 stacks, the int8 codes or the packed 4-bit codes reordered by moe_pack_weights_frag
+     (rows = E * H, K = d for gate and up; rows = E * d, K = H for down); the quantisation arrays
+     as for MOE_I8 and MOE_Q4 (unchanged, row-major), not read for MOE_BF16_FRAG. Same regime and
+     dtype conditions as above; the result equals that of the row-major weights bit for bit. */
   int32_t w_dtype;
   const void* w_gate_scale;   /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
   const void* w_up_scale;     /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
@@ -329,20 +333,28 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
                            uint32_t* qpar, void* stream);
 
 /*
- * Fragment-major copy of a bf16 weight matrix for the decode path (MOE_BF16_FRAG). The runtime on
- * the pages converts checkpoints once, offline, into its own storage (zonos2.cpp INTERNALS,
- * "Converting to GGUF"); this order is the library's own. For a row-major [rows, K] bf16 matrix w
- * (an expert stack is rows = E * N rows of length K), out holds the same rows * K values with
- *   w[r, k] at  ((r / 16) * (K / 32) + k / 32) * 512 + ((k % 32) / 8) * 128 + (r % 16) * 8 + k % 8
- * (integer division): every 16 x 32 block is 1 KiB, stored as the 64 sixteen-byte operands that
- * lanes 0..63 of a 16 x 16 x 32 matrix-core step take (lane l: row l % 16, eight consecutive k from
- * 8 (l / 16)), so a wave reads each step's weights as one contiguous kilobyte.
- * w, out: device bf16 bits, 16-byte aligned, not overlapping. rows % 16 == 0, rows >= 0 (0 is a
- * no-op), 32 <= K, K % 32 == 0, rows * K < 2^36; else MOE_ERR_SHAPE. NULL pointers (rows > 0):
- * MOE_ERR_NULL. Exact (a reordering). Asynchronous on `stream`, capturable, allocates nothing.
- * Added in ABI 5.
+ * Fragment-major copy of a decode weight matrix (MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG). The
+ * runtime on the pages converts checkpoints once, offline, into its own storage (zonos2.cpp
+ * INTERNALS, "Converting to GGUF"); this order is the library's own. w is a row-major matrix of
+ * `rows` rows with reduction length K (an expert stack is rows = E * N rows), stored as w_dtype:
+ * MOE_BF16 (bf16 bits, 2 K bytes per row), MOE_I8 (int8 codes of moe_quantize_rows_i8, K bytes
+ * per row) or MOE_Q4 (packed codes of moe_quantize_groups_q4, K / 2 bytes per row). out receives
+ * the same bytes with each slab of 16 rows (rows 16 b .. 16 b + 15) stored as consecutive
+ * 1024-byte chunks, bytes 16 l .. 16 l + 15 of chunk i (lane l = 0..63, g = l / 16) taken from row
+ * 16 b + l % 16:
+ *   MOE_BF16, MOE_Q4: row bytes 64 i + 16 g .. + 15 (bf16: the eight values k = 32 i + 8 g + 0..7,
+ *                     the operand that lane l of a 16 x 16 x 32 matrix-core step takes; q4: the
+ *                     four packed words of block i that hold k = 128 i + 32 c + 8 g + 0..7);
+ *   MOE_I8:           row bytes 128 (i / 2) + 32 g + 16 (i % 2) .. + 15 (codes at those k);
+ * i.e. the pieces in the order in which a wave of the decode kernels loads them, so that each load
+ * instruction reads one contiguous kilobyte. Scales and (scale, bias) pairs are not reordered.
+ * w, out: device, 16-byte aligned, not overlapping. rows % 16 == 0, rows >= 0 (0 is a no-op);
+ * K a multiple of 32 (MOE_BF16) or 128 (codes), K >= that multiple; rows * K < 2^36; else
+ * MOE_ERR_SHAPE. Other w_dtype: MOE_ERR_UNSUPPORTED. NULL pointers (rows > 0): MOE_ERR_NULL.
+ * Exact (a reordering). Asynchronous on `stream`, capturable, allocates nothing. Added in ABI 5.
  */
-int moe_pack_weights_frag(const void* w, int64_t rows, int K, void* out, void* stream);
+int moe_pack_weights_frag(const void* w, int64_t rows, int K, int w_dtype, void* out,
+                          void* stream);
 
 /*
  * Graph ladder (serving-side decode). zonos2.cpp INTERNALS, "Performance": the decode graph is

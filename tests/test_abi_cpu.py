@@ -294,9 +294,18 @@ def test_binding_checks_shapes_before_calling():
 
 def test_frag_weights_validation():
     L = moe.LIB
-    # moe_pack_weights_frag: rows % 16, K % 32, K >= 32, rows * K < 2^36; NULL; alignment
-    pack = lambda w=FAKE, rows=32, K=64, out=FAKE: L.moe_pack_weights_frag(w, rows, K, out, None)
+    # moe_pack_weights_frag: rows % 16, K % 32 (bf16) or 128 (codes), rows * K < 2^36; NULL;
+    # alignment; stored type
+    pack = lambda w=FAKE, rows=32, K=64, out=FAKE, dt=moe.MOE_BF16: L.moe_pack_weights_frag(
+        w, rows, K, dt, out, None)
     assert pack(rows=0) == moe.MOE_OK
+    assert pack(dt=moe.MOE_F32) == moe.MOE_ERR_UNSUPPORTED
+    assert pack(dt=moe.MOE_BF16_FRAG) == moe.MOE_ERR_UNSUPPORTED
+    for dt in (moe.MOE_I8, moe.MOE_Q4):
+        assert pack(dt=dt) == moe.MOE_ERR_SHAPE                      # K = 64: not a multiple of 128
+        assert pack(dt=dt, K=192) == moe.MOE_ERR_SHAPE
+        assert pack(dt=dt, K=256, rows=0) == moe.MOE_OK
+        assert pack(dt=dt, K=256, out=None) == moe.MOE_ERR_NULL
     assert pack(rows=0, w=None) == moe.MOE_OK
     assert pack(rows=-16) == moe.MOE_ERR_SHAPE
     assert pack(rows=24) == moe.MOE_ERR_SHAPE
@@ -317,6 +326,16 @@ def test_frag_weights_validation():
     assert run(_args(**{**fr, "dtype": 0})) == moe.MOE_ERR_UNSUPPORTED          # fp32 activations
     assert run(_args(**{**fr, "d": 128, "H": 128})) == moe.MOE_ERR_UNSUPPORTED  # not streaming
     assert run(_args(**{**fr, "T": 2048, "k": 2}), n=1 << 40) == moe.MOE_ERR_UNSUPPORTED  # prefill
+    # the quantised fragment-major types need their scale arrays, like MOE_I8 and MOE_Q4
+    for wd in (moe.MOE_I8_FRAG, moe.MOE_Q4_FRAG):
+        q = dict(fr, w_dtype=wd, w_gate_scale=FAKE.value, w_up_scale=FAKE.value,
+                 w_down_scale=FAKE.value)
+        assert run(_args(**q), n=0) == moe.MOE_ERR_WORKSPACE
+        assert run(_args(**{**q, "w_up_scale": None})) == moe.MOE_ERR_NULL
+        assert run(_args(**{**q, "w_gate_scale": MISALIGNED.value})) == moe.MOE_ERR_SHAPE
+        assert run(_args(**{**q, "dtype": 0})) == moe.MOE_ERR_UNSUPPORTED
+        assert run(_args(**{**q, "T": 2048, "k": 2}), n=1 << 40) == moe.MOE_ERR_UNSUPPORTED
+    assert run(_args(**{**fr, "w_dtype": 7})) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_python_pack_wrapper_checks_its_input():

@@ -1,8 +1,9 @@
-"""Fragment-major bf16 expert weights (MOE_BF16_FRAG) on the decode path: moe_pack_weights_frag
-bit-exact against the oracle's order, and moe_layer_forward on packed stacks (packed by the
-oracle, so the layer test does not depend on the GPU packer) equal to the plain bf16 layer bit
-for bit (the same values in the same lanes and the same sum order), through the workspace entry
-point, the no-alloc entry point and the graph ladder; plus the oracle check of one workload."""
+"""Fragment-major expert weights on the decode path (MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG):
+moe_pack_weights_frag bit-exact against the oracle's order for bf16 values, int8 codes and packed
+4-bit codes, and moe_layer_forward on reordered stacks (reordered by the oracle, so the layer tests
+do not depend on the GPU packer) equal bit for bit to the same layer on the row-major stacks (the
+same bytes reach the same lanes in the same sum order), through the workspace entry point, the
+no-alloc entry point and the graph ladder; plus the oracle check of one workload."""
 import dataclasses
 
 import numpy as np
@@ -148,6 +149,103 @@ def test_frag_ladder_equals_plain_calls():
             assert torch.equal(y[:T], ref), T
     finally:
         lad.close()
+
+
+# ------------------------------------------------------------------ int8 and 4-bit codes
+
+def _quantised(inp, fmt):
+    """Oracle codes of the three stacks (row-major, as the quantisers write them) and their scale
+    arrays, as host arrays."""
+    codes, scales = {}, []
+    for key in KEYS:
+        w = getattr(inp, key)
+        if fmt == "i8":
+            q, s = orc.quantize_rows_i8_ref(w)
+            codes[key], sc = q, s
+        else:
+            q, s, b = orc.quantize_groups_q4_ref(w)
+            codes[key], sc = orc.pack_q4_ref(q), orc.pack_q4_params_ref(s, b).view(np.int32)
+        scales.append(sc)
+    return codes, scales
+
+
+def _run_codes(inp, dv, codes, scales, w_format):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    outs = _outs(inp)
+    cd = {key: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for key, v in codes.items()}
+    sd = tuple(torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in scales)
+    y = moe.moe_layer_forward(dv["x"], dv["w_router"], cd["w_gate"], cd["w_up"], cd["w_down"],
+                              inp.k, inp.scoring, router_bias=dv["router_bias"],
+                              sel_bias=dv["sel_bias"], w_scales=sd, w_format=w_format, **outs)
+    torch.cuda.synchronize()
+    res = {key: v.cpu().numpy() for key, v in outs.items()}
+    res["y"] = y.cpu().numpy()
+    return res
+
+
+def _codes_case(inp, fmt):
+    dv = upload(inp)
+    codes, scales = _quantised(inp, fmt)
+    plain = _run_codes(inp, dv, codes, scales, "plain")
+    frag = {key: orc.pack_frag_ref(v, fmt) for key, v in codes.items()}
+    res = _run_codes(inp, dv, frag, scales, "frag")
+    _same(res, plain)
+    return res
+
+
+@pytest.mark.parametrize("fmt", ["i8", "q4"])
+@pytest.mark.parametrize("shape", [(3, 48, 256), (16, 2816, 2048), (64, 512, 1024), (1, 16, 128)])
+def test_pack_frag_codes_bit_exact(fmt, shape):
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    rng = np.random.default_rng(sum(shape) + len(fmt))
+    if fmt == "i8":
+        host = rng.integers(-127, 128, size=shape).astype(np.int8)
+    else:
+        host = rng.integers(0, 256, size=shape[:-1] + (shape[-1] // 2,)).astype(np.uint8)
+    got = moe.moe_pack_weights_frag(torch.from_numpy(host).to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), orc.pack_frag_ref(host, fmt))
+
+
+@pytest.mark.parametrize("fmt", ["i8", "q4"])
+@pytest.mark.parametrize("name", ["zonos2-decode", "zonos3mini-decode-cfg", "zonos2-layer26-decode"])
+def test_frag_codes_layer_equals_row_major_codes(fmt, name):
+    _codes_case(gen.make_inputs(name), fmt)
+
+
+@pytest.mark.parametrize("fmt", ["i8", "q4"])
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_frag_codes_edge_cases(fmt, case):
+    name, T, d, E, k, H, scoring, sbv, rb = case
+    router_bias = None
+    if rb == "hot5":
+        router_bias = np.full(E, -30.0, np.float32)
+        router_bias[5] = 30.0
+    inp = gen.make_inputs_custom(T, d, E, k, H, scoring, "bf16", seed=11 * T + E + k,
+                                 sel_bias_var=sbv, router_bias=router_bias)
+    _codes_case(inp, fmt)
+
+
+def test_frag_codes_with_gpu_quantiser_and_packer():
+    """The library's quantisers and packer end to end: equal to the oracle-prepared codes."""
+    import torch
+    from expert_routing_grouped_moe_amd import moe
+    inp = gen.make_inputs("zonos3mini-decode-cfg")
+    dv = upload(inp)
+    for fmt, qfn in (("i8", moe.moe_quantize_rows_i8), ("q4", moe.moe_quantize_groups_q4)):
+        codes, scales = _quantised(inp, fmt)
+        ref = _run_codes(inp, dv, {key: orc.pack_frag_ref(v, fmt) for key, v in codes.items()},
+                         scales, "frag")
+        g = {key: qfn(dv[key]) for key in KEYS}
+        fw = {key: moe.moe_pack_weights_frag(g[key][0]) for key in KEYS}
+        y = moe.moe_layer_forward(dv["x"], dv["w_router"], fw["w_gate"], fw["w_up"], fw["w_down"],
+                                  inp.k, inp.scoring, router_bias=dv["router_bias"],
+                                  sel_bias=dv["sel_bias"],
+                                  w_scales=tuple(g[key][1] for key in KEYS), w_format="frag")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref["y"])
 
 
 def test_frag_rejected_outside_decode_path():
