@@ -103,11 +103,16 @@ def _hip():
     return lib
 
 
+# fragment-major weight options and the row-major storage they reorder
+FRAG_BASE = {"frag": "native", "int8-frag": "int8", "q4-frag": "q4"}
+
+
 def algorithmic(inp, counts, weights="native"):
     """Bytes and FLOPs the step must move/do (touched experts only; intermediates excluded).
     int8 expert weights: one byte per weight plus the fp32 row scales of the touched experts;
-    q4: half a byte per weight plus one 4-byte (scale, bias) pair per group of 64; frag: the bf16
-    weights reordered, two bytes per weight."""
+    q4: half a byte per weight plus one 4-byte (scale, bias) pair per group of 64; the
+    fragment-major orders move the same bytes as the row-major ones."""
+    weights = FRAG_BASE.get(weights, weights)
     T, d, E, k, H = inp.T, inp.d, inp.E, inp.k, inp.H
     ab = 2 if inp.dtype == "bf16" else 4             # activations and router weights
     wb = {"int8": 1, "q4": 0.5}.get(weights, ab)     # expert weights
@@ -242,7 +247,8 @@ def dominant_kernel(inp, weights="native"):
         return "ffn_f32_kernel<true>"
     if T * k <= 2048 and d % 256 == 0 and H % 256 == 0 and T * k <= 32 * E:
         maxg = 2 if (H // 16) * E <= 2048 else 1
-        return "ffn_stream_kernel<true, %d, %d>" % (maxg, {"native": 0, "int8": 1, "q4": 2, "frag": 3}[weights])
+        return "ffn_stream_kernel<true, %d, %d>" % (maxg, {"native": 0, "int8": 1, "q4": 2, "frag": 4,
+                                                           "int8-frag": 5, "q4-frag": 6}[weights])
     return gemm_kernel_name(T * k, E, True)
 
 
@@ -336,16 +342,18 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
     x = up("x")
     wr = up("w_router")
     base = {key: up(key) for key in ("w_gate", "w_up", "w_down")}
-    quant = weights in ("int8", "q4")
-    w_format = "frag" if weights == "frag" else "plain"
-    if w_format == "frag":
-        base = {key: moe.moe_pack_weights_frag(t) for key, t in base.items()}
-        torch.cuda.synchronize()
+    stored = FRAG_BASE.get(weights, weights)
+    quant = stored in ("int8", "q4")
+    w_format = "frag" if weights in FRAG_BASE else "plain"
     if quant:
-        qfn = moe.moe_quantize_rows_i8 if weights == "int8" else moe.moe_quantize_groups_q4
+        qfn = moe.moe_quantize_rows_i8 if stored == "int8" else moe.moe_quantize_groups_q4
         qs = {key: qfn(t) for key, t in base.items()}
         base = {key: v[0] for key, v in qs.items()}
         base.update({key + "_scale": v[1] for key, v in qs.items()})
+        torch.cuda.synchronize()
+    if w_format == "frag":
+        for key in ("w_gate", "w_up", "w_down"):
+            base[key] = moe.moe_pack_weights_frag(base[key])
         torch.cuda.synchronize()
     wbytes = sum(t.numel() * t.element_size() for t in base.values())
     ncopies = 1 if warm else max(2, min(16, math.ceil(1.6e9 / wbytes)))
@@ -486,7 +494,9 @@ def run_workload(name, steps, warmup, weights="native", warm=False, eager=False,
                    "weights": "cold (rotating %d copies)" % ncopies if ncopies > 1 else "warm (1 copy)",
                    "expert_weights": {"int8": "int8, fp32 row scales",
                                       "q4": "4-bit affine, groups of 64, bf16 scale and bias",
-                                      "frag": "bf16, fragment-major (moe_pack_weights_frag)"
+                                      "frag": "bf16, fragment-major (moe_pack_weights_frag)",
+                                      "int8-frag": "int8, fp32 row scales, codes fragment-major",
+                                      "q4-frag": "4-bit affine, groups of 64, codes fragment-major"
                                       }.get(weights, inp.dtype),
                    "timing": ("host launches" if eager else
                               "HIP graph replay: cycles of one step per weight copy, single "
@@ -532,12 +542,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one weight copy (cache-warm, labelled)")
-    ap.add_argument("--weights", choices=("native", "int8", "q4", "frag"), default="native",
+    ap.add_argument("--weights", choices=("native", "int8", "q4", "frag", "int8-frag", "q4-frag"),
+                    default="native",
                     help="expert weights as given (bf16/fp32), int8 codes with per-row scales "
                          "(moe_quantize_rows_i8), 4-bit affine codes in groups of 64 "
-                         "(moe_quantize_groups_q4) or bf16 reordered fragment-major "
-                         "(moe_pack_weights_frag); these on decode shapes only, headline workload "
-                         "only")
+                         "(moe_quantize_groups_q4), or any of these three reordered fragment-major "
+                         "(moe_pack_weights_frag); all but the first on decode shapes only, "
+                         "headline workload only")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
