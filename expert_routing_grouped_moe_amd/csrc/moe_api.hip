@@ -254,7 +254,9 @@ int moe_pack_weights_frag(const void* w, int64_t rows, int K, int w_dtype, void*
                           void* stream) {
   if (w_dtype != MOE_BF16 && w_dtype != MOE_I8 && w_dtype != MOE_Q4) return MOE_ERR_UNSUPPORTED;
   const int kmul = w_dtype == MOE_BF16 ? 32 : 128;
-  if (rows < 0 || rows % 16 != 0 || K < kmul || K % kmul != 0) return MOE_ERR_SHAPE;
+  // K <= 2^20 keeps a row's bytes (2 K for bf16) inside an int
+  if (rows < 0 || rows % 16 != 0 || K < kmul || K % kmul != 0 || K > (1 << 20))
+    return MOE_ERR_SHAPE;
   if (rows * K >= kMaxQuantElems) return MOE_ERR_SHAPE;
   if (rows == 0) return MOE_OK;
   if (!w || !out) return MOE_ERR_NULL;

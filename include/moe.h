@@ -349,8 +349,8 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
  * i.e. the pieces in the order in which a wave of the decode kernels loads them, so that each load
  * instruction reads one contiguous kilobyte. Scales and (scale, bias) pairs are not reordered.
  * w, out: device, 16-byte aligned, not overlapping. rows % 16 == 0, rows >= 0 (0 is a no-op);
- * K a multiple of 32 (MOE_BF16) or 128 (codes), K >= that multiple; rows * K < 2^36; else
- * MOE_ERR_SHAPE. Other w_dtype: MOE_ERR_UNSUPPORTED. NULL pointers (rows > 0): MOE_ERR_NULL.
+ * K a multiple of 32 (MOE_BF16) or 128 (codes), that multiple <= K <= 2^20; rows * K < 2^36;
+ * else MOE_ERR_SHAPE. Other w_dtype: MOE_ERR_UNSUPPORTED. NULL pointers (rows > 0): MOE_ERR_NULL.
  * Exact (a reordering). Asynchronous on `stream`, capturable, allocates nothing. Added in ABI 5.
  */
 int moe_pack_weights_frag(const void* w, int64_t rows, int K, int w_dtype, void* out,

@@ -312,6 +312,8 @@ def test_frag_weights_validation():
     assert pack(K=48) == moe.MOE_ERR_SHAPE
     assert pack(K=0) == moe.MOE_ERR_SHAPE
     assert pack(rows=1 << 26, K=1 << 10) == moe.MOE_ERR_SHAPE
+    assert pack(rows=16, K=(1 << 20) + 32) == moe.MOE_ERR_SHAPE       # past the row-length limit
+    assert pack(rows=16, K=1 << 30) == moe.MOE_ERR_SHAPE
     assert pack(w=None) == moe.MOE_ERR_NULL
     assert pack(out=None) == moe.MOE_ERR_NULL
     assert pack(w=MISALIGNED) == moe.MOE_ERR_SHAPE
