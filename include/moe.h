@@ -31,8 +31,9 @@
  *                asynchronous: it only enqueues kernels. No call reads device memory on the host,
  *                synchronises, or allocates, so every call may be captured into a HIP graph.
  *                Launch shapes depend only on the scalar arguments, never on routing results.
- *   Dtypes       `dtype` (MOE_F32 or MOE_BF16) is the type of x and of every weight matrix.
- *                Logits, biases, routing weights and expert outputs are always fp32; y is fp32
+ *   Dtypes       `dtype` (MOE_F32 or MOE_BF16) is the type of x and of every weight matrix
+ *                (the layer's expert stacks may instead be in a prepared decode format:
+ *                moe_layer_args.w_dtype, moe_quantize_*, moe_pack_weights_frag). Logits, biases, routing weights and expert outputs are always fp32; y is fp32
  *                unless a `y_dtype` argument asks for bf16 (the sum is formed in fp32 and
  *                rounded once to nearest even).
  *   Errors       A negative return means nothing was enqueued, except MOE_ERR_HIP, which reports
