@@ -44,10 +44,15 @@ bf16 (the model's dtype):
   q_i = clamp(rint(fl32(fl32(w_i - b) / s)), 0, 15)   (ties to even; s = 0 gives q = 0),
 and the layer computes with the weights s * q + b exactly. bf16() is round-to-nearest-even.
 
+Storage orders (the library's own, no arithmetic): the packed 4-bit code order and the
+fragment-major order of bf16 values, int8 codes or packed 4-bit codes (pack_frag_ref), a pure
+reordering of bytes so that each load instruction of the decode kernels reads one kilobyte.
+
 Pins (checked by the CPU tests against values the mathematics fixes, not against this code):
 brute-force selection, closed-form softmax weights, exact fp32 rounding cases, dispatch
-invariants, the E=1 layer equal to a dense SwiGLU FFN computed with torch's silu, and the full
-layer equal to a dense run-every-expert brute force.
+invariants, the E=1 layer equal to a dense SwiGLU FFN computed with torch's silu, the full layer
+equal to a dense run-every-expert brute force, hand-encoded packed words, and the storage orders
+read back the way the matrix cores take their operands, summed per row, equal to plain products.
 """
 from __future__ import annotations
 
