@@ -562,8 +562,9 @@ int route_split_slice(int d) {
 
 int route_split_ks(int T, int d, int E) {
   // worth a second launch only when every fused block would pull a large router matrix
-  // (>= 128 KB of bf16: 64 experts x 1024 measured 9.4 us split against 11.7 us fused; 16 x 2048
-  // measured 8.7 us split against 7.4 us fused)
+  // (>= 128 KB of bf16: 64 experts x 1024 measured 9.4 us split against 11.7 us fused, and with
+  // the fused kernel's whole-line copies still 39.8 against 40.2 us per graph-replayed ZONOS3-Mini
+  // decode step; 16 x 2048 measured 8.7 us split against 7.4 us fused)
   if (T > kRouteSplitMaxT || static_cast<long long>(E) * d < 65536) return 0;
   const int slice = route_split_slice(d);
   return (d + slice - 1) / slice;
