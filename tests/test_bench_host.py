@@ -59,6 +59,13 @@ def test_algorithmic_q4(bench):
     assert a["gu_bytes"] == 393216 + 49152 + 4096 + 8192
 
 
+def test_algorithmic_fragment_major_equals_row_major(bench):
+    # the fragment-major orders move exactly the bytes of the storage they reorder
+    for frag, base in (("frag", "native"), ("int8-frag", "int8"), ("q4-frag", "q4")):
+        assert bench.algorithmic(_inp("bf16"), COUNTS, frag) == \
+            bench.algorithmic(_inp("bf16"), COUNTS, base)
+
+
 def test_algorithmic_fp32(bench):
     a = bench.algorithmic(_inp("f32"), COUNTS)
     assert a["gu_bytes"] == 2 * 1572864 + 2 * 4096 + 2 * 8192
@@ -119,6 +126,10 @@ def test_dominant_kernel_names(bench):
     assert bench.dominant_kernel(mk(64, 2048, 16, 1, 2816)) == "ffn_stream_kernel<true, 1, 0>"
     assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512)) == "ffn_stream_kernel<true, 2, 0>"
     assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512), "q4") == "ffn_stream_kernel<true, 2, 2>"
+    # fragment-major: the weight-format template argument carries the order flag (4)
+    assert bench.dominant_kernel(mk(64, 2048, 16, 1, 2816), "frag") == "ffn_stream_kernel<true, 1, 4>"
+    assert bench.dominant_kernel(mk(64, 2048, 16, 1, 2816), "int8-frag") == "ffn_stream_kernel<true, 1, 5>"
+    assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512), "q4-frag") == "ffn_stream_kernel<true, 2, 6>"
     # prefill shapes: the grouped GEMM, wide tiles once experts average 256 rows
     assert bench.dominant_kernel(mk(8192, 2048, 16, 1, 2816)).startswith("gemm_dma_kernel<true, 256, 256")
     assert bench.dominant_kernel(mk(4096, 1024, 64, 2, 512)).startswith("gemm_dma_kernel<true, 128, 256")
