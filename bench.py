@@ -249,16 +249,18 @@ def dominant_kernel(inp, weights="native"):
         maxg = 2 if (H // 16) * E <= 2048 else 1
         return "ffn_stream_kernel<true, %d, %d>" % (maxg, {"native": 0, "int8": 1, "q4": 2, "frag": 4,
                                                            "int8-frag": 5, "q4-frag": 6}[weights])
-    return gemm_kernel_name(T * k, E, True)
+    # fragment-major bf16 stacks run the GEMM's fragment-major variant
+    return gemm_kernel_name(T * k, E, True, frag=weights == "frag")
 
 
-def gemm_kernel_name(rows, E, gateup):
-    """Name of the grouped-GEMM instantiation for `rows` assignment rows over E experts."""
+def gemm_kernel_name(rows, E, gateup, frag=False):
+    """Name of the grouped-GEMM instantiation for `rows` assignment rows over E experts (the last
+    template argument: weight stacks fragment-major)."""
     if rows >= 256 * E:     # experts average a full 256-row tile: the wide tiles
-        return ("gemm_dma_kernel<true, 256, 256, 2, 64, 64>" if gateup
-                else "gemm_dma_kernel<false, 256, 128, 3, 64, 32>")
-    return ("gemm_dma_kernel<true, 128, 256, 3, 64, 32>" if gateup
-            else "gemm_dma_kernel<false, 128, 256, 3, 64, 32>")
+        shape = "true, 256, 256, 2, 64, 64" if gateup else "false, 256, 128, 3, 64, 32"
+    else:
+        shape = "true, 128, 256, 3, 64, 32" if gateup else "false, 128, 256, 3, 64, 32"
+    return "gemm_dma_kernel<%s, %s>" % (shape, "true" if frag else "false")
 
 
 def ep_shard_timing(gpus=8, calls=48):
@@ -547,8 +549,8 @@ def main():
                     help="expert weights as given (bf16/fp32), int8 codes with per-row scales "
                          "(moe_quantize_rows_i8), 4-bit affine codes in groups of 64 "
                          "(moe_quantize_groups_q4), or any of these three reordered fragment-major "
-                         "(moe_pack_weights_frag); all but the first on decode shapes only, "
-                         "headline workload only")
+                         "(moe_pack_weights_frag); the codes on decode shapes only; headline "
+                         "workload only")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of graph replay (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -122,7 +122,12 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool GATEUP, int BM, int BN, int RING, int WROWS, int BK>
+// BFRAG: the weight stacks (B) are stored fragment-major (moe_pack_weights_frag): each 16-row x
+// 32-k fragment is one contiguous kilobyte, lane l's piece (row l % 16, k 8 (l / 16) .. + 7) at
+// 16 l. Such a fragment is copied as one of the step's 1 KB chunks and lands in LDS already in the
+// order the MFMA reads it (lane l's piece at 16 l), so those reads need no swizzle; the products
+// and their order are the same as with row-major weights.
+template <bool GATEUP, int BM, int BN, int RING, int WROWS, int BK, bool BFRAG>
 __global__ __launch_bounds__(BM / WROWS * (BN / 64) * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
@@ -166,15 +171,26 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
   // the step (A rows first, then B rows); lane i fills row RPC j + i / PCS, position i % PCS
   const uint16_t* src[CPW];
   int ldsoff[CPW];
+  bool fragc[CPW];                          // a fragment-major weight chunk (16 k per K step)
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int j = wave + NW * c;
     const int r = RPC * j + lane / PCS;     // row of the step tile (A: < BM)
     const int pos = lane % PCS;
+    fragc[c] = BFRAG && j >= CHA;
     if (j < CHA) {
       const int pr = ti.row0 + (r < ti.rows ? r : 0);
       const long long arow = GATEUP ? static_cast<long long>(sorted_rows[pr] / k) : pr;
       src[c] = A + arow * K + ((pos ^ swz<BK>(r)) * 8);
+    } else if constexpr (BFRAG) {
+      // chunk jb of the step's weight rows: 16-row block jb / (BK / 32), its fragment jb % (BK /
+      // 32) of the step; N % 16 == 0, so a block past the last row reads the last block
+      const int jb = j - CHA;
+      const int rb16 = 16 * (jb / (BK / 32));
+      const int f0 = min(n0 + (GATEUP ? (rb16 % FEAT) : rb16), N - 16);
+      const uint16_t* wsrc = (GATEUP && rb16 >= FEAT) ? W1 : W0;
+      const long long blk = (static_cast<long long>(ti.e) * N + f0) / 16;
+      src[c] = wsrc + (blk * (K / 32) + jb % (BK / 32)) * 512 + 8 * lane;
     } else {
       const int rb = r - BM;
       const int f = min(n0 + (GATEUP ? (rb % FEAT) : rb), N - 1);
@@ -189,8 +205,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     const int slot = kt % RING;
     const int k0 = min(kt, nk - 1) * BK;    // prologue past the end: re-read the last step
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
-      dma16(src[c] + k0, ring0 + 2u * static_cast<uint32_t>(slot * STAGE + ldsoff[c]));
+    for (int c = 0; c < CPW; ++c)   // a fragment-major chunk advances 512 elements per 32 k
+      dma16(src[c] + (fragc[c] ? 16 * k0 : k0),
+            ring0 + 2u * static_cast<uint32_t>(slot * STAGE + ldsoff[c]));
   };
 
   int brow[NBK];
@@ -214,7 +231,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
 #pragma unroll
   for (int cb = 0; cb < NBK; ++cb) {
     const int r = brow[cb] + l16;
-    boff[cb] = BM * BK + r * BK + ((q ^ swz<BK>(r)) * 8);
+    boff[cb] = BFRAG ? BM * BK + (brow[cb] / 16) * (BK / 32) * 512 + 8 * lane
+                     : BM * BK + r * BK + ((q ^ swz<BK>(r)) * 8);
   }
 
   f32x4 acc[MB][NBK];
@@ -232,7 +250,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) af[mb] = load16(st + (aoff[mb] ^ x));
 #pragma unroll
-      for (int cb = 0; cb < NBK; ++cb) bf[cb] = load16(st + (boff[cb] ^ x));
+      for (int cb = 0; cb < NBK; ++cb)
+        bf[cb] = load16(st + (BFRAG ? boff[cb] + 16 * x : (boff[cb] ^ x)));
       if constexpr (!GATEUP) {              // h is fp16: the bf16 weights go to fp16
 #pragma unroll
         for (int cb = 0; cb < NBK; ++cb) bf[cb] = bf16x8_to_f16x8(bf[cb]);
@@ -737,12 +756,17 @@ hipError_t launch_streaming(const uint16_t* x, const void* wg, const void* wu, c
 template <bool GATEUP, int BM, int BN, int RING, int BK>
 hipError_t launch_gemm(int rows, int E, hipStream_t s, const StageMarks& marks,
                        const uint16_t* A, const void* W0, const void* W1, int K, int N, int k,
-                       const RowSource& rs, uint16_t* h, const DownArgs& down) {
+                       const RowSource& rs, uint16_t* h, const DownArgs& down, bool bfrag) {
   constexpr int NT = BM / kTileWaveRows * (BN / 64) * kWave;
   constexpr int FEAT = GATEUP ? BN / 2 : BN;
   const int ntn = (N + FEAT - 1) / FEAT;
   const long long grid = prefill_grid(max_tiles(rows, E, BM), ntn);
-  return launch_marked(gemm_dma_kernel<GATEUP, BM, BN, RING, kTileWaveRows, BK>,
+  if (bfrag)
+    return launch_marked(gemm_dma_kernel<GATEUP, BM, BN, RING, kTileWaveRows, BK, true>,
+                         dim3(static_cast<unsigned>(grid)), dim3(NT), s, marks, A,
+                         static_cast<const uint16_t*>(W0), static_cast<const uint16_t*>(W1), K,
+                         N, E, k, rs.offsets, rs.sorted_rows, h, down);
+  return launch_marked(gemm_dma_kernel<GATEUP, BM, BN, RING, kTileWaveRows, BK, false>,
                        dim3(static_cast<unsigned>(grid)), dim3(NT), s, marks, A,
                        static_cast<const uint16_t*>(W0), static_cast<const uint16_t*>(W1), K, N,
                        E, k, rs.offsets, rs.sorted_rows, h, down);
@@ -775,20 +799,24 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const void* wg, const void* wu, co
       default: return hipErrorInvalidValue;
     }
   }
-  // quantised weights: weight-streaming shapes only (checked by the callers)
-  if (qw.fmt != kWBf16) return hipErrorInvalidValue;
+  // quantised weights: weight-streaming shapes only (checked by the callers); bf16 weights
+  // row-major or fragment-major
+  if (qw.fmt != kWBf16 && qw.fmt != (kWBf16 | kWFragMajor)) return hipErrorInvalidValue;
+  const bool bfrag = qw.fmt != kWBf16;
   // grouped GEMM over the dispatch order; 1-D grids sized for the worst-case tile count
   const StageMarks no_marks{};
   if (prefill_wide_tiles(rows, E, kTileM)) {
-    err = launch_gemm<true, 256, 256, 2, 64>(rows, E, s, gu, x, wg, wu, d, H, k, rs, h, none);
+    err = launch_gemm<true, 256, 256, 2, 64>(rows, E, s, gu, x, wg, wu, d, H, k, rs, h, none,
+                                             bfrag);
     if (err != hipSuccess) return err;
     return launch_gemm<false, 256, 128, 3, 32>(rows, E, s, no_marks, h, wd, nullptr, H, d, k, rs,
-                                               nullptr, down);
+                                               nullptr, down, bfrag);
   }
-  err = launch_gemm<true, 128, 256, 3, 32>(rows, E, s, gu, x, wg, wu, d, H, k, rs, h, none);
+  err = launch_gemm<true, 128, 256, 3, 32>(rows, E, s, gu, x, wg, wu, d, H, k, rs, h, none,
+                                           bfrag);
   if (err != hipSuccess) return err;
   return launch_gemm<false, 128, 256, 3, 32>(rows, E, s, no_marks, h, wd, nullptr, H, d, k, rs,
-                                             nullptr, down);
+                                             nullptr, down, bfrag);
 }
 
 }  // namespace moe

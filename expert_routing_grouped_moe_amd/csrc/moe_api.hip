@@ -302,8 +302,9 @@ int moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes, void* 
     const bool frag = w_dtype == MOE_BF16_FRAG || w_dtype == MOE_I8_FRAG || w_dtype == MOE_Q4_FRAG;
     const int base = w_dtype == MOE_BF16_FRAG ? MOE_BF16
                      : (w_dtype == MOE_I8_FRAG ? MOE_I8 : (w_dtype == MOE_Q4_FRAG ? MOE_Q4 : w_dtype));
+    // fragment-major bf16 weights serve both kernel families; the codes, the decode path only
     if ((base != MOE_BF16 && base != MOE_I8 && base != MOE_Q4) || dtype != MOE_BF16 ||
-        !moe::ffn_bf16_streaming(T, d, E, H, k))
+        (base != MOE_BF16 && !moe::ffn_bf16_streaming(T, d, E, H, k)))
       return MOE_ERR_UNSUPPORTED;
     const int fmt = (base == MOE_I8 ? moe::kWI8 : (base == MOE_Q4 ? moe::kWQ4 : moe::kWBf16)) |
                     (frag ? moe::kWFragMajor : 0);

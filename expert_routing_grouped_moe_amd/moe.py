@@ -423,7 +423,8 @@ def moe_quantize_groups_q4(w, q=None, qpar=None, stream=None):
 
 
 def moe_pack_weights_frag(w, out=None, stream=None):
-    """Fragment-major copy of decode weights for w_format="frag": w [..., R, K] bf16 values
+    """Fragment-major copy of expert weights for w_format="frag" (bf16: every shape; codes: the
+    decode path): w [..., R, K] bf16 values
     (K % 32 == 0), int8 codes (moe_quantize_rows_i8, K % 128 == 0) or uint8 packed 4-bit codes
     [..., R, K / 2] (moe_quantize_groups_q4, K % 128 == 0); R % 16 == 0. Returns the same shape
     and dtype, bytes reordered (moe_pack_weights_frag in include/moe.h)."""

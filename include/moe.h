@@ -81,8 +81,8 @@ enum moe_dtype {
   MOE_Q4 = 3,
   /* bf16 expert weights, int8 codes (with MOE_I8's scales) or packed 4-bit codes (with MOE_Q4's
      (scale, bias) pairs) in the fragment-major order of moe_pack_weights_frag (the same bytes,
-     reordered). Only as moe_layer_args.w_dtype, with bf16 activations, on the decode path.
-     Added in ABI 5. */
+     reordered). Only as moe_layer_args.w_dtype, with bf16 activations; MOE_BF16_FRAG on every
+     shape, the codes on the decode path only. Added in ABI 5. */
   MOE_BF16_FRAG = 4,
   MOE_I8_FRAG = 5,
   MOE_Q4_FRAG = 6
@@ -248,8 +248,10 @@ typedef struct moe_layer_args {
      w_dtype = MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG (ABI 5): w_gate, w_up and w_down hold the
      bf16 stacks, the int8 codes or the packed 4-bit codes reordered by moe_pack_weights_frag
      (rows = E * H, K = d for gate and up; rows = E * d, K = H for down); the quantisation arrays
-     as for MOE_I8 and MOE_Q4 (unchanged, row-major), not read for MOE_BF16_FRAG. Same regime and
-     dtype conditions as above; the result equals that of the row-major weights bit for bit. */
+     as for MOE_I8 and MOE_Q4 (unchanged, row-major), not read for MOE_BF16_FRAG. dtype must be
+     MOE_BF16; MOE_I8_FRAG and MOE_Q4_FRAG need the weight-streaming regime above, MOE_BF16_FRAG
+     serves every shape (the grouped GEMM reads each fragment as one of its 1 KB copies). The
+     result equals that of the row-major weights bit for bit. */
   int32_t w_dtype;
   const void* w_gate_scale;   /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
   const void* w_up_scale;     /* MOE_I8: float [E, H];  MOE_Q4: uint32 [E, H, d / 64] */
@@ -334,7 +336,7 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
                            uint32_t* qpar, void* stream);
 
 /*
- * Fragment-major copy of a decode weight matrix (MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG). The
+ * Fragment-major copy of an expert weight matrix (MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG). The
  * runtime on the pages converts checkpoints once, offline, into its own storage (zonos2.cpp
  * INTERNALS, "Converting to GGUF"); this order is the library's own. w is a row-major matrix of
  * `rows` rows with reduction length K (an expert stack is rows = E * N rows), stored as w_dtype:
@@ -348,7 +350,8 @@ int moe_quantize_groups_q4(const void* w, int64_t rows, int K, int dtype, uint8_
  *                     four packed words of block i that hold k = 128 i + 32 c + 8 g + 0..7);
  *   MOE_I8:           row bytes 128 (i / 2) + 32 g + 16 (i % 2) .. + 15 (codes at those k);
  * i.e. the pieces in the order in which a wave of the decode kernels loads them, so that each load
- * instruction reads one contiguous kilobyte. Scales and (scale, bias) pairs are not reordered.
+ * instruction reads one contiguous kilobyte (bf16: also one K step's copy of 16 weight rows in the
+ * prefill GEMM). Scales and (scale, bias) pairs are not reordered.
  * w, out: device, 16-byte aligned, not overlapping. rows % 16 == 0, rows >= 0 (0 is a no-op);
  * K a multiple of 32 (MOE_BF16) or 128 (codes), that multiple <= K <= 2^20; rows * K < 2^36;
  * else MOE_ERR_SHAPE. Other w_dtype: MOE_ERR_UNSUPPORTED. NULL pointers (rows > 0): MOE_ERR_NULL.

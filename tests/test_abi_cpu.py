@@ -326,8 +326,9 @@ def test_frag_weights_validation():
     assert run(_args(**{**fr, "T": 0})) == moe.MOE_OK
     assert run(_args(**fr), n=0) == moe.MOE_ERR_WORKSPACE            # accepted up to the workspace
     assert run(_args(**{**fr, "dtype": 0})) == moe.MOE_ERR_UNSUPPORTED          # fp32 activations
-    assert run(_args(**{**fr, "d": 128, "H": 128})) == moe.MOE_ERR_UNSUPPORTED  # not streaming
-    assert run(_args(**{**fr, "T": 2048, "k": 2}), n=1 << 40) == moe.MOE_ERR_UNSUPPORTED  # prefill
+    # bf16 fragment-major weights also serve the grouped-GEMM (prefill) path
+    assert run(_args(**{**fr, "T": 2048, "k": 2}), n=0) == moe.MOE_ERR_WORKSPACE
+    assert run(_args(**{**fr, "d": 128, "H": 128}), n=0) == moe.MOE_ERR_WORKSPACE
     # the quantised fragment-major types need their scale arrays, like MOE_I8 and MOE_Q4
     for wd in (moe.MOE_I8_FRAG, moe.MOE_Q4_FRAG):
         q = dict(fr, w_dtype=wd, w_gate_scale=FAKE.value, w_up_scale=FAKE.value,

@@ -131,7 +131,10 @@ def test_dominant_kernel_names(bench):
     assert bench.dominant_kernel(mk(64, 2048, 16, 1, 2816), "int8-frag") == "ffn_stream_kernel<true, 1, 5>"
     assert bench.dominant_kernel(mk(64, 1024, 64, 2, 512), "q4-frag") == "ffn_stream_kernel<true, 2, 6>"
     # prefill shapes: the grouped GEMM, wide tiles once experts average 256 rows
-    assert bench.dominant_kernel(mk(8192, 2048, 16, 1, 2816)).startswith("gemm_dma_kernel<true, 256, 256")
+    assert bench.dominant_kernel(mk(8192, 2048, 16, 1, 2816)) == \
+        "gemm_dma_kernel<true, 256, 256, 2, 64, 64, false>"
+    assert bench.dominant_kernel(mk(8192, 2048, 16, 1, 2816), "frag") == \
+        "gemm_dma_kernel<true, 256, 256, 2, 64, 64, true>"
     assert bench.dominant_kernel(mk(4096, 1024, 64, 2, 512)).startswith("gemm_dma_kernel<true, 128, 256")
     assert bench.dominant_kernel(mk(64, 128, 8, 1, 256, "f32")) == "ffn_f32_kernel<true>"
 

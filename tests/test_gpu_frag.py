@@ -1,4 +1,5 @@
-"""Fragment-major expert weights on the decode path (MOE_BF16_FRAG, MOE_I8_FRAG, MOE_Q4_FRAG):
+"""Fragment-major expert weights (MOE_BF16_FRAG on both kernel families, MOE_I8_FRAG and
+MOE_Q4_FRAG on the decode path):
 moe_pack_weights_frag bit-exact against the oracle's order for bf16 values, int8 codes and packed
 4-bit codes, and moe_layer_forward on reordered stacks (reordered by the oracle, so the layer tests
 do not depend on the GPU packer) equal bit for bit to the same layer on the row-major stacks (the
@@ -248,12 +249,48 @@ def test_frag_codes_with_gpu_quantiser_and_packer():
         np.testing.assert_array_equal(y.cpu().numpy(), ref["y"])
 
 
-def test_frag_rejected_outside_decode_path():
+# ------------------------------------------------------------------------ prefill (grouped GEMM)
+
+PREFILL = [
+    # name, T, d, E, k, H, scoring, sel_bias_var: the wide tiles (>= 256 rows per expert on average)
+    # and the narrow ones, each with partial column tiles (H = 320 and d = 192 are not multiples of
+    # the 128- or 256-column tiles)
+    ("wide-partial-cols", 600, 192, 4, 2, 320, orc.SELECTED_SOFTMAX, 0.5),
+    ("narrow-partial-cols", 1000, 192, 8, 2, 320, orc.SELECTED_SOFTMAX, 0.5),
+    ("narrow-top1", 700, 256, 16, 1, 512, orc.SOFTMAX, None),
+]
+
+
+@pytest.mark.parametrize("name", ["zonos2-skewed-prefill", "zonos3mini-prefill"])
+def test_frag_prefill_workload_equals_plain(name):
+    """bf16 fragment-major stacks on the grouped-GEMM path: the same output bit for bit."""
+    inp = gen.make_inputs(name)
+    dv = upload(inp)
+    _same(_run_frag(inp, dv, _frag(inp)), run_layer(inp, dv))
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
+def test_frag_prefill_edge_cases(case):
+    name, T, d, E, k, H, scoring, sbv = case
+    inp = gen.make_inputs_custom(T, d, E, k, H, scoring, "bf16", seed=3 * T + E, sel_bias_var=sbv)
+    dv = upload(inp)
+    plain = run_layer(inp, dv)
+    res = _run_frag(inp, dv, _frag(inp))
+    _same(res, plain)
+    print(f"{name}: {check_layer(inp, res)}")
+
+
+def test_frag_codes_rejected_outside_decode_path():
+    """The int8 and 4-bit codes, fragment-major or not, stay on the decode path."""
+    import torch
     from expert_routing_grouped_moe_amd import moe
     inp = gen.make_inputs_custom(3000, 256, 8, 1, 256, orc.SOFTMAX, "bf16", seed=9)
     dv = upload(inp)
-    fw = _frag(inp)
-    with pytest.raises(moe.MoeError) as ei:
-        moe.moe_layer_forward(dv["x"], dv["w_router"], fw["w_gate"], fw["w_up"], fw["w_down"], 1,
-                              inp.scoring, w_format="frag")
-    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    for fmt in ("i8", "q4"):
+        codes, scales = _quantised(inp, fmt)
+        cd = {key: torch.from_numpy(orc.pack_frag_ref(v, fmt)).to(DEV) for key, v in codes.items()}
+        sd = tuple(torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in scales)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_layer_forward(dv["x"], dv["w_router"], cd["w_gate"], cd["w_up"], cd["w_down"],
+                                  1, inp.scoring, w_scales=sd, w_format="frag")
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
