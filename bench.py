@@ -597,10 +597,11 @@ def main():
             print(f"[bench] {name}: {others[name]['ms_per_step'] * 1e3:.1f} us/step",
                   file=sys.stderr, flush=True)
 
-    # the decode workloads again on fragment-major bf16 weights (same values, reordered once)
+    # the decode workloads and the ZONOS3-Mini prefill again on fragment-major bf16 weights (same
+    # values, reordered once)
     frag = {}
     if not args.only and args.weights == "native":
-        for name in ("zonos2-decode", "zonos3mini-decode-cfg"):
+        for name in ("zonos2-decode", "zonos3mini-decode-cfg", "zonos3mini-prefill"):
             r = run_workload(name, args.other_steps, max(1, args.other_steps // 10), weights="frag",
                              warm=args.warm, eager=args.eager)
             frag[name] = {key: r[key] for key in ("ms_per_step", "tokens_per_s", "stage_median_us",
@@ -644,7 +645,7 @@ def main():
         table.update(others)
         result["workloads"] = {name: table[name] for name in FIVE if name in table}
     if frag:
-        result["decode_fragment_major_weights"] = frag
+        result["fragment_major_weights"] = frag
     print(json.dumps(result))
 
 
