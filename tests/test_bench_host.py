@@ -97,6 +97,23 @@ def test_committed_traffic_table_parses(bench):
         [float(c) for c in cells[3:7]]
 
 
+def test_traffic_table_names_the_kernels_the_bench_reports(bench):
+    """Each bf16 workload's dominant kernel, as bench.py names it, has a row in the committed
+    table for that workload (a renamed kernel would otherwise leave `traffic` null)."""
+    from expert_routing_grouped_moe_amd import inputs as gen
+    with open(bench.TRAFFIC_TABLE) as f:
+        keys = {tuple(c.strip() for c in l.strip().strip("|").split("|")[:2])
+                for l in f if l.startswith("| ") and not l.startswith("| kernel")}
+    for name in ("zonos2-skewed-prefill", "zonos3mini-prefill", "zonos2-decode",
+                 "zonos3mini-decode-cfg"):
+        wl = gen.WORKLOADS[name]
+        inp = SimpleNamespace(dtype="bf16", T=wl.T, d=wl.d, E=wl.E, k=wl.k, H=wl.H)
+        assert (bench.dominant_kernel(inp), name) in keys, name
+    wl = gen.WORKLOADS["zonos3mini-prefill"]
+    inp = SimpleNamespace(dtype="bf16", T=wl.T, d=wl.d, E=wl.E, k=wl.k, H=wl.H)
+    assert (bench.dominant_kernel(inp, "frag"), "zonos3mini-prefill/frag") in keys
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
